@@ -1,0 +1,332 @@
+"""Plain CPU oracle of the fused MoE layer with weight-only quantised experts (w4a16 / w8a16).
+
+TEST INFRASTRUCTURE ONLY (imported by tests, the smoke check and the benchmark's CPU baseline).
+It shares no code with the GPU library and is deliberately slow: numpy, float64 for the layer
+arithmetic, Python loops where the definition is a loop.
+
+What it computes, and where each step is defined:
+
+* Storage decoding of the expert weights.  "[Kernel] add triton fused moe kernel for gptq/awq"
+  (review thread: the kernel takes its own weight format that accepts GPTQ/AWQ checkpoints) and
+  "[Kernel] optimize performance of gptq marlin kernel when n is small" (benchmark script: uint4,
+  group size 128, integer zero point, has_zp=True, is_zp_float=False) fix the encoding family:
+  w = (q - z) * s per group of 128 along K.  The int8 variant is symmetric with one scale per output
+  channel and no zero point (the int8 MoE backend listing, make_int8_moe_quant_config: w8a16 config
+  with w1_zp = w2_zp = None; _humming_int8_weight_schema: symmetric, strategy "channel").
+  Nibble order and zero packing are not on the pages; the reading used is low nibble = even k.
+* Routing.  The pages describe none; the workloads fix it: softmax top-k (renormalised), or
+  DeepSeek-V3-style sigmoid scores with group-limited selection and a routed scaling factor.
+* moe_align_block_size.  Named in the first PR's notes (shared-memory version for large expert
+  counts, usable under CUDA graphs); its output format is not printed, the reading used is the
+  plainest one (stable grouping by expert, each group padded to BLOCK_M with a sentinel).
+* The expert FFN out[m] = sum_j w[m,j] * W2[e_mj] (SiLU(W1[e_mj] x_m) * W3[e_mj] x_m), with W1/W3 the
+  gate/up halves of w13 (rows [0,I) and [I,2I)); the pages name the one-launch grouped GEMM that
+  computes it (first PR, description).
+
+Every reading the pages leave open is listed with its justification in the design notes.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 128
+
+__all__ = [
+    "GROUP", "unpack_uint4", "dequant_uint4", "dequant_int8", "dequant_bits",
+    "exp_f32_spec", "sigmoid_f32_spec", "route_softmax", "route_sigmoid_grouped", "route",
+    "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
+    "grouped_gemm", "to_numpy",
+]
+
+
+def to_numpy(t):
+    """torch tensor (any device, any dtype incl. bfloat16) -> numpy; bf16 arrives as float32."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        return np.asarray(t)
+    if isinstance(t, torch.Tensor):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            t = t.float()
+        return t.numpy()
+    return np.asarray(t)
+
+
+# ================================================================================================
+# storage decoding
+# ================================================================================================
+def unpack_uint4(packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., n] -> uint8 [..., 2n]: element 2j is bits 0-3 of byte j, element 2j+1 bits 4-7."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 0x0F
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def dequant_uint4(qweight, scales, zeros) -> np.ndarray:
+    """Exact dequantised weights (q - z) * s as float64 [N, K] for one expert.
+
+    qweight uint8 [N, K/2], scales float [N, K/128], zeros uint8 [N, K/256]."""
+    q = unpack_uint4(qweight).astype(np.float64)
+    z = unpack_uint4(zeros).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float64)
+    N, K = q.shape
+    ng = K // GROUP
+    assert s.shape == (N, ng) and z.shape == (N, ng), (s.shape, z.shape, (N, ng))
+    return ((q.reshape(N, ng, GROUP) - z[..., None]) * s[..., None]).reshape(N, K)
+
+
+def dequant_int8(qweight, scales) -> np.ndarray:
+    """Exact dequantised weights q * s as float64 [N, K]; qweight int8 [N, K], scales [N]."""
+    q = np.asarray(qweight, dtype=np.int8).astype(np.float64)
+    s = np.asarray(scales, dtype=np.float64)
+    return q * s[:, None]
+
+
+def dequant_bits(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """Round exact dequantised values to the activation dtype (round to nearest even).
+
+    Returns the uint16 bit patterns.  The exact value (q - z) * s has at most 18 significant bits, so
+    it is exact in float32 and one rounding from there is the correct rounding."""
+    x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), np.asarray(x64, dtype=np.float64))
+    if dtype == "fp16":
+        return x32.astype(np.float16).view(np.uint16)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+# ================================================================================================
+# routing
+# ================================================================================================
+# e^x in float32, specified operation by operation so that any two IEEE-754 implementations that
+# follow it produce the same bits: clamp x to [-80, 80]; n = rint(x * log2(e)); Cody-Waite two-part
+# reduction r = (x - n*C1) - n*C2 with C1 = 355/512 and C2 = ln2 - C1 (rounded to float32); degree-7
+# Taylor polynomial of e^r in Horner form with coefficients 1/i! rounded to float32; scale by 2^n.
+# Every step is one float32 operation rounded to nearest even, in exactly this order, never fused.
+_LOG2E = np.float32(1.4426950408889634)
+_C1 = np.float32(355.0 / 512.0)
+_C2 = np.float32(math.log(2.0) - 355.0 / 512.0)
+_INV_FACT = [np.float32(1.0 / math.factorial(i)) for i in range(8)]
+
+
+def exp_f32_spec(x) -> np.ndarray:
+    x = np.clip(np.asarray(x, dtype=np.float32), np.float32(-80.0), np.float32(80.0))
+    n = np.rint(x * _LOG2E)
+    r = (x - n * _C1) - n * _C2
+    p = _INV_FACT[7]
+    for i in range(6, -1, -1):
+        p = p * r + _INV_FACT[i]      # separate multiply then add (numpy never fuses)
+    return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+
+
+def sigmoid_f32_spec(x) -> np.ndarray:
+    """1 / (1 + e^-x) in float32 with the exp above and a correctly rounded division."""
+    e = exp_f32_spec(-np.asarray(x, dtype=np.float32))
+    return (np.float32(1.0) / (np.float32(1.0) + e)).astype(np.float32)
+
+
+def route_softmax(logits, topk: int, renormalize: bool = True, scale: float = 1.0):
+    """Softmax top-k.  ids: the k largest logits, descending, ties to the lower expert id (softmax is
+    monotone, so ranking logits ranks probabilities without rounding).  weights (float64): the
+    softmax probabilities of the chosen experts, divided by their sum when renormalising, times the
+    routed scaling factor."""
+    lg = np.asarray(logits, dtype=np.float32)
+    M, E = lg.shape
+    ids = np.zeros((M, topk), np.int32)
+    w = np.zeros((M, topk), np.float64)
+    for m in range(M):
+        row = lg[m]
+        order = sorted(range(E), key=lambda e: (-float(row[e]), e))[:topk]
+        l64 = row.astype(np.float64)
+        p = np.exp(l64 - l64.max())
+        p /= p.sum()
+        sel = p[order]
+        if renormalize:
+            sel = sel / sel.sum()
+        ids[m] = order
+        w[m] = sel * scale
+    return ids, w
+
+
+def route_sigmoid_grouped(logits, topk: int, num_groups: int, topk_groups: int,
+                          renormalize: bool = True, scale: float = 1.0):
+    """DeepSeek-V3-style group-limited routing on sigmoid scores.
+
+    1. sigma = sigmoid_f32_spec(logit) per expert (float32: these values decide which ids win).
+    2. Experts form num_groups contiguous groups; a group's score is the float32 sum of its two
+       largest sigma (its single sigma if the group has one expert).
+    3. Keep the topk_groups best groups (descending score, ties to the lower group id).
+    4. ids = the topk largest sigma inside kept groups (descending, ties to the lower expert id).
+    5. weights = sigma of the chosen experts / their sum (if renormalising) * scale, in float64.
+    """
+    lg = np.asarray(logits, dtype=np.float32)
+    M, E = lg.shape
+    assert E % num_groups == 0
+    gs = E // num_groups
+    sig = sigmoid_f32_spec(lg)
+    ids = np.zeros((M, topk), np.int32)
+    w = np.zeros((M, topk), np.float64)
+    for m in range(M):
+        s = sig[m]
+        gscore = []
+        for g in range(num_groups):
+            members = sorted((float(v) for v in s[g * gs:(g + 1) * gs]), reverse=True)
+            if gs >= 2:
+                gscore.append(np.float32(members[0]) + np.float32(members[1]))
+            else:
+                gscore.append(np.float32(members[0]))
+        kept = set(sorted(range(num_groups), key=lambda g: (-float(gscore[g]), g))[:topk_groups])
+        cand = [e for e in range(E) if e // gs in kept]
+        sel = sorted(cand, key=lambda e: (-float(s[e]), e))[:topk]
+        v = s[sel].astype(np.float64)
+        if renormalize:
+            v = v / v.sum()
+        ids[m] = sel
+        w[m] = v * scale
+    return ids, w
+
+
+def route(logits, topk, score="softmax", renormalize=True, num_groups=1, topk_groups=1, scale=1.0):
+    if score == "softmax":
+        assert num_groups == 1
+        return route_softmax(logits, topk, renormalize, scale)
+    return route_sigmoid_grouped(logits, topk, num_groups, topk_groups, renormalize, scale)
+
+
+# ================================================================================================
+# moe_align_block_size
+# ================================================================================================
+def align_capacity(numel: int, E: int, block_m: int) -> int:
+    """Largest possible padded length: every non-empty expert adds at most block_m - 1 padding."""
+    return numel + min(E, numel) * (block_m - 1)
+
+
+def align_block_size(topk_ids, E: int, block_m: int, capacity: int | None = None):
+    """Group token-slots by expert and pad each group to a multiple of block_m.
+
+    Slot s = m * topk + j.  For experts in ascending order, the slots routed to expert e are listed
+    in ascending slot order, followed by sentinel entries (value numel) up to the next multiple of
+    block_m; an expert with no slots takes no space.  Entries from the padded total T up to the
+    capacity are sentinels too.  expert_ids[b] is the expert of block b (entries b*block_m ...), or -1
+    for blocks at or beyond T.  Ids outside [0, E) are not listed.
+    Returns (sorted_token_ids int32 [cap], expert_ids int32 [ceil(cap/block_m)], T).
+    """
+    flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    numel = flat.size
+    cap = align_capacity(numel, E, block_m) if capacity is None else capacity
+    sorted_ids = np.full(cap, numel, dtype=np.int32)
+    expert_ids = np.full(-(-cap // block_m), -1, dtype=np.int32)
+    pos = 0
+    for e in range(E):
+        slots = np.nonzero(flat == e)[0]
+        if slots.size == 0:
+            continue
+        padded = -(-slots.size // block_m) * block_m
+        sorted_ids[pos:pos + slots.size] = slots
+        expert_ids[pos // block_m:(pos + padded) // block_m] = e
+        pos += padded
+    return sorted_ids, expert_ids, pos
+
+
+# ================================================================================================
+# expert FFN and the layer
+# ================================================================================================
+def silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+class ExpertSource:
+    """Serves exact float64 dequantised weights of one expert at a time.
+
+    `layer` maps w13, w13_scales, w13_zeros, w2, w2_scales, w2_zeros to arrays indexed by the
+    position in `experts` (default: position = expert id)."""
+
+    def __init__(self, layer: dict, bits: int, experts=None):
+        self.layer = {k: (to_numpy(v) if v is not None else None) for k, v in layer.items()}
+        self.bits = bits
+        self.index = None if experts is None else {int(e): i for i, e in enumerate(experts)}
+
+    def _i(self, e):
+        return int(e) if self.index is None else self.index[int(e)]
+
+    def _deq(self, name, i):
+        L = self.layer
+        if self.bits == 4:
+            return dequant_uint4(L[name][i], L[name + "_scales"][i], L[name + "_zeros"][i])
+        return dequant_int8(L[name][i], L[name + "_scales"][i])
+
+    def w13(self, e):
+        return self._deq("w13", self._i(e))
+
+    def w2(self, e):
+        return self._deq("w2", self._i(e))
+
+
+def moe_layer_rows(x, topk_ids, topk_weights, src: ExpertSource, rows=None):
+    """out[m] = sum_j w[m,j] * W2[e] (SiLU(gate_e x_m) * up_e x_m) for the token rows `rows`.
+
+    Float64 throughout; the per-slot results are summed over j in ascending order.
+    Returns (out float64 [len(rows), H], per-slot y float64 [len(rows), topk, H])."""
+    x64 = np.asarray(to_numpy(x), dtype=np.float64)
+    ids = np.asarray(to_numpy(topk_ids), dtype=np.int64)
+    wts = np.asarray(to_numpy(topk_weights), dtype=np.float64)
+    rows = np.arange(ids.shape[0]) if rows is None else np.asarray(rows)
+    k = ids.shape[1]
+    sub = ids[rows]
+    y = None
+    for e in sorted(set(sub.reshape(-1).tolist())):
+        W13 = src.w13(e)
+        W2 = src.w2(e)
+        I = W13.shape[0] // 2
+        rr, jj = np.nonzero(sub == e)
+        h = x64[rows[rr]] @ W13.T                 # each row is one token's product with expert e
+        a = silu(h[:, :I]) * h[:, I:]
+        ye = a @ W2.T
+        if y is None:
+            y = np.zeros((len(rows), k, W2.shape[0]), np.float64)
+        y[rr, jj] = ye
+    out = np.zeros((len(rows), y.shape[2]), np.float64)
+    for j in range(k):
+        out += wts[rows, j][:, None] * y[:, j]
+    return out, y
+
+
+def moe_layer(x, topk_ids, topk_weights, src: ExpertSource):
+    return moe_layer_rows(x, topk_ids, topk_weights, src)[0]
+
+
+def grouped_gemm(A, a_row_div: int, weight_of, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                 block_m: int, num_slots: int, topk_weights=None, act: int = 0):
+    """The grouped GEMM over align output, as a definition.
+
+    For every listed slot s at position p < T: e = expert_ids[p // block_m],
+    h = A[s // a_row_div] @ W[e]^T (float64); with act == 1, c = SiLU(h[:N/2]) * h[N/2:], else c = h;
+    times topk_weights[s] if given.  Returns ({slot: row float64}) for the listed slots."""
+    A64 = np.asarray(to_numpy(A), dtype=np.float64)
+    st = np.asarray(sorted_token_ids)
+    ex = np.asarray(expert_ids)
+    tw = None if topk_weights is None else np.asarray(to_numpy(topk_weights), np.float64).reshape(-1)
+    out = {}
+    cache = {}
+    for p in range(int(num_tokens_post_padded)):
+        s = int(st[p])
+        if s >= num_slots:
+            continue
+        e = int(ex[p // block_m])
+        if e not in cache:
+            cache[e] = weight_of(e)
+        W = cache[e]
+        h = W @ A64[s // a_row_div]
+        if act == 1:
+            n2 = W.shape[0] // 2
+            h = silu(h[:n2]) * h[n2:]
+        if tw is not None:
+            h = h * tw[s]
+        out[s] = h
+    return out

@@ -1,0 +1,345 @@
+"""Pins of the CPU oracle against things other than itself: hand-worked fixtures, library routines,
+closed forms, brute force and the quantisation error bound.  CPU only."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+
+# ------------------------------------------------------------------------------------------------
+# storage decoding
+# ------------------------------------------------------------------------------------------------
+def test_uint4_layout_golden(golden):
+    g = golden("uint4_layout.txt")
+    period = bytes.fromhex(g["row_bytes_period"][0].replace(" ", ""))
+    row = np.frombuffer(period * 16, dtype=np.uint8)[None, :]
+    zeros = np.array([[int(g["zero_byte"][0], 16)]], dtype=np.uint8)
+    sbits = [int(v, 16) for v in g["scales_fp16_bits"][0].split()]
+    scales = np.array([sbits], dtype=np.uint16).view(np.float16)
+    w = O.dequant_uint4(row, scales, zeros)[0]
+    for item in g["expect"]:
+        k, v = item.split()
+        assert w[int(k)] == float(v), (k, w[int(k)], v)
+    # and the whole row from the closed form of the fixture
+    k = np.arange(256)
+    q = (7 * k + 3) % 16
+    ref = np.where(k < 128, (q - 3) * 0.5, (q - 12) * 0.25)
+    assert np.array_equal(w, ref)
+
+
+def test_unpack_is_inverse_of_encoder_packing():
+    rng = np.random.default_rng(1)
+    q = rng.integers(0, 16, size=(7, 512), dtype=np.uint8)
+    packed = (torch.from_numpy(q[:, 0::2]) | (torch.from_numpy(q[:, 1::2]) << 4)).numpy()
+    assert np.array_equal(O.unpack_uint4(packed), q)
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_encode_decode_on_grid_is_exact(dt):
+    """Weights placed exactly on a uint4 grid whose extremes hit codes 0 and 15 come back exactly:
+    the encoder recovers (q, z, s) and the oracle's decoding reproduces w bit for bit."""
+    rng = np.random.default_rng(2)
+    N, K = 8, 512
+    ng = K // 128
+    s = np.array([[2.0 ** -rng.integers(4, 9) * (1 + rng.integers(0, 8) / 8) for _ in range(ng)]
+                  for _ in range(N)])
+    s = torch.tensor(s).to(dt).double().numpy()           # representable in the scale dtype
+    z = rng.integers(1, 15, size=(N, ng))
+    q = rng.integers(0, 16, size=(N, K))
+    q[:, 0::128] = 0                                        # lo hits code 0
+    q[:, 1::128] = 15                                       # hi hits code 15
+    w = (q.reshape(N, ng, 128) - z[..., None]) * s[..., None]
+    w = w.reshape(N, K)
+    qp, sc, zp = synth.encode_uint4_g128(torch.tensor(w, dtype=torch.float64).float(), dt)
+    assert np.array_equal(O.unpack_uint4(qp.numpy()), q)
+    assert np.array_equal(O.unpack_uint4(zp.numpy()), z)
+    assert np.array_equal(sc.double().numpy(), s)
+    back = O.dequant_uint4(qp.numpy(), O.to_numpy(sc), zp.numpy())
+    assert np.array_equal(back, w)
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_uint4_error_bound_half_scale(dt):
+    """Every dequantised weight is within s/2 of the drawn weight (asymmetric min/max, scale rounded
+    up), and all codes are in [0, 15]."""
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn(64, 1024, generator=g) * 0.02
+    qp, sc, zp = synth.encode_uint4_g128(w, dt)
+    back = O.dequant_uint4(qp.numpy(), O.to_numpy(sc), zp.numpy())
+    s = np.repeat(O.to_numpy(sc).astype(np.float64), 128, axis=1)
+    err = np.abs(back - w.double().numpy())
+    assert (err <= s / 2).all(), float((err / s).max())
+    # scale rounded up: 15 s >= hi - lo for every group
+    wg = w.double().numpy().reshape(64, 8, 128)
+    assert (15 * O.to_numpy(sc).astype(np.float64) >= wg.max(-1) - wg.min(-1)).all()
+
+
+def test_int8_error_bound_half_scale():
+    g = torch.Generator().manual_seed(4)
+    w = torch.randn(32, 768, generator=g) * 0.02
+    q, s = synth.encode_int8_channel(w, torch.bfloat16)
+    assert int(q.abs().max()) <= 127
+    back = O.dequant_int8(q.numpy(), O.to_numpy(s))
+    err = np.abs(back - w.double().numpy())
+    assert (err <= O.to_numpy(s).astype(np.float64)[:, None] / 2).all()
+
+
+def test_dequant_bits_matches_torch_rounding():
+    """The bit-exact dequantised object rounds (q - z) * s to the activation dtype; check the oracle's
+    rounding against torch's float64 -> fp16 / float32 -> bf16 conversion (library routine)."""
+    rng = np.random.default_rng(5)
+    v = (rng.integers(-15, 16, 4096) * rng.uniform(1e-4, 1e-1, 4096))
+    v32 = v.astype(np.float32).astype(np.float64)         # make each value an exact fp32
+    assert np.array_equal(O.dequant_bits(v32, "fp16"),
+                          torch.tensor(v32).to(torch.float16).view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(O.dequant_bits(v32, "bf16"),
+                          torch.tensor(v32, dtype=torch.float32).to(torch.bfloat16)
+                          .view(torch.int16).numpy().view(np.uint16))
+
+
+# ------------------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------------------
+def _ulp32(x):
+    return np.spacing(np.abs(np.float32(x))).astype(np.float64)
+
+
+def test_exp_spec_within_one_ulp_of_libm():
+    x = np.linspace(-80, 80, 200001, dtype=np.float32)
+    got = O.exp_f32_spec(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    err = np.abs(got - ref) / np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert err.max() <= 1.5, err.max()
+
+
+def test_sigmoid_spec_close_to_exact():
+    x = np.linspace(-20, 20, 100001, dtype=np.float32)
+    got = O.sigmoid_f32_spec(x).astype(np.float64)
+    ref = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+    err = np.abs(got - ref) / np.spacing(ref.astype(np.float32)).astype(np.float64)
+    # exp error (<= 1.5 ulp) + rounding of 1 + e + rounding of the division, each up to 0.5 ulp
+    # relative, measured in ulps of the result's binade (up to 2x apart): at most 3 ulp
+    assert err.max() <= 3.0, err.max()
+    assert O.sigmoid_f32_spec(np.float32(0.0)) == np.float32(0.5)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (256, 8)])
+def test_route_softmax_vs_argsort(E, k):
+    rng = np.random.default_rng(E)
+    lg = rng.standard_normal((40, E)).astype(np.float32)
+    ids, w = O.route_softmax(lg, k, renormalize=True)
+    assert np.array_equal(ids, np.argsort(-lg, axis=1, kind="stable")[:, :k])
+    # renormalised softmax over the chosen experts == softmax of the chosen logits alone
+    sel = np.take_along_axis(lg.astype(np.float64), ids.astype(np.int64), 1)
+    ref = np.exp(sel - sel.max(1, keepdims=True))
+    ref /= ref.sum(1, keepdims=True)
+    np.testing.assert_allclose(w, ref, rtol=1e-12)
+    ids2, w2 = O.route_softmax(lg, k, renormalize=False)
+    full = torch.softmax(torch.tensor(lg, dtype=torch.float64), dim=1).numpy()
+    np.testing.assert_allclose(w2, np.take_along_axis(full, ids2.astype(np.int64), 1), rtol=1e-12)
+
+
+def test_route_softmax_ties_go_to_lower_id():
+    lg = np.array([[0.5, 1.0, 1.0, -1.0, 1.0]], np.float32)
+    ids, _ = O.route_softmax(lg, 3)
+    assert ids.tolist() == [[1, 2, 4]]
+
+
+def _brute_grouped(sig, num_groups, topk_groups, topk):
+    """Brute force: score every group by the best pair sum, try every set of kept groups, keep the
+    set with the largest total score, then the topk experts inside by sigma."""
+    E = sig.size
+    gs = E // num_groups
+    score = []
+    for g in range(num_groups):
+        m = sig[g * gs:(g + 1) * gs]
+        if gs == 1:
+            score.append(float(m[0]))
+        else:
+            score.append(max(float(np.float32(m[a]) + np.float32(m[b]))
+                             for a in range(gs) for b in range(gs) if a != b))
+    best = max(itertools.combinations(range(num_groups), topk_groups),
+               key=lambda c: sum(score[g] for g in c))
+    cand = [e for e in range(E) if e // gs in best]
+    cand.sort(key=lambda e: -float(sig[e]))
+    return cand[:topk]
+
+
+@pytest.mark.parametrize("E,ng,tg,k", [(256, 8, 4, 8), (64, 8, 3, 6), (32, 4, 2, 4)])
+def test_route_sigmoid_grouped_vs_brute_force(E, ng, tg, k):
+    rng = np.random.default_rng(E + ng)
+    lg = rng.standard_normal((30, E)).astype(np.float32)
+    ids, w = O.route_sigmoid_grouped(lg, k, ng, tg, renormalize=True, scale=2.5)
+    sig = O.sigmoid_f32_spec(lg)
+    for m in range(lg.shape[0]):
+        assert ids[m].tolist() == _brute_grouped(sig[m], ng, tg, k)
+    np.testing.assert_allclose(w.sum(1), 2.5, rtol=1e-12)
+    # weights are proportional to sigma of the chosen experts
+    s_sel = np.take_along_axis(sig.astype(np.float64), ids.astype(np.int64), 1)
+    np.testing.assert_allclose(w / s_sel, (w / s_sel)[:, :1].repeat(k, 1), rtol=1e-12)
+
+
+def test_route_sigmoid_single_group_is_plain_topk():
+    rng = np.random.default_rng(9)
+    lg = rng.standard_normal((50, 64)).astype(np.float32)
+    ids, _ = O.route_sigmoid_grouped(lg, 6, 1, 1)
+    assert np.array_equal(ids, np.argsort(-lg, axis=1, kind="stable")[:, :6])
+
+
+# ------------------------------------------------------------------------------------------------
+# align
+# ------------------------------------------------------------------------------------------------
+def test_align_golden(golden):
+    g = golden("align_example.txt")
+    ids = np.array([int(v) for v in g["topk_ids"][0].split()], np.int32).reshape(-1, 2)
+    for case in ("A", "B"):
+        E = int(g[f"{case}.E"][0])
+        bm = int(g[f"{case}.block_m"][0])
+        st, ex, T = O.align_block_size(ids, E, bm)
+        assert st.tolist() == [int(v) for v in g[f"{case}.sorted_token_ids"][0].split()]
+        assert ex.tolist() == [int(v) for v in g[f"{case}.expert_ids"][0].split()]
+        assert T == int(g[f"{case}.num_tokens_post_padded"][0])
+
+
+def _align_by_argsort(flat, E, bm):
+    order = np.argsort(flat, kind="stable")       # library stable sort
+    cnt = np.bincount(flat, minlength=E)
+    pieces, experts = [], []
+    start = 0
+    for e in range(E):
+        c = int(cnt[e])
+        if c == 0:
+            continue
+        p = -(-c // bm) * bm
+        pieces.append(np.concatenate([order[start:start + c], np.full(p - c, flat.size)]))
+        experts += [e] * (p // bm)
+        start += c
+    return np.concatenate(pieces), np.array(experts)
+
+
+@pytest.mark.parametrize("M,k,E,bm", [(16, 2, 8, 16), (1, 8, 256, 16), (64, 8, 256, 32),
+                                      (512, 8, 64, 64), (333, 2, 8, 128), (7, 3, 5, 4)])
+def test_align_vs_stable_sort_and_invariants(M, k, E, bm):
+    rng = np.random.default_rng(M * 31 + E)
+    ids = rng.integers(0, E, size=(M, k)).astype(np.int32)
+    flat = ids.reshape(-1)
+    st, ex, T = O.align_block_size(ids, E, bm)
+    ref_st, ref_ex = _align_by_argsort(flat, E, bm)
+    assert T == ref_st.size
+    assert np.array_equal(st[:T], ref_st)
+    assert np.array_equal(ex[:T // bm], ref_ex)
+    cap = O.align_capacity(flat.size, E, bm)
+    assert st.size == cap and T <= cap and T % bm == 0
+    assert (st[T:] == flat.size).all() and (ex[T // bm:] == -1).all()
+    real = st[st < flat.size]
+    assert np.array_equal(np.sort(real), np.arange(flat.size))    # a permutation of the slots
+    for b in range(T // bm):                                        # every block single-expert
+        blk = st[b * bm:(b + 1) * bm]
+        blk = blk[blk < flat.size]
+        assert (flat[blk] == ex[b]).all()
+
+
+# ------------------------------------------------------------------------------------------------
+# the layer
+# ------------------------------------------------------------------------------------------------
+def _tiny_layer(E=4, H=256, I=256, bits=4, dt="fp16", seed=0):
+    wl = synth.Workload("t", E=E, H=H, I=I, topk=2, Ms=(5,), dtype=dt, bits=bits)
+    return wl, synth.make_layer(wl, seed=seed)
+
+
+@pytest.mark.parametrize("bits,dt", [(4, "fp16"), (4, "bf16"), (8, "bf16")])
+def test_layer_vs_dense_all_experts(bits, dt):
+    """Dense formulation: evaluate every expert on every token with explicit loops over experts and
+    a dense gate matrix that is zero off the chosen experts; must equal the routed oracle."""
+    wl, layer = _tiny_layer(bits=bits, dt=dt)
+    x = synth.make_x(wl, 5, seed=1)
+    lg = synth.make_logits(wl, 5, seed=1)
+    ids, w = O.route_softmax(O.to_numpy(lg), 2)
+    src = O.ExpertSource(layer, bits)
+    out = O.moe_layer(x, ids, w, src)
+    x64 = O.to_numpy(x).astype(np.float64)
+    G = np.zeros((5, wl.E))
+    for m in range(5):
+        for j in range(2):
+            G[m, ids[m, j]] += w[m, j]
+    ref = np.zeros_like(out)
+    for e in range(wl.E):
+        W13, W2 = src.w13(e), src.w2(e)
+        t = torch.tensor(x64)
+        h = t @ torch.tensor(W13).T
+        a = torch.nn.functional.silu(h[:, :wl.I]) * h[:, wl.I:]
+        ref += G[:, e:e + 1] * (a @ torch.tensor(W2).T).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_layer_one_expert_weight_one_is_dense_ffn_of_drawn_weights():
+    """Route every token to one expert with weight 1 and put the drawn weights exactly on the quant
+    grid: the layer equals the dense SwiGLU FFN of the original float weights (torch, float64)."""
+    wl = synth.Workload("t", E=3, H=256, I=256, topk=1, Ms=(6,), dtype="fp16")
+    w13, w2 = synth.expert_weights_fp32(wl, 1, seed=7)
+    # snap to the grid the encoder would produce, so encoding is lossless
+    q13, s13, z13 = synth.encode_uint4_g128(w13, torch.float16)
+    q2, s2, z2 = synth.encode_uint4_g128(w2, torch.float16)
+    W13 = O.dequant_uint4(q13.numpy(), O.to_numpy(s13), z13.numpy())
+    W2 = O.dequant_uint4(q2.numpy(), O.to_numpy(s2), z2.numpy())
+    layer = synth.make_layer(wl, seed=7)
+    src = O.ExpertSource(layer, 4)
+    x = synth.make_x(wl, 6, seed=7)
+    ids = np.ones((6, 1), np.int32)
+    out = O.moe_layer(x, ids, np.ones((6, 1)), src)
+    t = torch.tensor(O.to_numpy(x), dtype=torch.float64)
+    h1 = t @ torch.tensor(W13[:256]).T
+    h3 = t @ torch.tensor(W13[256:]).T
+    ref = (torch.nn.functional.silu(h1) * h3) @ torch.tensor(W2).T
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-15)
+    # and the dequantised grid is within s/2 of the original draws
+    assert np.abs(W13 - w13.double().numpy()).max() <= O.to_numpy(s13).max() / 2
+
+
+def test_layer_brute_force_python_loops():
+    """Tiny case with plain Python loops (no numpy products) for the FFN of each routed slot."""
+    wl = synth.Workload("t", E=3, H=256, I=256, topk=2, Ms=(2,), dtype="fp16")
+    layer = synth.make_layer(wl, seed=11)
+    src = O.ExpertSource(layer, 4)
+    x = O.to_numpy(synth.make_x(wl, 2, seed=11)).astype(np.float64)
+    lg = O.to_numpy(synth.make_logits(wl, 2, seed=11))
+    ids, w = O.route_softmax(lg, 2)
+    out = O.moe_layer(x, ids, w, src)
+    for m in range(2):
+        acc = [0.0] * wl.H
+        for j in range(2):
+            W13 = src.w13(ids[m, j]).tolist()
+            W2 = src.w2(ids[m, j]).tolist()
+            xm = x[m].tolist()
+            h = [sum(W13[r][c] * xm[c] for c in range(wl.H)) for r in range(2 * wl.I)]
+            a = [h[i] / (1.0 + math.exp(-h[i])) * h[wl.I + i] for i in range(wl.I)]
+            for r in range(wl.H):
+                acc[r] += w[m, j] * sum(W2[r][i] * a[i] for i in range(wl.I))
+        np.testing.assert_allclose(out[m], acc, rtol=1e-10, atol=1e-14)
+
+
+def test_grouped_gemm_definition_matches_layer():
+    """GEMM1 with SiLU-and-mul, then GEMM2 scaled by the routing weight, summed over j in order,
+    equals the per-token layer (two formulations over the align output)."""
+    wl = synth.WORKLOADS["tiny"]
+    layer = synth.make_layer(wl, seed=0)
+    src = O.ExpertSource(layer, 4)
+    M = 16
+    x = synth.make_x(wl, M)
+    lg = synth.make_logits(wl, M)
+    ids, w = O.route_softmax(O.to_numpy(lg), wl.topk)
+    st, ex, T = O.align_block_size(ids, wl.E, 16)
+    ns = M * wl.topk
+    a = O.grouped_gemm(x, wl.topk, src.w13, st, ex, T, 16, ns, act=1)
+    A = np.stack([a[s] for s in range(ns)])
+    y = O.grouped_gemm(A, 1, src.w2, st, ex, T, 16, ns, topk_weights=w)
+    out = np.zeros((M, wl.H))
+    for m in range(M):
+        for j in range(wl.topk):
+            out[m] += y[m * wl.topk + j]
+    np.testing.assert_allclose(out, O.moe_layer(x, ids, w, src), rtol=1e-12, atol=1e-16)
