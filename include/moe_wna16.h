@@ -1,0 +1,164 @@
+/*
+ * moe_wna16 — fused mixture-of-experts layer with weight-only quantised experts on MI355X (gfx950).
+ *
+ * The layer: top-k routing -> moe_align_block_size -> one grouped GEMM over all experts for w13 with
+ * the weights decoded in registers -> SiLU(gate) * up -> grouped GEMM for w2 -> top-k weighted
+ * combine.  The one-launch grouped GEMM over every expert (instead of one launch per expert) is the
+ * method of "[Kernel] add triton fused moe kernel for gptq/awq" (PR description); the align step and
+ * its graph-capturable form are named in that PR's notes; the weight encodings follow the same PR's
+ * review thread (a format that accepts GPTQ/AWQ weights) and the benchmark script of "[Kernel]
+ * optimize performance of gptq marlin kernel when n is small" (uint4, group 128, integer zero
+ * point).  The int8 variant (w8a16: symmetric, one scale per output channel, no zero point) follows
+ * the int8 MoE backend listing (make_int8_moe_quant_config and the int8 weight schema).
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers are caller-owned device buffers; the library never
+ *     allocates, frees or synchronises inside these calls, and never reads device data on the host.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = default stream) and is
+ *     safe to capture in a HIP graph.  Results are available once the stream reaches that point.
+ *   - Every output element is written (padding included), so outputs need no initialisation.
+ *   - Arguments are checked on the host before anything is enqueued.  A non-zero status means
+ *     nothing was enqueued (except MOE_ERR_HIP, a launch failure); moe_last_error() then returns a
+ *     message for the calling thread.
+ *   - dtype: 0 = fp16, 1 = bf16.  Activations, outputs and weight scales share it.
+ *   - Rows are contiguous (row-major) and every device pointer must be 16-byte aligned.
+ *
+ * Weight storage (row-major, expert-major; N = output features, K = input features):
+ *   int4 (quant {4, 128, 1}): B uint8 [E, N, K/2], byte j of a row holds k = 2j in bits 0-3 and
+ *        k = 2j+1 in bits 4-7; scales [E, N, K/128]; zeros uint8 [E, N, K/256], byte j holds the
+ *        zero point of group 2j in bits 0-3 and of group 2j+1 in bits 4-7.
+ *        Decoded weight w[n][k] = (q - z) * s of its group.
+ *   int8 (quant {8, 0, 0}): B int8 [E, N, K]; scales [E, N]; no zeros.  w[n][k] = q * s.
+ *   w13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
+ */
+#ifndef MOE_WNA16_H
+#define MOE_WNA16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, non-positive size, inconsistent args */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid request outside what the kernels implement */
+  MOE_ERR_CAPACITY = -3,      /* an output buffer is smaller than the worst case needs */
+  MOE_ERR_WORKSPACE = -4,     /* workspace smaller than fused_moe_wna16_workspace_size() */
+  MOE_ERR_HIP = -5            /* a HIP launch failed (message in moe_last_error) */
+};
+
+enum { MOE_DTYPE_FP16 = 0, MOE_DTYPE_BF16 = 1 };
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1 };
+
+/* Weight encoding. {4, 128, 1}: uint4 with per-group-of-128 scales and integer zero points.
+ * {8, 0, 0}: int8 symmetric with one scale per output channel.  Anything else: UNSUPPORTED. */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int32_t has_zero;
+} moe_quant_t;
+
+/* Routing rule.
+ * score 0 (softmax): ids = the topk largest logits (descending, ties to the lower expert id);
+ *   weight = softmax probability, divided by the sum over the chosen experts if renormalize,
+ *   times scale.  num_groups must be 1.
+ * score 1 (sigmoid): s = 1/(1+e^-logit) in float32 with a specified exp (Cody-Waite reduction
+ *   with C1 = 355/512, degree-7 Taylor polynomial, no fused multiply-add), so ids are reproducible
+ *   bit for bit; experts form num_groups contiguous groups scored by the sum of their two largest s;
+ *   the topk_groups best groups are kept (ties to the lower group id) and ids are the topk largest
+ *   s inside them (ties to the lower id); weight = s / (sum over chosen, if renormalize) * scale.
+ * DeepSeek-V3 uses {1, 1, 8, 4, 2.5f}; Mixtral-style top-2 softmax uses {0, 1, 1, 1, 1.0f}. */
+typedef struct {
+  int32_t score;
+  int32_t renormalize;
+  int32_t num_groups;
+  int32_t topk_groups;
+  float scale;
+} moe_routing_t;
+
+/* Top-k routing of M tokens over E experts.
+ *   logits       device float [M, E]
+ *   topk_weights device float [M, topk]   (out)
+ *   topk_ids     device int32 [M, topk]   (out; slot s = m*topk + j is token m's j-th choice)
+ * Limits: 1 <= E <= 1024, 1 <= topk <= min(E, 32); for sigmoid, E % num_groups == 0,
+ * num_groups <= 64, 1 <= topk_groups <= num_groups and topk <= topk_groups * E / num_groups.
+ * M == 0 is a no-op.  Logits must be finite. */
+int moe_topk_softmax(const float* logits, int M, int E, int topk, const moe_routing_t* routing,
+                     float* topk_weights, int32_t* topk_ids, void* stream);
+
+/* Length that sorted_token_ids needs for numel slots: numel + min(E, numel) * (block_m - 1). */
+int64_t moe_align_capacity(int numel, int E, int block_m);
+
+/* moe_align_block_size ("[Kernel] add triton fused moe kernel for gptq/awq", PR notes: the
+ * shared-memory version for large expert counts that works under graph capture).
+ * Groups the numel = M*topk token-slots by expert and pads each group to a multiple of block_m:
+ *   sorted_token_ids device int32 [capacity] (out): for experts in ascending order, the slots of
+ *     expert e in ascending slot order, then sentinel entries (value numel) up to the next multiple
+ *     of block_m; experts with no slots take no space; entries from T to capacity are sentinels.
+ *   expert_ids device int32 [ceil(capacity / block_m)] (out): expert of each block, -1 past T.
+ *   num_tokens_post_padded device int32 [1] (out): T, the padded total (stays on the device).
+ * Ids outside [0, E) are not listed (a slot of another shard).  The result is deterministic.
+ * Limits: 1 <= E <= 1024, block_m in {16, 32, 64, 128}, numel <= 2^24,
+ * capacity >= moe_align_capacity(numel, E, block_m) (else MOE_ERR_CAPACITY). */
+int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
+                         int32_t* sorted_token_ids, int32_t* expert_ids,
+                         int32_t* num_tokens_post_padded, int64_t capacity, void* stream);
+
+/* Grouped GEMM over all experts in one launch with in-kernel weight decoding (the fused-MoE
+ * kernel of "[Kernel] add triton fused moe kernel for gptq/awq"; the K tile always equals the
+ * quantisation group, the bug reported in "[Model] Add Support for GPTQ Fused MOE" cannot occur).
+ * For every slot s listed at position p < T of sorted_token_ids, with e = expert_ids[p / block_m]:
+ *   h = A[s / a_row_div, :] . W[e]^T  (float32 accumulation of the decoded weights)
+ *   act 0: C[s, 0:N]   = h                         (C is [num_slots, N])
+ *   act 1: C[s, 0:N/2] = SiLU(h[:N/2]) * h[N/2:]   (C is [num_slots, N/2]; w13 gate/up)
+ *   then times topk_weights[s] if topk_weights is not NULL; rounded to dtype.
+ *   A      device dtype [num_a_rows, K]   (a_row_div = topk for the first GEMM of the layer,
+ *                                           1 for the second)
+ *   B, scales, zeros: weight storage of E experts with N rows and K columns (zeros NULL for int8)
+ *   sorted_token_ids/expert_ids/num_tokens_post_padded: output of moe_align_block_size
+ *     with the same block_m; capacity = length of sorted_token_ids.
+ * Rows of C whose slot is not listed are not written.
+ * Limits: K % 256 == 0, N % 128 == 0, block_m in
+ * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots. */
+int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, const void* scales,
+                   const void* zeros, const moe_quant_t* quant, int E, int N, int K, int dtype,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
+                   int num_slots, const float* topk_weights, int act, void* C, void* stream);
+
+/* Workspace bytes fused_moe_wna16 needs for these sizes (block_m 0 = library's choice). */
+size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, const moe_quant_t* quant,
+                                      int dtype, int block_m);
+
+/* The whole layer:  out[m] = sum_j w[m,j] * W2[e_mj] (SiLU(gate_e x_m) * up_e x_m), with (e_mj, w[m,j])
+ * from the routing rule applied to router_logits.
+ *   x             device dtype [M, H]
+ *   router_logits device float [M, E]
+ *   w13*          weight storage of E experts, N = 2I rows, K = H columns
+ *   w2*           weight storage of E experts, N = H rows, K = I columns
+ *   workspace     device buffer of at least fused_moe_wna16_workspace_size(...) bytes
+ *   out           device dtype [M, H]
+ *   topk_weights_out / topk_ids_out: optional device [M, topk] copies of the routing result
+ *   block_m       0 = library's choice, else one of {16, 32, 64, 128}
+ * Launches: routing, align, GEMM1 (+SiLU*up), GEMM2 (split over K into float32 partials),
+ * combine.  Deterministic: identical inputs give bitwise identical outputs.
+ * Limits: those of the calls above with N = 2I and N = H; H % 256 == 0, I % 256 == 0. */
+int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+                    const moe_routing_t* routing, const void* w13, const void* w13_scales,
+                    const void* w13_zeros, const void* w2, const void* w2_scales,
+                    const void* w2_zeros, const moe_quant_t* quant, int dtype, int block_m,
+                    void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
+                    int32_t* topk_ids_out, void* stream);
+
+/* Message for the last non-zero status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_WNA16_H */

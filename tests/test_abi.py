@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports every function include/*.h declares, and
+its host-side argument checks return the documented status codes (no call here reaches a launch)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import weight_only_int4_topk_amd as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: every call below fails validation
+NULL = None
+
+
+def _declared_functions():
+    names = []
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe_wna16.so is not built (python -m weight_only_int4_topk_amd.build)")
+    return B.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("moe_topk_softmax", "moe_align_block_size", "moe_align_capacity", "moe_wna16_gemm",
+              "fused_moe_wna16", "fused_moe_wna16_workspace_size", "moe_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+        assert n in B._SIGS, f"binding has no signature for {n}"
+
+
+def _rt(score=0, renorm=1, ng=1, tg=1, scale=1.0):
+    return ctypes.byref(B.MoeRouting(score, renorm, ng, tg, scale))
+
+
+def test_routing_validation(lib):
+    f = lib.moe_topk_softmax
+    assert f(FAKE, 4, 8, 2, None, FAKE, FAKE, NULL) == INVALID            # routing NULL
+    assert f(NULL, 4, 8, 2, _rt(), FAKE, FAKE, NULL) == INVALID           # logits NULL
+    assert f(FAKE, -1, 8, 2, _rt(), FAKE, FAKE, NULL) == INVALID
+    assert f(FAKE, 4, 2000, 2, _rt(), FAKE, FAKE, NULL) == UNSUPPORTED    # E > 1024
+    assert f(FAKE, 4, 8, 9, _rt(), FAKE, FAKE, NULL) == INVALID           # topk > E
+    assert f(FAKE, 4, 8, 2, _rt(0, 1, 2, 1), FAKE, FAKE, NULL) == UNSUPPORTED  # grouped softmax
+    assert f(FAKE, 4, 256, 8, _rt(1, 1, 7, 4), FAKE, FAKE, NULL) == INVALID    # groups !| E
+    assert f(FAKE, 4, 256, 8, _rt(1, 1, 8, 9), FAKE, FAKE, NULL) == INVALID    # topk_groups > groups
+    assert f(FAKE, 4, 16, 8, _rt(1, 1, 8, 2), FAKE, FAKE, NULL) == INVALID     # 8 > 2 groups * 2
+    assert f(FAKE, 4, 8, 9, _rt(), FAKE, FAKE, NULL) == INVALID
+    assert b"topk" in lib.moe_last_error()
+    assert f(FAKE, 4, 8, 2, _rt(5), FAKE, FAKE, NULL) == INVALID               # unknown score
+    assert b"score" in lib.moe_last_error()
+    assert f(NULL, 0, 8, 2, _rt(), NULL, NULL, NULL) == OK                      # M == 0: no-op
+
+
+def test_align_capacity_formula(lib):
+    assert lib.moe_align_capacity(8, 4, 4) == 20      # hand-worked fixture
+    assert lib.moe_align_capacity(8, 5, 2) == 13
+    assert lib.moe_align_capacity(1, 256, 16) == 16
+    assert lib.moe_align_capacity(32768, 256, 128) == 32768 + 256 * 127
+    assert lib.moe_align_capacity(-1, 4, 4) == -1
+
+
+def test_align_validation(lib):
+    f = lib.moe_align_block_size
+    assert f(FAKE, 8, 4, 48, FAKE, FAKE, FAKE, 100, NULL) == UNSUPPORTED   # block_m 48
+    assert f(FAKE, 8, 0, 16, FAKE, FAKE, FAKE, 100, NULL) == INVALID
+    assert f(FAKE, 8, 2048, 16, FAKE, FAKE, FAKE, 100, NULL) == UNSUPPORTED
+    assert f(FAKE, 8, 4, 4 * 4, NULL, FAKE, FAKE, 100, NULL) == INVALID    # sorted NULL
+    assert f(FAKE, 8, 4, 16, FAKE, FAKE, FAKE, 8 + 4 * 15 - 1, NULL) == CAPACITY
+    assert b"capacity" in lib.moe_last_error()
+    assert f(ctypes.c_void_p(0x100002), 8, 4, 16, FAKE, FAKE, FAKE, 100, NULL) == INVALID  # align
+
+
+def _q(bits, g, z):
+    return ctypes.byref(B.MoeQuant(bits, g, z))
+
+
+def _gemm(lib, **kw):
+    a = dict(A=FAKE, rows=32, div=2, Bw=FAKE, S=FAKE, Z=FAKE, q=_q(4, 128, 1), E=8, N=1024, K=256,
+             dt=0, st=FAKE, ex=FAKE, npost=FAKE, cap=152, bm=16, slots=32, tw=NULL, act=1, C=FAKE)
+    a.update(kw)
+    return lib.moe_wna16_gemm(a["A"], a["rows"], a["div"], a["Bw"], a["S"], a["Z"], a["q"], a["E"],
+                              a["N"], a["K"], a["dt"], a["st"], a["ex"], a["npost"], a["cap"],
+                              a["bm"], a["slots"], a["tw"], a["act"], a["C"], NULL)
+
+
+def test_gemm_validation(lib):
+    assert _gemm(lib, q=_q(3, 128, 1)) == UNSUPPORTED          # bits
+    assert _gemm(lib, q=_q(4, 64, 1)) == UNSUPPORTED           # K tile must be the 128 group
+    assert _gemm(lib, q=_q(4, 128, 0)) == UNSUPPORTED          # uint4 needs zero points
+    assert _gemm(lib, q=_q(8, 0, 1)) == UNSUPPORTED            # int8 is symmetric
+    assert _gemm(lib, q=_q(8, 0, 0)) == INVALID                # zeros given with has_zero = 0
+    assert _gemm(lib, Z=NULL) == INVALID                       # zeros missing with has_zero = 1
+    assert _gemm(lib, dt=2) == UNSUPPORTED
+    assert _gemm(lib, K=300) == UNSUPPORTED
+    assert _gemm(lib, N=1000) == UNSUPPORTED
+    assert _gemm(lib, bm=24) == UNSUPPORTED
+    assert _gemm(lib, act=2) == INVALID
+    assert _gemm(lib, rows=15) == INVALID                      # 15 rows * 2 < 32 slots
+    assert _gemm(lib, A=ctypes.c_void_p(0x100008)) == INVALID  # A not 16-byte aligned
+    assert _gemm(lib, Bw=NULL) == INVALID
+    assert _gemm(lib, slots=0) == OK                           # nothing to do, no launch
+
+
+def test_fused_validation_and_workspace(lib):
+    q4 = _q(4, 128, 1)
+    ws = lib.fused_moe_wna16_workspace_size(16, 256, 512, 8, 2, q4, 0, 16)
+    assert ws > 16 * 2 * 512 * 2                              # at least the intermediate rows
+    assert lib.fused_moe_wna16_workspace_size(16, 256, 512, 8, 2, q4, 0, 24) == 0
+    assert (lib.fused_moe_wna16_workspace_size(64, 4096, 14336, 8, 2, q4, 0, 0)
+            > lib.fused_moe_wna16_workspace_size(1, 4096, 14336, 8, 2, q4, 0, 0))
+
+    def fused(**kw):
+        a = dict(x=FAKE, lg=FAKE, M=16, H=256, I=512, E=8, k=2, rt=_rt(), w13=FAKE, s13=FAKE,
+                 z13=FAKE, w2=FAKE, s2=FAKE, z2=FAKE, q=q4, dt=0, bm=16, ws=FAKE, wsb=ws,
+                 out=FAKE, tw=NULL, ti=NULL)
+        a.update(kw)
+        return lib.fused_moe_wna16(a["x"], a["lg"], a["M"], a["H"], a["I"], a["E"], a["k"],
+                                   a["rt"], a["w13"], a["s13"], a["z13"], a["w2"], a["s2"],
+                                   a["z2"], a["q"], a["dt"], a["bm"], a["ws"], a["wsb"], a["out"],
+                                   a["tw"], a["ti"], NULL)
+
+    assert fused(wsb=ws - 1) == WORKSPACE
+    assert b"workspace" in lib.moe_last_error()
+    assert fused(H=320) == UNSUPPORTED
+    assert fused(I=200) == UNSUPPORTED
+    assert fused(bm=8) == UNSUPPORTED
+    assert fused(z2=NULL) == INVALID
+    assert fused(out=NULL) == INVALID
+    assert fused(ws=ctypes.c_void_p(0x100010)) == INVALID       # workspace needs 256-byte alignment
+    assert fused(rt=_rt(1, 1, 3, 1)) == INVALID
+    assert fused(M=0) == OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(ImportError):
+        B.lib()

@@ -1,0 +1,253 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on an MI355X.
+
+Bit-exact: routing ids, align outputs, decoded weights.  Layer outputs: |gpu - ref| <= 1e-2 +
+1e-2*|ref| per element plus relative L2 <= 1e-2.  Small cases compare every element and span several
+tiles with ragged tails; full-size layers (drawn on the GPU) compare sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_only_int4_topk_amd as B
+from tests.helpers import (assert_layer_close, assert_weights_close, cuda_layer, fused_vs_oracle,
+                           oracle_route, routing_of, run_fused)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+# ------------------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "qwen2", "dsv3_tp8", "dsv3_prefill_int4"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_routing_ids_exact(name, seed):
+    wl = W[name]
+    M = max(wl.Ms) if max(wl.Ms) <= 1024 else 1024
+    lg = synth.make_logits(wl, M, seed=seed)
+    tw, ti = B.moe_topk_softmax(lg.cuda(), wl.topk, routing_of(wl))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    assert_weights_close(tw, w_ref)
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("score,E,k,ng,tg", [("softmax", 64, 6, 1, 1), ("sigmoid", 96, 5, 6, 3),
+                                              ("sigmoid", 1024, 8, 8, 4), ("sigmoid", 8, 8, 1, 1)])
+def test_routing_variants(score, E, k, ng, tg, renorm):
+    wl = synth.Workload("r", E=E, H=256, I=256, topk=k, Ms=(77,), score=score, renormalize=bool(renorm),
+                        num_groups=ng, topk_groups=tg, scale=1.5)
+    lg = synth.make_logits(wl, 77, seed=3)
+    tw, ti = B.moe_topk_softmax(lg.cuda(), k, routing_of(wl))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    assert_weights_close(tw, w_ref)
+
+
+# ------------------------------------------------------------------------------------------------
+# align
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,k,E,bm", [(16, 2, 8, 16), (1, 8, 256, 16), (64, 8, 256, 16),
+                                      (256, 8, 256, 16), (512, 8, 64, 32), (4096, 8, 256, 128),
+                                      (1023, 2, 8, 64), (333, 3, 1024, 16), (5, 1, 1, 16)])
+def test_align_exact(M, k, E, bm):
+    rng = np.random.default_rng(M + E + bm)
+    ids = rng.integers(0, E, size=(M, k)).astype(np.int32)
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), E, bm)
+    r_st, r_ex, r_T = O.align_block_size(ids, E, bm)
+    assert int(npost.item()) == r_T
+    assert np.array_equal(O.to_numpy(st), r_st)
+    assert np.array_equal(O.to_numpy(ex), r_ex)
+
+
+def test_align_skewed_and_foreign_ids():
+    """All slots on one expert (many blocks), and ids outside [0, E) (not listed)."""
+    ids = np.full((300, 2), 5, np.int32)
+    ids[::7, 1] = -1
+    ids[::11, 0] = 64
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), 64, 16)
+    r_st, r_ex, r_T = O.align_block_size(ids, 64, 16)
+    assert int(npost.item()) == r_T
+    assert np.array_equal(O.to_numpy(st), r_st)
+    assert np.array_equal(O.to_numpy(ex), r_ex)
+
+
+def test_align_golden(golden):
+    g = golden("align_example.txt")
+    ids = np.array([int(v) for v in g["topk_ids"][0].split()], np.int32)
+    E = int(g["C.E"][0])
+    bm = int(g["C.block_m"][0])
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), E, bm)
+    assert O.to_numpy(st).tolist() == [int(v) for v in g["C.sorted_token_ids"][0].split()]
+    assert O.to_numpy(ex).tolist() == [int(v) for v in g["C.expert_ids"][0].split()]
+    assert int(npost.item()) == int(g["C.num_tokens_post_padded"][0])
+
+
+# ------------------------------------------------------------------------------------------------
+# decoded weights (identity probe) and the grouped GEMM
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,bits", [("fp16", 4), ("bf16", 4), ("fp16", 8), ("bf16", 8)])
+def test_dequant_identity_probe(dt, bits):
+    """One-hot activation rows routed to one expert with weight 1: GEMM row k is the decoded
+    column k of that expert, which must equal the oracle's correctly rounded (q - z) * s exactly."""
+    wl = synth.Workload("p", E=3, H=512, I=256, topk=1, Ms=(1,), dtype=dt, bits=bits)
+    layer = synth.make_layer(wl, seed=5)
+    lay = cuda_layer(layer)
+    K = wl.H
+    eye = torch.eye(K, dtype=wl.torch_dtype, device="cuda")
+    for e in range(wl.E):
+        ids = torch.full((K, 1), e, dtype=torch.int32, device="cuda")
+        st, ex, npost = B.moe_align_block_size(ids, wl.E, 16)
+        C = B.moe_wna16_gemm(eye, 1, lay["w13"], lay["w13_scales"], lay["w13_zeros"], st, ex,
+                             npost, 16, K)
+        src = O.ExpertSource(layer, bits)
+        ref_bits = O.dequant_bits(src.w13(e), dt)          # [2I, K]
+        got = C.view(torch.int16).cpu().numpy().view(np.uint16).T   # [N, K]
+        assert np.array_equal(got, ref_bits), f"expert {e}"
+
+
+@pytest.mark.parametrize("dt,bits", [("fp16", 4), ("bf16", 4), ("bf16", 8)])
+@pytest.mark.parametrize("bm", [16, 64])
+@pytest.mark.parametrize("act,weighted", [(1, False), (0, True), (0, False)])
+def test_grouped_gemm_vs_oracle(dt, bits, bm, act, weighted):
+    wl = synth.Workload("g", E=6, H=512, I=512, topk=3, Ms=(45,), dtype=dt, bits=bits)
+    layer = synth.make_layer(wl, seed=8)
+    lay = cuda_layer(layer)
+    M = 45
+    x = synth.make_x(wl, M, seed=8)
+    lg = synth.make_logits(wl, M, seed=8)
+    ids, w = oracle_route(wl, lg)
+    ns = M * wl.topk
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), wl.E, bm)
+    tw = torch.from_numpy(w.astype(np.float32)).cuda() if weighted else None
+    src = O.ExpertSource(layer, bits)
+    if act:
+        C = B.moe_wna16_gemm(x.cuda(), wl.topk, lay["w13"], lay["w13_scales"], lay["w13_zeros"],
+                             st, ex, npost, bm, ns, topk_weights=tw, act=1)
+        ref = O.grouped_gemm(x, wl.topk, src.w13, *O.align_block_size(ids, wl.E, bm), bm, ns,
+                             topk_weights=w if weighted else None, act=1)
+    else:
+        A = (torch.randn(ns, wl.I, generator=torch.Generator().manual_seed(9)) * 0.3).to(wl.torch_dtype)
+        C = B.moe_wna16_gemm(A.cuda(), 1, lay["w2"], lay["w2_scales"], lay["w2_zeros"], st, ex,
+                             npost, bm, ns, topk_weights=tw, act=0)
+        ref = O.grouped_gemm(A, 1, src.w2, *O.align_block_size(ids, wl.E, bm), bm, ns,
+                             topk_weights=w if weighted else None, act=0)
+    torch.cuda.synchronize()
+    refm = np.stack([ref[s] for s in range(ns)])
+    assert_layer_close(C, refm, f"gemm act={act}")
+
+
+# ------------------------------------------------------------------------------------------------
+# the fused layer
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fused_tiny_layer(seed):
+    out, ids, rel = fused_vs_oracle(W["tiny"], 16, seed=seed)
+    assert rel < 5e-3
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_fused_tiny_block_sizes(bm):
+    fused_vs_oracle(W["tiny"], 16, seed=0, block_m=bm)
+
+
+SMALL = {
+    "tiny_bf16": W["tiny"].with_(dtype="bf16"),
+    "tiny_int8_fp16": W["tiny"].with_(bits=8),
+    "tiny_int8_bf16": W["tiny"].with_(bits=8, dtype="bf16"),
+    "sigmoid_groups": synth.Workload("sg", E=64, H=512, I=256, topk=8, Ms=(37,), score="sigmoid",
+                                     num_groups=8, topk_groups=4, scale=2.5),
+    "softmax_bias": synth.Workload("sb", E=64, H=768, I=512, topk=8, Ms=(50,), logit_bias=True),
+    "prefill_bf16_int4": synth.Workload("pi4", E=16, H=1024, I=512, topk=4, Ms=(300,), dtype="bf16"),
+    "prefill_bf16_int8": synth.Workload("pi8", E=16, H=1024, I=512, topk=4, Ms=(300,), dtype="bf16",
+                                        bits=8),
+    "no_renorm": synth.Workload("nr", E=32, H=512, I=256, topk=4, Ms=(40,), renormalize=False),
+    "dense_single_expert": synth.Workload("d1", E=1, H=512, I=512, topk=1, Ms=(33,)),
+    "all_experts": synth.Workload("ae", E=4, H=256, I=256, topk=4, Ms=(21,)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_fused_small_variants(name):
+    wl = SMALL[name]
+    fused_vs_oracle(wl, wl.Ms[0], seed=4)
+
+
+def test_fused_one_hot_expert_load():
+    """Every token's first choice is the same expert (one expert with many blocks)."""
+    wl = synth.Workload("hot", E=8, H=512, I=256, topk=2, Ms=(200,))
+    layer = synth.make_layer(wl, seed=6)
+    x = synth.make_x(wl, 200, seed=6)
+    lg = synth.make_logits(wl, 200, seed=6)
+    lg[:, 3] += 50.0
+    out, tw, ti = run_fused(wl, x.cuda(), lg.cuda(), cuda_layer(layer))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    ref = O.moe_layer(x, ids_ref, w_ref, O.ExpertSource(layer, 4))
+    assert_layer_close(out, ref, "hot expert")
+
+
+def test_fused_single_token():
+    fused_vs_oracle(W["tiny"], 1, seed=2)
+
+
+def test_fused_deterministic_and_graph_replay():
+    wl = W["tiny"]
+    layer = cuda_layer(synth.make_layer(wl, seed=1))
+    x = synth.make_x(wl, 16, seed=1).cuda()
+    lg = synth.make_logits(wl, 16, seed=1).cuda()
+    out1, _, _ = run_fused(wl, x, lg, layer)
+    out2, _, _ = run_fused(wl, x, lg, layer)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    # capture into a graph and replay it, with eager work between replays
+    M = 16
+    ws = torch.empty((B.fused_moe_wna16_workspace_size(M, wl.H, wl.I, wl.E, wl.topk, B.QUANT_INT4,
+                                                       wl.torch_dtype, 16),), dtype=torch.uint8,
+                     device="cuda")
+    gout = torch.empty_like(out1)
+    run = lambda: B.fused_moe_wna16(x, lg, wl.topk, routing_of(wl), layer["w13"],
+                                    layer["w13_scales"], layer["w13_zeros"], layer["w2"],
+                                    layer["w2_scales"], layer["w2_zeros"], block_m=16,
+                                    workspace=ws, out=gout)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        gout.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gout.view(torch.int16), out1.view(torch.int16)), f"replay {i}"
+        run_fused(wl, x, lg, layer)  # eager work between replays
+
+
+def test_fused_empty_batch():
+    wl = W["tiny"]
+    layer = cuda_layer(synth.make_layer(wl, seed=0))
+    x = torch.empty((0, wl.H), dtype=torch.float16, device="cuda")
+    lg = torch.empty((0, wl.E), dtype=torch.float32, device="cuda")
+    out = B.fused_moe_wna16(x, lg, wl.topk, routing_of(wl), layer["w13"], layer["w13_scales"],
+                            layer["w13_zeros"], layer["w2"], layer["w2_scales"], layer["w2_zeros"],
+                            workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    assert out.shape == (0, wl.H)
+
+
+# ------------------------------------------------------------------------------------------------
+# full-size layers (drawn on the GPU), sampled tokens against the oracle
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name,M", [("mixtral", 64), ("mixtral", 1), ("qwen2", 512), ("dsv3_tp8", 256),
+                                    ("dsv3_tp8", 1), ("dsv3_prefill_int4", 4096),
+                                    ("dsv3_prefill_int8", 1024)])
+def test_fused_full_size_sampled(name, M):
+    wl = W[name]
+    rows = sorted({0, M // 2, M - 1})
+    out, ids, rel = fused_vs_oracle(wl, M, seed=0, device="cuda", rows=rows)
+    # align of the full routing result is exact too
+    bm = 16
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), wl.E, bm)
+    r_st, r_ex, r_T = O.align_block_size(ids, wl.E, bm)
+    assert int(npost.item()) == r_T and np.array_equal(O.to_numpy(st), r_st)
+    assert torch.isfinite(out.float()).all()

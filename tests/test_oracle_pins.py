@@ -197,7 +197,7 @@ def test_route_sigmoid_single_group_is_plain_topk():
 def test_align_golden(golden):
     g = golden("align_example.txt")
     ids = np.array([int(v) for v in g["topk_ids"][0].split()], np.int32).reshape(-1, 2)
-    for case in ("A", "B"):
+    for case in ("A", "B", "C"):
         E = int(g[f"{case}.E"][0])
         bm = int(g[f"{case}.block_m"][0])
         st, ex, T = O.align_block_size(ids, E, bm)

@@ -1,0 +1,189 @@
+"""Python binding of the moe_wna16 C ABI (include/moe_wna16.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of libmoe_wna16.so.
+torch provides device memory and the current stream; this module passes pointers, sizes and the
+stream handle, allocates outputs the caller did not provide, and turns a non-zero status into a
+MoeError.  There is no fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MoeError", "lib", "QUANT_INT4", "QUANT_INT8", "routing", "moe_topk_softmax",
+    "moe_align_capacity", "moe_align_block_size", "moe_wna16_gemm",
+    "fused_moe_wna16_workspace_size", "fused_moe_wna16", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wna16.so")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"moe_wna16 status {status}: {message}")
+        self.status = status
+
+
+class MoeQuant(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("has_zero", ctypes.c_int32)]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [("score", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("num_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+QUANT_INT4 = MoeQuant(4, 128, 1)
+QUANT_INT8 = MoeQuant(8, 0, 0)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SIGS = {
+    "moe_last_error": ([], ctypes.c_char_p),
+    "moe_topk_softmax": ([_P, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P], _I),
+    "moe_align_capacity": ([_I, _I, _I], _I64),
+    "moe_align_block_size": ([_P, _I, _I, _I, _P, _P, _P, _I64, _P], _I),
+    "moe_wna16_gemm": ([_P, _I, _I, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _I, _I,
+                        _P, _P, _P, _I64, _I, _I, _P, _I, _P, _P], _I),
+    "fused_moe_wna16_workspace_size": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I],
+                                       ctypes.c_size_t),
+    "fused_moe_wna16": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P, _P,
+                         _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _P, ctypes.c_size_t, _P, _P,
+                         _P, _P], _I),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m weight_only_int4_topk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoeError(-1, "tensor is not on a GPU device")
+    if not t.is_contiguous():
+        raise MoeError(-1, "tensor is not contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float16:
+        return 0
+    if dt == torch.bfloat16:
+        return 1
+    raise MoeError(-2, f"unsupported activation dtype {dt}")
+
+
+def _quant_of(B: torch.Tensor, zeros) -> MoeQuant:
+    if B.dtype == torch.uint8 and zeros is not None:
+        return QUANT_INT4
+    if B.dtype == torch.int8 and zeros is None:
+        return QUANT_INT8
+    raise MoeError(-2, f"weights of dtype {B.dtype} with zeros={'set' if zeros is not None else 'None'}")
+
+
+def routing(score="softmax", renormalize=True, num_groups=1, topk_groups=1, scale=1.0) -> MoeRouting:
+    return MoeRouting(0 if score == "softmax" else 1, int(bool(renormalize)), num_groups,
+                      topk_groups, float(scale))
+
+
+def moe_topk_softmax(logits, topk, rt: MoeRouting, topk_weights=None, topk_ids=None, stream=None):
+    M, E = logits.shape
+    if topk_weights is None:
+        topk_weights = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
+    if topk_ids is None:
+        topk_ids = torch.empty((M, topk), dtype=torch.int32, device=logits.device)
+    _check(lib().moe_topk_softmax(_ptr(logits), M, E, topk, ctypes.byref(rt), _ptr(topk_weights),
+                                  _ptr(topk_ids), _stream(stream)))
+    return topk_weights, topk_ids
+
+
+def moe_align_capacity(numel, E, block_m) -> int:
+    return int(lib().moe_align_capacity(numel, E, block_m))
+
+
+def moe_align_block_size(topk_ids, E, block_m, capacity=None, stream=None):
+    numel = topk_ids.numel()
+    cap = moe_align_capacity(numel, E, block_m) if capacity is None else capacity
+    dev = topk_ids.device
+    sorted_ids = torch.empty((cap,), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(((cap + block_m - 1) // block_m,), dtype=torch.int32, device=dev)
+    num_post = torch.empty((1,), dtype=torch.int32, device=dev)
+    _check(lib().moe_align_block_size(_ptr(topk_ids), numel, E, block_m, _ptr(sorted_ids),
+                                      _ptr(expert_ids), _ptr(num_post), cap, _stream(stream)))
+    return sorted_ids, expert_ids, num_post
+
+
+def moe_wna16_gemm(A, a_row_div, B, scales, zeros, sorted_ids, expert_ids, num_post, block_m,
+                   num_slots, topk_weights=None, act=0, C=None, stream=None):
+    quant = _quant_of(B, zeros)
+    E, N = B.shape[0], B.shape[1]
+    K = B.shape[2] * (2 if quant.bits == 4 else 1)
+    n_out = N // 2 if act == 1 else N
+    if C is None:
+        C = torch.empty((num_slots, n_out), dtype=A.dtype, device=A.device)
+    _check(lib().moe_wna16_gemm(_ptr(A), A.shape[0], a_row_div, _ptr(B), _ptr(scales), _ptr(zeros),
+                                ctypes.byref(quant), E, N, K, _dtype_code(A.dtype),
+                                _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post),
+                                sorted_ids.numel(), block_m, num_slots, _ptr(topk_weights), act,
+                                _ptr(C), _stream(stream)))
+    return C
+
+
+def fused_moe_wna16_workspace_size(M, H, I, E, topk, quant: MoeQuant, dtype, block_m=0) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().fused_moe_wna16_workspace_size(M, H, I, E, topk, ctypes.byref(quant), code,
+                                                    block_m))
+
+
+def fused_moe_wna16(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w13_zeros, w2,
+                    w2_scales, w2_zeros, block_m=0, workspace=None, out=None, topk_weights=None,
+                    topk_ids=None, stream=None):
+    """The whole layer; returns out [M, H] (and writes topk_weights / topk_ids if given)."""
+    quant = _quant_of(w13, w13_zeros)
+    M, H = x.shape
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    need = fused_moe_wna16_workspace_size(M, H, I, E, topk, quant, x.dtype, block_m)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=x.dtype, device=x.device)
+    _check(lib().fused_moe_wna16(_ptr(x), _ptr(router_logits), M, H, I, E, topk, ctypes.byref(rt),
+                                 _ptr(w13), _ptr(w13_scales), _ptr(w13_zeros), _ptr(w2),
+                                 _ptr(w2_scales), _ptr(w2_zeros), ctypes.byref(quant),
+                                 _dtype_code(x.dtype), block_m, _ptr(workspace),
+                                 workspace.numel(), _ptr(out), _ptr(topk_weights),
+                                 _ptr(topk_ids), _stream(stream)))
+    return out

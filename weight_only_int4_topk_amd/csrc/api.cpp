@@ -1,0 +1,344 @@
+// C ABI of the moe_wna16 library: argument checks (host only, no device access), the tile plan,
+// the workspace layout of the fused layer, and the launch sequence.  Declarations and the full
+// contract of every entry point are in include/moe_wna16.h.
+#include "moe_wna16.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int check_dtype(int dtype) {
+  if (dtype != MOE_DTYPE_FP16 && dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "dtype %d is not fp16 (0) or bf16 (1)", dtype);
+  return MOE_OK;
+}
+
+int check_quant(const moe_quant_t* q) {
+  if (!q) return fail(MOE_ERR_INVALID_ARG, "quant is NULL");
+  if (q->bits == 4) {
+    if (q->group_size != 128)
+      return fail(MOE_ERR_UNSUPPORTED, "uint4 weights need group_size 128 (got %d)", q->group_size);
+    if (!q->has_zero)
+      return fail(MOE_ERR_UNSUPPORTED, "uint4 weights need integer zero points (has_zero = 1)");
+    return MOE_OK;
+  }
+  if (q->bits == 8) {
+    if (q->group_size != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "int8 weights use one scale per output channel (group_size 0)");
+    if (q->has_zero)
+      return fail(MOE_ERR_UNSUPPORTED, "int8 weights are symmetric (has_zero = 0)");
+    return MOE_OK;
+  }
+  return fail(MOE_ERR_UNSUPPORTED, "bits = %d (supported: 4, 8)", q->bits);
+}
+
+int check_routing(const moe_routing_t* r, int E, int topk) {
+  if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  if (E <= 0 || topk <= 0) return fail(MOE_ERR_INVALID_ARG, "E = %d, topk = %d", E, topk);
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 1024", E);
+  if (topk > E || topk > 32)
+    return fail(MOE_ERR_INVALID_ARG, "topk = %d must be <= min(E, 32)", topk);
+  if (r->score == MOE_SCORE_SOFTMAX) {
+    if (r->num_groups != 1)
+      return fail(MOE_ERR_UNSUPPORTED, "softmax routing takes num_groups = 1 (got %d)", r->num_groups);
+    return MOE_OK;
+  }
+  if (r->score != MOE_SCORE_SIGMOID) return fail(MOE_ERR_INVALID_ARG, "score = %d", r->score);
+  if (r->num_groups < 1 || r->num_groups > 64 || E % r->num_groups)
+    return fail(MOE_ERR_INVALID_ARG, "num_groups = %d must divide E = %d and be <= 64",
+                r->num_groups, E);
+  if (r->topk_groups < 1 || r->topk_groups > r->num_groups)
+    return fail(MOE_ERR_INVALID_ARG, "topk_groups = %d not in [1, num_groups]", r->topk_groups);
+  if (topk > r->topk_groups * (E / r->num_groups))
+    return fail(MOE_ERR_INVALID_ARG, "topk = %d exceeds the experts of %d kept groups", topk,
+                r->topk_groups);
+  return MOE_OK;
+}
+
+int64_t align_capacity(int64_t numel, int E, int bm) {
+  return numel + std::min<int64_t>(E, numel) * (bm - 1);
+}
+
+// ------------------------------------------------------------------------------------------------
+// tile plan of the fused layer
+// ------------------------------------------------------------------------------------------------
+struct Plan {
+  int bm;
+  int64_t cap;
+  int nblk;
+  int split2;
+  size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
+};
+
+int pick_block_m(int M, int topk, int E) {
+  const int64_t slots = (int64_t)M * topk;
+  const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, slots));
+  const int64_t avg = (slots + active - 1) / active;
+  const int64_t need = avg + avg / 2;
+  for (int bm : {16, 32, 64, 128})
+    if (need <= bm) return bm;
+  return 128;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int block_m) {
+  (void)dtype;
+  Plan p{};
+  const int64_t slots = (int64_t)M * topk;
+  p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E);
+  p.cap = align_capacity(slots, E, p.bm);
+  p.nblk = (int)((p.cap + p.bm - 1) / p.bm);
+  // split the second GEMM (K = I) until there are enough workgroups to fill the chip
+  const int kb = bits == 4 ? 128 : 64;
+  const int kb_total = I / kb;
+  const int64_t est_blocks = std::max<int64_t>(std::min<int64_t>(E, slots), slots / p.bm);
+  const int64_t wgs = est_blocks * (H / 128);
+  int split = 1;
+  while (kb_total % (2 * split) == 0 && wgs * split < 2048) split *= 2;
+  p.split2 = split;
+  size_t off = 0;
+  p.off_w = off;      off += up256((size_t)slots * 4);
+  p.off_ids = off;    off += up256((size_t)slots * 4);
+  p.off_sorted = off; off += up256((size_t)p.cap * 4);
+  p.off_eids = off;   off += up256((size_t)p.nblk * 4);
+  p.off_npost = off;  off += 256;
+  p.off_inter = off;  off += up256((size_t)slots * I * 2);
+  p.off_part = off;   off += up256((size_t)split * slots * H * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int64_t moe_align_capacity(int numel, int E, int block_m) {
+  if (numel < 0 || E <= 0 || block_m <= 0) return -1;
+  return align_capacity(numel, E, block_m);
+}
+
+int moe_topk_softmax(const float* logits, int M, int E, int topk, const moe_routing_t* routing,
+                     float* topk_weights, int32_t* topk_ids, void* stream) {
+  if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M = %d", M);
+  if (int rc = check_routing(routing, E, topk)) return rc;
+  if (M == 0) return MOE_OK;
+  if (!logits || !topk_weights || !topk_ids)
+    return fail(MOE_ERR_INVALID_ARG, "NULL logits / topk_weights / topk_ids");
+  if (!aligned(logits, 4) || !aligned(topk_weights, 4) || !aligned(topk_ids, 4))
+    return fail(MOE_ERR_INVALID_ARG, "routing buffers must be 4-byte aligned");
+  const moe::RoutingParams rp{routing->score, routing->renormalize, routing->num_groups,
+                              routing->topk_groups, routing->scale};
+  hipError_t e = moe::launch_routing(logits, M, E, topk, rp, topk_weights, topk_ids,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "routing launch");
+}
+
+int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
+                         int32_t* sorted_token_ids, int32_t* expert_ids,
+                         int32_t* num_tokens_post_padded, int64_t capacity, void* stream) {
+  if (numel < 0 || E <= 0) return fail(MOE_ERR_INVALID_ARG, "numel = %d, E = %d", numel, E);
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 1024", E);
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
+  if (numel > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "numel = %d > 2^24", numel);
+  if ((numel > 0 && !topk_ids) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
+    return fail(MOE_ERR_INVALID_ARG, "NULL align buffer");
+  if (!aligned(topk_ids, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_post_padded, 4))
+    return fail(MOE_ERR_INVALID_ARG, "align buffers must be 4-byte aligned");
+  const int64_t need = align_capacity(numel, E, block_m);
+  if (capacity < need)
+    return fail(MOE_ERR_CAPACITY, "capacity %lld < %lld needed", (long long)capacity,
+                (long long)need);
+  if (capacity > (int64_t)1 << 30) return fail(MOE_ERR_UNSUPPORTED, "capacity too large");
+  hipError_t e = moe::launch_align(topk_ids, numel, E, block_m, sorted_token_ids, expert_ids,
+                                   num_tokens_post_padded, capacity, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "align launch");
+}
+
+static int check_weights(const void* B, const void* scales, const void* zeros,
+                         const moe_quant_t* q) {
+  if (!B || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL weight or scale pointer");
+  if (q->has_zero && !zeros) return fail(MOE_ERR_INVALID_ARG, "zeros are NULL but has_zero = 1");
+  if (!q->has_zero && zeros)
+    return fail(MOE_ERR_INVALID_ARG, "zeros given but has_zero = 0 (both or neither)");
+  if (!aligned(B, 16)) return fail(MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  if (!aligned(scales, 2)) return fail(MOE_ERR_INVALID_ARG, "scales must be 2-byte aligned");
+  return MOE_OK;
+}
+
+int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, const void* scales,
+                   const void* zeros, const moe_quant_t* quant, int E, int N, int K, int dtype,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
+                   int num_slots, const float* topk_weights, int act, void* C, void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (int rc = check_quant(quant)) return rc;
+  if (E <= 0 || N <= 0 || K <= 0 || num_a_rows < 0 || a_row_div <= 0 || num_slots < 0 ||
+      capacity < 0)
+    return fail(MOE_ERR_INVALID_ARG, "E=%d N=%d K=%d rows=%d a_row_div=%d slots=%d", E, N, K,
+                num_a_rows, a_row_div, num_slots);
+  if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL)
+    return fail(MOE_ERR_INVALID_ARG, "act = %d", act);
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
+  if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
+  if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
+  if ((int64_t)num_a_rows * a_row_div < num_slots)
+    return fail(MOE_ERR_INVALID_ARG, "A has %d rows, slots need %lld", num_a_rows,
+                (long long)((num_slots + a_row_div - 1) / a_row_div));
+  if (int rc = check_weights(B, scales, zeros, quant)) return rc;
+  if (!A || !C || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
+    return fail(MOE_ERR_INVALID_ARG, "NULL A / C / align buffer");
+  if (!aligned(A, 16) || !aligned(C, 16))
+    return fail(MOE_ERR_INVALID_ARG, "A and C must be 16-byte aligned");
+  if (topk_weights && !aligned(topk_weights, 4))
+    return fail(MOE_ERR_INVALID_ARG, "topk_weights must be 4-byte aligned");
+  if (num_slots == 0 || capacity == 0) return MOE_OK;
+  moe::GemmParams p{};
+  p.A = A;
+  p.a_row_div = a_row_div;
+  p.B = (const uint8_t*)B;
+  p.scales = scales;
+  p.zeros = (const uint8_t*)zeros;
+  p.E = E;
+  p.N = N;
+  p.K = K;
+  p.sorted_ids = sorted_token_ids;
+  p.expert_ids = expert_ids;
+  p.num_post = num_tokens_post_padded;
+  // T is a multiple of block_m and <= capacity, so whole blocks below capacity cover every real
+  // block; a corrupt num_tokens_post_padded then cannot push reads past sorted_token_ids
+  p.num_blocks = (int)(capacity / block_m);
+  p.num_slots = num_slots;
+  p.topk_w = topk_weights;
+  p.C = C;
+  p.split_k = 1;
+  const moe::GemmConfig c{dtype, quant->bits, block_m, act, 0};
+  hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm launch");
+}
+
+size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
+                                      const moe_quant_t* quant, int dtype, int block_m) {
+  if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || !quant) return 0;
+  if (block_m != 0 && !valid_block_m(block_m)) return 0;
+  return make_plan(M, H, I, E, topk, quant->bits, dtype, block_m).total;
+}
+
+int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+                    const moe_routing_t* routing, const void* w13, const void* w13_scales,
+                    const void* w13_zeros, const void* w2, const void* w2_scales,
+                    const void* w2_zeros, const moe_quant_t* quant, int dtype, int block_m,
+                    void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
+                    int32_t* topk_ids_out, void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (int rc = check_quant(quant)) return rc;
+  if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d H=%d I=%d", M, H, I);
+  if (int rc = check_routing(routing, E, topk)) return rc;
+  if (block_m != 0 && !valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128)", block_m);
+  if (H % 256 || I % 256)
+    return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
+  if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");
+  if (M == 0) return MOE_OK;
+  if (int rc = check_weights(w13, w13_scales, w13_zeros, quant)) return rc;
+  if (int rc = check_weights(w2, w2_scales, w2_zeros, quant)) return rc;
+  if (!x || !router_logits || !out || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "NULL x / router_logits / out / workspace");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256) || !aligned(router_logits, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x/out need 16-byte, workspace 256-byte alignment");
+  if ((topk_weights_out && !aligned(topk_weights_out, 4)) ||
+      (topk_ids_out && !aligned(topk_ids_out, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "routing outputs must be 4-byte aligned");
+  const Plan pl = make_plan(M, H, I, E, topk, quant->bits, dtype, block_m);
+  if (workspace_bytes < pl.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.total);
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* tw = topk_weights_out ? topk_weights_out : (float*)(ws + pl.off_w);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(ws + pl.off_ids);
+  int32_t* sorted = (int32_t*)(ws + pl.off_sorted);
+  int32_t* eids = (int32_t*)(ws + pl.off_eids);
+  int32_t* npost = (int32_t*)(ws + pl.off_npost);
+  void* inter = ws + pl.off_inter;
+  float* part = (float*)(ws + pl.off_part);
+  const int slots = M * topk;
+
+  const moe::RoutingParams rp{routing->score, routing->renormalize, routing->num_groups,
+                              routing->topk_groups, routing->scale};
+  hipError_t e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
+  if (e != hipSuccess) return hip_fail(e, "routing launch");
+  e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
+  if (e != hipSuccess) return hip_fail(e, "align launch");
+
+  moe::GemmParams g1{};
+  g1.A = x;
+  g1.a_row_div = topk;
+  g1.B = (const uint8_t*)w13;
+  g1.scales = w13_scales;
+  g1.zeros = (const uint8_t*)w13_zeros;
+  g1.E = E;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.sorted_ids = sorted;
+  g1.expert_ids = eids;
+  g1.num_post = npost;
+  g1.num_blocks = (int)(pl.cap / pl.bm);
+  g1.num_slots = slots;
+  g1.topk_w = nullptr;
+  g1.C = inter;
+  g1.split_k = 1;
+  e = moe::launch_gemm(g1, moe::GemmConfig{dtype, quant->bits, pl.bm, 1, 0}, st);
+  if (e != hipSuccess) return hip_fail(e, "gemm1 launch");
+
+  moe::GemmParams g2 = g1;
+  g2.A = inter;
+  g2.a_row_div = 1;
+  g2.B = (const uint8_t*)w2;
+  g2.scales = w2_scales;
+  g2.zeros = (const uint8_t*)w2_zeros;
+  g2.N = H;
+  g2.K = I;
+  g2.C = part;
+  g2.split_k = pl.split2;
+  e = moe::launch_gemm(g2, moe::GemmConfig{dtype, quant->bits, pl.bm, 0, 1}, st);
+  if (e != hipSuccess) return hip_fail(e, "gemm2 launch");
+
+  e = moe::launch_combine(part, pl.split2, tw, M, topk, H, dtype, out, st);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Host-side launchers implemented by the .hip translation units; the C ABI in api.cpp validates
+// arguments and then calls these.  Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RoutingParams {
+  int score;        // 0 softmax, 1 sigmoid
+  int renormalize;
+  int num_groups;
+  int topk_groups;
+  float scale;
+};
+
+hipError_t launch_routing(const float* logits, int M, int E, int topk, const RoutingParams& p,
+                          float* topk_w, int32_t* topk_ids, hipStream_t stream);
+
+hipError_t launch_align(const int32_t* topk_ids, int numel, int E, int block_m,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post,
+                        int64_t capacity, hipStream_t stream);
+
+struct GemmParams {
+  const void* A;              // dtype [rows, K]
+  int a_row_div;
+  const uint8_t* B;           // int4: uint8 [E, N, K/2]; int8: int8 [E, N, K]
+  const void* scales;         // int4: [E, N, K/128]; int8: [E, N]
+  const uint8_t* zeros;       // int4: uint8 [E, N, K/256]; int8: unused
+  int E, N, K;
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* num_post;
+  int num_blocks;             // floor(capacity / block_m): grid extent over blocks
+  int num_slots;              // sentinel value (M * topk)
+  const float* topk_w;        // nullable: scale output row s by topk_w[s]
+  void* C;                    // act: dtype [num_slots, N/2]; out_f32: float [split, num_slots, N];
+                              // else dtype [num_slots, N]
+  int split_k;                // K split count (out_f32 only, else 1)
+};
+
+struct GemmConfig {
+  int dtype;     // 0 fp16, 1 bf16
+  int bits;      // 4 or 8
+  int block_m;   // 16, 32, 64, 128
+  int act;       // 0 none, 1 silu-mul
+  int out_f32;   // 1: float partials [split, num_slots, N]
+};
+
+// Columns of output one workgroup covers (N % this must be 0; act: gate columns).
+int gemm_wg_cols(const GemmConfig& c);
+hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
+
+hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
+                          int H, int dtype, void* out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,208 @@
+// Top-k routing on gfx950: one 64-lane wavefront per token, four tokens per workgroup.
+//
+// Softmax rule: ids are the topk largest logits (ties to the lower expert id); ranking logits ranks
+// softmax probabilities without any rounding, so ids are exact.  Sigmoid rule (DeepSeek-V3 style):
+// scores s = 1/(1+e^-x) computed with a fully specified float32 exp so that every IEEE-754
+// implementation gets the same bits, group score = sum of the two largest s of a contiguous group,
+// keep topk_groups groups, then the topk largest s inside them.  The pages do not describe the
+// routing; this is the rule of the Mixtral-, Qwen2- and DeepSeek-V3-shaped layers the library serves.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTokensPerWG = 4;
+constexpr int kMaxEPL = 16;  // experts per lane: E <= 1024
+
+// e^x in float32: clamp to [-80, 80]; n = rint(x * log2 e); r = (x - n*C1) - n*C2 with
+// C1 = 355/512 (exact, so n*C1 is exact) and C2 = ln 2 - C1 rounded to float32 (Cody & Waite's
+// two-constant reduction); p = Taylor polynomial of degree 7 in Horner form with coefficients 1/i!
+// rounded to float32; result p * 2^n.  Each operation is a separately rounded float32 operation.
+__device__ float exp_spec(float x) {
+#pragma clang fp contract(off)
+  const float kLog2e = 0x1.715476p+0f;
+  const float kC1 = 0x1.63p-1f;
+  const float kC2 = -0x1.bd0106p-13f;
+  x = fminf(fmaxf(x, -80.0f), 80.0f);
+  const float n = __builtin_rintf(x * kLog2e);
+  const float r = (x - n * kC1) - n * kC2;
+  float p = 0x1.a01a02p-13f;   // 1/7!
+  p = p * r + 0x1.6c16c2p-10f; // 1/6!
+  p = p * r + 0x1.111112p-7f;  // 1/5!
+  p = p * r + 0x1.555556p-5f;  // 1/4!
+  p = p * r + 0x1.555556p-3f;  // 1/3!
+  p = p * r + 0x1.0p-1f;       // 1/2!
+  p = p * r + 1.0f;            // 1/1!
+  p = p * r + 1.0f;            // 1/0!
+  return ldexpf(p, (int)n);
+}
+
+__device__ float sigmoid_spec(float x) {
+#pragma clang fp contract(off)
+  const float e = exp_spec(-x);
+  return 1.0f / (1.0f + e);  // correctly rounded division (HIP default)
+}
+
+template <int EPL>
+__global__ void __launch_bounds__(256) routing_kernel(const float* __restrict__ logits, int M, int E,
+                                                      int topk, RoutingParams p,
+                                                      float* __restrict__ out_w,
+                                                      int32_t* __restrict__ out_ids) {
+  __shared__ float s_score[kTokensPerWG][EPL * kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int token = blockIdx.x * kTokensPerWG + wid;
+  if (token >= M) return;
+  const float* row = logits + (size_t)token * E;
+  const float kNone = -__builtin_inff();
+
+  // expert e = lane + 64*i lives in v[i]
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < E ? row[e] : kNone;
+  }
+
+  uint32_t taken[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) taken[i] = 0;
+  // lane j (< topk) keeps the j-th winner; every lane sees every winner through the reduction
+  float my_val = 0.0f;
+  int my_id = 0;
+  float denom = 0.0f;
+
+  if (p.score == 0) {
+    // softmax: rank raw logits; the first winner is the maximum logit
+    float mx = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+      float bv = kNone;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E && !taken[i] && better(v[i], e, bv, bi)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+      wave_argbest(bv, bi);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i == bi) taken[i] = 1;
+      if (j == 0) mx = bv;
+      const float ej = expf(bv - mx);
+      denom += ej;
+      if (lane == j) {
+        my_val = ej;
+        my_id = bi;
+      }
+    }
+    if (!p.renormalize) {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) part += expf(v[i] - mx);
+      denom = wave_sum(part);
+    }
+    if (lane < topk) {
+      out_w[(size_t)token * topk + lane] = my_val / denom * p.scale;
+      out_ids[(size_t)token * topk + lane] = my_id;
+    }
+    return;
+  }
+
+  // sigmoid scores (exact spec)
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + kWave * i < E) v[i] = sigmoid_spec(v[i]);
+
+  const int ng = p.num_groups;
+  const int gs = E / ng;
+  uint64_t kept = ~0ull;
+  if (p.topk_groups < ng) {
+    // publish scores to LDS; lane g < ng scores group g by the sum of its two largest values
+    float* sc = s_score[wid];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E) sc[e] = v[i];
+    }
+    __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in program order
+    float gscore = kNone;
+    if (lane < ng) {
+      float b1 = kNone, b2 = kNone;
+      for (int t = 0; t < gs; ++t) {
+        const float s = sc[lane * gs + t];
+        if (s > b1) {
+          b2 = b1;
+          b1 = s;
+        } else if (s > b2) {
+          b2 = s;
+        }
+      }
+      gscore = gs >= 2 ? b1 + b2 : b1;
+    }
+    // keep the topk_groups best groups (ties -> lower group id)
+    kept = 0;
+    bool gtaken = false;
+    for (int r = 0; r < p.topk_groups; ++r) {
+      float bv = (lane < ng && !gtaken) ? gscore : kNone;
+      int bi = (lane < ng && !gtaken) ? lane : 0x7fffffff;
+      wave_argbest(bv, bi);
+      kept |= 1ull << bi;
+      if (lane == bi) gtaken = true;
+    }
+  }
+  // topk largest scores inside kept groups (ties -> lower expert id)
+  for (int j = 0; j < topk; ++j) {
+    float bv = kNone;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && !taken[i] && ((kept >> (e / gs)) & 1ull) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    wave_argbest(bv, bi);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i == bi) taken[i] = 1;
+    denom += bv;
+    if (lane == j) {
+      my_val = bv;
+      my_id = bi;
+    }
+  }
+  if (!p.renormalize) denom = 1.0f;
+  if (lane < topk) {
+    out_w[(size_t)token * topk + lane] = my_val / denom * p.scale;
+    out_ids[(size_t)token * topk + lane] = my_id;
+  }
+}
+
+template <int EPL>
+hipError_t launch_epl(const float* logits, int M, int E, int topk, const RoutingParams& p,
+                      float* w, int32_t* ids, hipStream_t stream) {
+  const int grid = (M + kTokensPerWG - 1) / kTokensPerWG;
+  hipLaunchKernelGGL(routing_kernel<EPL>, dim3(grid), dim3(kTokensPerWG * kWave), 0, stream, logits,
+                     M, E, topk, p, w, ids);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_routing(const float* logits, int M, int E, int topk, const RoutingParams& p,
+                          float* topk_w, int32_t* topk_ids, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (E <= 64) return launch_epl<1>(logits, M, E, topk, p, topk_w, topk_ids, stream);
+  if (E <= 128) return launch_epl<2>(logits, M, E, topk, p, topk_w, topk_ids, stream);
+  if (E <= 256) return launch_epl<4>(logits, M, E, topk, p, topk_w, topk_ids, stream);
+  if (E <= 512) return launch_epl<8>(logits, M, E, topk, p, topk_w, topk_ids, stream);
+  return launch_epl<kMaxEPL>(logits, M, E, topk, p, topk_w, topk_ids, stream);
+}
+
+}  // namespace moe
