@@ -1,0 +1,275 @@
+#!/usr/bin/env python
+"""Throughput of the fused MoE layer with uint4/int8 experts on one MI355X; prints one JSON line.
+
+A step is one call of the whole layer (routing, align, w13 grouped GEMM + SiLU*up, w2 grouped GEMM,
+weighted combine) on one batch of M tokens whose inputs are already in HBM.  `value` is tokens/s
+over exactly --steps steps.  The layer exists in L device copies that the steps cycle through, as a
+model's layer stack would, so that the experts a step reads have been evicted from the 256 MiB
+Infinity Cache by the time the same copy comes round again.  Steps are replayed from HIP graphs
+that hold several consecutive layer calls.
+
+Also reported: the roofline of the dominant kernel (the w13 grouped GEMM with the SiLU epilogue),
+timed alone with HIP events on the stream it is launched on; an M sweep of the workload; and the
+CPU oracle's throughput on a bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 MFMA
+MIB = 1 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--m", type=int, default=0, help="tokens per step (default: largest decode M)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--sweep-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, wl, seed):
+        import torch
+
+        import synth
+        import weight_only_int4_topk_amd as B
+        self.torch, self.synth, self.B = torch, synth, B
+        self.wl = wl
+        self.seed = seed
+        t0 = time.perf_counter()
+        self.layer = synth.make_layer(wl, seed=seed, device="cuda")
+        torch.cuda.synchronize()
+        self.layer_bytes = sum(v.numel() * v.element_size() for v in self.layer.values()
+                               if v is not None)
+        log(f"[bench] drew {wl.name} layer ({self.layer_bytes / MIB:.0f} MiB) in "
+            f"{time.perf_counter() - t0:.1f}s")
+        self.copies = [self.layer]
+        self.rt = B.routing(wl.score, wl.renormalize, wl.num_groups, wl.topk_groups, wl.scale)
+
+    def ensure_copies(self, L):
+        while len(self.copies) < L:
+            self.copies.append({k: (v.clone() if v is not None else None)
+                                for k, v in self.layer.items()})
+
+    def n_copies(self, active_bytes):
+        # between two uses of a copy, (L - 1) * active_bytes >= 512 MiB (twice the Infinity Cache)
+        L = max(2, min(64, math.ceil(512 * MIB / max(active_bytes, 1)) + 1))
+        cap = max(2, int((64 << 30) // self.layer_bytes))
+        return min(L, cap)
+
+    def _graph_steps(self, fns, steps, warmup):
+        """Replay `steps` calls cycling through fns (one per layer copy), in graphs of G calls."""
+        torch = self.torch
+        L = len(fns)
+        G = L * max(1, 16 // L)
+        for f in fns:                          # compile/warm every code path eagerly first
+            f()
+        torch.cuda.synchronize()
+        chunk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(chunk):
+            for i in range(G):
+                fns[i % L]()
+        singles = []
+        for f in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            singles.append(g)
+
+        def run(n):
+            done = 0
+            while n - done >= G:
+                chunk.replay()
+                done += G
+            while done < n:
+                singles[done % L].replay()
+                done += 1
+
+        run(warmup)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        t0 = time.perf_counter()
+        run(steps)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(end) / 1e3, wall, G
+
+    def measure(self, M, steps, warmup):
+        torch, synth, B, wl = self.torch, self.synth, self.B, self.wl
+        x = synth.make_x(wl, M, seed=self.seed, device="cuda")
+        lg = synth.make_logits(wl, M, seed=self.seed, device="cuda")
+        tw, ti = B.moe_topk_softmax(lg, wl.topk, self.rt)
+        torch.cuda.synchronize()
+        active = int(torch.unique(ti).numel())
+        act_bytes = active * synth.weight_bytes_per_expert(wl)
+        w13_bytes = active * synth.w13_bytes_per_expert(wl)
+        L = self.n_copies(act_bytes)
+        self.ensure_copies(L)
+        bm = B.moe_pick_block_m(M, wl.E, wl.topk)
+        quant = B.QUANT_INT4 if wl.bits == 4 else B.QUANT_INT8
+        ws = torch.empty((B.fused_moe_wna16_workspace_size(M, wl.H, wl.I, wl.E, wl.topk, quant,
+                                                           wl.torch_dtype, 0),),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((M, wl.H), dtype=wl.torch_dtype, device="cuda")
+
+        def layer_fn(c):
+            return lambda: B.fused_moe_wna16(x, lg, wl.topk, self.rt, c["w13"], c["w13_scales"],
+                                             c["w13_zeros"], c["w2"], c["w2_scales"],
+                                             c["w2_zeros"], block_m=0, workspace=ws, out=out)
+
+        t_layer, wall, G = self._graph_steps([layer_fn(c) for c in self.copies[:L]], steps, warmup)
+
+        # the dominant kernel alone: w13 grouped GEMM with the SiLU epilogue, same tiles
+        st, ex, npost = B.moe_align_block_size(ti, wl.E, bm)
+        inter = torch.empty((M * wl.topk, wl.I), dtype=wl.torch_dtype, device="cuda")
+
+        def gemm1_fn(c):
+            return lambda: B.moe_wna16_gemm(x, wl.topk, c["w13"], c["w13_scales"], c["w13_zeros"],
+                                            st, ex, npost, bm, M * wl.topk, act=1, C=inter)
+
+        t_g1, _, _ = self._graph_steps([gemm1_fn(c) for c in self.copies[:L]], steps, warmup)
+        us_layer = t_layer / steps * 1e6
+        us_g1 = t_g1 / steps * 1e6
+        flops_layer = 6.0 * wl.H * wl.I * M * wl.topk
+        flops_g1 = 4.0 * wl.H * wl.I * M * wl.topk
+        res = dict(
+            M=M, block_m=bm, active_experts=active, layer_copies=L, graph_calls=G,
+            us_per_layer=round(us_layer, 2), tokens_per_s=round(M / (us_layer * 1e-6), 1),
+            layer_GBps=round(act_bytes / (us_layer * 1e-6) / 1e9, 1),
+            layer_hbm_frac=round(act_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            layer_mfma_frac=round(flops_layer / (us_layer * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            w13_us=round(us_g1, 2),
+            w13_GBps=round(w13_bytes / (us_g1 * 1e-6) / 1e9, 1),
+            w13_TFLOPs=round(flops_g1 / (us_g1 * 1e-6) / 1e12, 2),
+            active_weight_bytes=act_bytes, w13_bytes=w13_bytes,
+        )
+        return res, t_layer, wall, (x, lg)
+
+
+def cpu_baseline(bench, M, x, lg, ntok):
+    """The oracle as it stands on the first ntok tokens of the batch (host cores)."""
+    import numpy as np
+
+    import oracle as O
+    torch, wl = bench.torch, bench.wl
+    rows = np.arange(min(ntok, M))
+    lg_np = O.to_numpy(lg)[rows]
+    ids, _ = O.route(lg_np, wl.topk, wl.score, wl.renormalize, wl.num_groups, wl.topk_groups,
+                     wl.scale)
+    experts = sorted(set(ids.reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    sub = {k: (v.index_select(0, idx).cpu() if v is not None else None)
+           for k, v in bench.layer.items()}
+    xs = x[: len(rows)].cpu()
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    ids, w = O.route(lg_np, wl.topk, wl.score, wl.renormalize, wl.num_groups, wl.topk_groups,
+                     wl.scale)
+    O.moe_layer_rows(xs, ids, w, O.ExpertSource(sub, wl.bits, experts))
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of the {M} tokens of the timed batch ({len(experts)} experts): "
+                      f"routing, float64 decoding of those experts and their FFN, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the layer is run on one GPU's share and multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    decode = [m for m in wl.Ms if m <= 64]
+    M = args.m or (max(decode) if decode else max(wl.Ms))
+    bench = Bench(wl, args.seed)
+
+    res, t_layer, wall, (x, lg) = bench.measure(M, args.steps, args.warmup)
+    log(f"[bench] M={M}: {res}")
+    sweep = []
+    if not args.no_sweep:
+        for m in wl.Ms:
+            r = res if m == M else bench.measure(m, args.sweep_steps, max(10, args.warmup // 4))[0]
+            sweep.append(r)
+            log(f"[bench] sweep M={m}: {r}")
+
+    hbm_frac = res["w13_GBps"] / HBM_PEAK_GBPS
+    mfma_frac = res["w13_TFLOPs"] / MFMA_PEAK_TFLOPS
+    if mfma_frac > hbm_frac:
+        roof = {"bound": "mfma", "achieved": res["w13_TFLOPs"], "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(mfma_frac, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": res["w13_GBps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": None}
+    roof.update({"kernel": f"wna16_gemm_kernel (w13 + SiLU*up, block_m {res['block_m']})",
+                 "avg_launch_us": res["w13_us"],
+                 "algorithmic_per_launch": (res["w13_bytes"] if roof["bound"] == "hbm"
+                                            else 4.0 * wl.H * wl.I * M * wl.topk)})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bench, M, x, lg, args.cpu_tokens)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    value = M * args.steps / t_layer
+    line = {
+        "metric": "fused-MoE w4a16 layer tokens/s + achieved HBM GB/s vs peak, M=1..4096",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_layer / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: seeded N(0,0.02^2) experts encoded "
+                + ("uint4 g128 asymmetric" if wl.bits == 4 else "int8 per-channel symmetric")
+                + ", N(0,0.1^2) activations, N(0,1) router logits",
+        "config": {"workload": f"{wl.name}: {wl.notes}", "E": wl.E, "H": wl.H, "I": wl.I,
+                   "topk": wl.topk, "M": M, "bits": wl.bits, "block_m": res["block_m"],
+                   "layer_copies": res["layer_copies"], "active_experts": res["active_experts"],
+                   "layer_GBps": res["layer_GBps"], "layer_hbm_frac": res["layer_hbm_frac"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,14 @@ def test_routing_validation(lib):
     assert f(NULL, 0, 8, 2, _rt(), NULL, NULL, NULL) == OK                      # M == 0: no-op
 
 
+def test_pick_block_m(lib):
+    assert lib.moe_pick_block_m(16, 8, 2) == 16       # 4 slots per expert
+    assert lib.moe_pick_block_m(64, 8, 2) == 32       # 16 per expert -> 24 needed
+    assert lib.moe_pick_block_m(1024, 256, 8) == 64
+    assert lib.moe_pick_block_m(4096, 256, 8) == 128
+    assert lib.moe_pick_block_m(0, 8, 2) == -1
+
+
 def test_align_capacity_formula(lib):
     assert lib.moe_align_capacity(8, 4, 4) == 20      # hand-worked fixture
     assert lib.moe_align_capacity(8, 5, 2) == 13

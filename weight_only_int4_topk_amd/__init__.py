@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "MoeError", "lib", "QUANT_INT4", "QUANT_INT8", "routing", "moe_topk_softmax",
-    "moe_align_capacity", "moe_align_block_size", "moe_wna16_gemm",
+    "moe_align_capacity", "moe_align_block_size", "moe_pick_block_m", "moe_wna16_gemm",
     "fused_moe_wna16_workspace_size", "fused_moe_wna16", "LIB_PATH",
 ]
 
@@ -48,6 +48,7 @@ _SIGS = {
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_topk_softmax": ([_P, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P], _I),
     "moe_align_capacity": ([_I, _I, _I], _I64),
+    "moe_pick_block_m": ([_I, _I, _I], _I),
     "moe_align_block_size": ([_P, _I, _I, _I, _P, _P, _P, _I64, _P], _I),
     "moe_wna16_gemm": ([_P, _I, _I, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _I, _I,
                         _P, _P, _P, _I64, _I, _I, _P, _I, _P, _P], _I),
@@ -127,6 +128,10 @@ def moe_topk_softmax(logits, topk, rt: MoeRouting, topk_weights=None, topk_ids=N
     _check(lib().moe_topk_softmax(_ptr(logits), M, E, topk, ctypes.byref(rt), _ptr(topk_weights),
                                   _ptr(topk_ids), _stream(stream)))
     return topk_weights, topk_ids
+
+
+def moe_pick_block_m(M, E, topk) -> int:
+    return int(lib().moe_pick_block_m(M, E, topk))
 
 
 def moe_align_capacity(numel, E, block_m) -> int:

@@ -94,6 +94,7 @@ struct Plan {
   int64_t cap;
   int nblk;
   int split2;
+  int ntw1, ntw2;
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
 };
 
@@ -109,6 +110,19 @@ int pick_block_m(int M, int topk, int E) {
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Column tiles of 16 per wavefront for a grouped GEMM with N weight rows.  Four tiles halve the
+// activation traffic per weight byte; they need block_m <= 32, N divisible by the wider
+// workgroup, and (for the SiLU epilogue, whose grid is narrower) enough workgroups to fill the chip.
+int pick_ntw(int act, int N, int bm, int64_t est_blocks) {
+  if (bm > 32) return 2;
+  if (act) return ((N / 2) % 128 == 0 && est_blocks * ((N / 2) / 128) >= 1024) ? 4 : 2;
+  return N % 256 == 0 ? 4 : 2;
+}
+
+int64_t estimate_blocks(int64_t slots, int E, int bm) {
+  return std::max<int64_t>(std::min<int64_t>(E, slots), slots / bm);
+}
+
 Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int block_m) {
   (void)dtype;
   Plan p{};
@@ -119,10 +133,14 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   // split the second GEMM (K = I) until there are enough workgroups to fill the chip
   const int kb = bits == 4 ? 128 : 64;
   const int kb_total = I / kb;
-  const int64_t est_blocks = std::max<int64_t>(std::min<int64_t>(E, slots), slots / p.bm);
-  const int64_t wgs = est_blocks * (H / 128);
+  const int64_t est_blocks = estimate_blocks(slots, E, p.bm);
+  p.ntw1 = pick_ntw(1, 2 * I, p.bm, est_blocks);
+  p.ntw2 = pick_ntw(0, H, p.bm, est_blocks);
+  const int64_t wgs = est_blocks * (H / (p.ntw2 * 64));
+  // each split must start on an even k-block (scales are fetched in pairs), so only split while
+  // the per-split count stays even
   int split = 1;
-  while (kb_total % (2 * split) == 0 && wgs * split < 2048) split *= 2;
+  while (kb_total % (4 * split) == 0 && wgs * split < 2048) split *= 2;
   p.split2 = split;
   size_t off = 0;
   p.off_w = off;      off += up256((size_t)slots * 4);
@@ -141,6 +159,11 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_pick_block_m(int M, int E, int topk) {
+  if (M <= 0 || E <= 0 || topk <= 0) return -1;
+  return pick_block_m(M, topk, E);
+}
 
 int64_t moe_align_capacity(int numel, int E, int block_m) {
   if (numel < 0 || E <= 0 || block_m <= 0) return -1;
@@ -214,6 +237,9 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
     return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
   if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
   if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
+  if ((int64_t)num_a_rows * K * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)N * (quant->bits == 4 ? K / 2 : K) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "A or one expert's weights exceed 2 GiB");
   if ((int64_t)num_a_rows * a_row_div < num_slots)
     return fail(MOE_ERR_INVALID_ARG, "A has %d rows, slots need %lld", num_a_rows,
                 (long long)((num_slots + a_row_div - 1) / a_row_div));
@@ -227,6 +253,7 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   if (num_slots == 0 || capacity == 0) return MOE_OK;
   moe::GemmParams p{};
   p.A = A;
+  p.num_a_rows = num_a_rows;
   p.a_row_div = a_row_div;
   p.B = (const uint8_t*)B;
   p.scales = scales;
@@ -244,7 +271,8 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   p.topk_w = topk_weights;
   p.C = C;
   p.split_k = 1;
-  const moe::GemmConfig c{dtype, quant->bits, block_m, act, 0};
+  const moe::GemmConfig c{dtype, quant->bits, block_m, act, 0,
+                          pick_ntw(act, N, block_m, estimate_blocks(num_slots, E, block_m))};
   hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm launch");
 }
@@ -271,6 +299,9 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   if (H % 256 || I % 256)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");
+  if ((int64_t)M * topk * I * 2 >= ((int64_t)1 << 31) || (int64_t)M * H * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)2 * I * (quant->bits == 4 ? H / 2 : H) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "activations or one expert's weights exceed 2 GiB");
   if (M == 0) return MOE_OK;
   if (int rc = check_weights(w13, w13_scales, w13_zeros, quant)) return rc;
   if (int rc = check_weights(w2, w2_scales, w2_zeros, quant)) return rc;
@@ -305,6 +336,7 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
 
   moe::GemmParams g1{};
   g1.A = x;
+  g1.num_a_rows = M;
   g1.a_row_div = topk;
   g1.B = (const uint8_t*)w13;
   g1.scales = w13_scales;
@@ -320,11 +352,12 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   g1.topk_w = nullptr;
   g1.C = inter;
   g1.split_k = 1;
-  e = moe::launch_gemm(g1, moe::GemmConfig{dtype, quant->bits, pl.bm, 1, 0}, st);
+  e = moe::launch_gemm(g1, moe::GemmConfig{dtype, quant->bits, pl.bm, 1, 0, pl.ntw1}, st);
   if (e != hipSuccess) return hip_fail(e, "gemm1 launch");
 
   moe::GemmParams g2 = g1;
   g2.A = inter;
+  g2.num_a_rows = slots;
   g2.a_row_div = 1;
   g2.B = (const uint8_t*)w2;
   g2.scales = w2_scales;
@@ -333,7 +366,7 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   g2.K = I;
   g2.C = part;
   g2.split_k = pl.split2;
-  e = moe::launch_gemm(g2, moe::GemmConfig{dtype, quant->bits, pl.bm, 0, 1}, st);
+  e = moe::launch_gemm(g2, moe::GemmConfig{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2}, st);
   if (e != hipSuccess) return hip_fail(e, "gemm2 launch");
 
   e = moe::launch_combine(part, pl.split2, tw, M, topk, H, dtype, out, st);

@@ -34,7 +34,8 @@ namespace moe {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family buffer descriptor: 32-bit data format
 
 template <int DT>
 struct Mfma;
@@ -65,10 +66,9 @@ template <int DT, int BITS>
 __device__ __forceinline__ DecodeK make_decode(uint32_t sbits, uint32_t z) {
   DecodeK d;
   if constexpr (DT == 0) {
-    d.s2 = sbits | (sbits << 16);
+    d.s2 = (sbits & 0xFFFFu) * 0x10001u;
     if constexpr (BITS == 4) {
-      const uint32_t zb = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + (float)z)));
-      d.zn2 = zb | (zb << 16);
+      d.zn2 = (0xE400u | z) * 0x10001u;  // fp16 -(1024 + z): sign, exponent of 1024, mantissa z
     } else {
       const uint32_t zb = __builtin_bit_cast(uint16_t, (_Float16)(-1152.0f));
       d.zn2 = zb | (zb << 16);
@@ -139,28 +139,91 @@ __device__ __forceinline__ u32x4_t decode_s8(uint32_t lo, uint32_t hi, const Dec
   return b;
 }
 
-template <int MT>
+// (a & m) | c in one gfx950 v_bitop3_b32 (truth table 0xEA: S0 & S1 | S2).  Left to itself the
+// compiler splits this into an and plus an or, because VOP3 encodings take no literal operands.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
+}
+
+// Biased decode for the decode-regime kernels: the MFMA sees magic + q exactly (fp16 1024 + q, or
+// bf16 128 + q), pairs (k0,k4)(k1,k5)(k2,k6)(k3,k7) as in decode_u4.  The bias and the zero point
+// are removed by a second MFMA against -(magic + z) and the group scale is applied to the float32
+// partial sum of the k-block, so per 8 weights the VALU does 3 shifts and 4 and-or.
+__device__ __forceinline__ u32x4_t bias_u4(uint32_t w, uint32_t mask, uint32_t magic) {
+  return u32x4_t{and_or(w, mask, magic), and_or(w >> 4, mask, magic), and_or(w >> 8, mask, magic),
+                 and_or(w >> 12, mask, magic)};
+}
+
+// int8 biased decode: u = q + 128 in natural k order; fp16 as 1024 + u, bf16 as u itself (exact).
+template <int DT>
+__device__ __forceinline__ u32x4_t bias_s8(uint32_t lo, uint32_t hi) {
+  const uint32_t ulo = lo ^ 0x80808080u;
+  const uint32_t uhi = hi ^ 0x80808080u;
+  if constexpr (DT == 0) {
+    const uint32_t C = 0x64646464u;
+    return u32x4_t{__builtin_amdgcn_perm(C, ulo, 0x04010400u), __builtin_amdgcn_perm(C, ulo, 0x04030402u),
+                   __builtin_amdgcn_perm(C, uhi, 0x04010400u), __builtin_amdgcn_perm(C, uhi, 0x04030402u)};
+  } else {
+    return u32x4_t{f32x2_to_bf16x2((float)(ulo & 0xFFu), (float)((ulo >> 8) & 0xFFu)),
+                   f32x2_to_bf16x2((float)((ulo >> 16) & 0xFFu), (float)(ulo >> 24)),
+                   f32x2_to_bf16x2((float)(uhi & 0xFFu), (float)((uhi >> 8) & 0xFFu)),
+                   f32x2_to_bf16x2((float)((uhi >> 16) & 0xFFu), (float)(uhi >> 24))};
+  }
+}
+
+// LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its global loads, so the
+// weight prefetch stays in flight across it.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+template <int BITS, int MT, int NTW>
 struct Shape {
   static constexpr int BM = 16 * MT;
-  static constexpr int KC = MT == 1 ? 1024 : (MT == 2 ? 512 : (MT == 4 ? 256 : 128));
-  static constexpr int LDA = KC + 8;  // LDS row stride in 16-bit elements (16-byte pad)
-  static constexpr int PF = MT <= 2 ? 4 : 2;
+  static constexpr int KB = BITS == 4 ? 128 : 64;            // k per k-block
+  // activation chunk: four 16-byte vectors per thread, at least one k-block
+  static constexpr int KC0 = 4 * 8 * kThreads / BM;
+  static constexpr int KC = KC0 < KB ? KB : KC0;
+  static constexpr int AV = BM * KC / 8 / kThreads;           // 16-byte vectors per thread
+  static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
+  static constexpr int KBC = KC / KB;                         // k-blocks per chunk
+  static constexpr int PF = MT <= 2 ? (NTW == 2 ? 4 : 2) : (NTW == 2 ? 2 : 1);
+  static constexpr int U = KBC / gcd_c(KBC, PF) * PF;         // unroll: lcm(KBC, PF)
 };
 
 template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32>
 __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
-  using S = Shape<MT>;
+  using S = Shape<BITS, MT, NTW>;
   constexpr int BM = S::BM;
   constexpr int KC = S::KC;
   constexpr int LDA = S::LDA;
   constexpr int PF = S::PF;
-  constexpr int KB = BITS == 4 ? 128 : 64;        // k per k-block (64 bytes of a weight row)
+  constexpr int KB = S::KB;
+  constexpr int AV = S::AV;
+  constexpr int KBC = S::KBC;
+  constexpr int U = S::U;
   constexpr int STEPS = KB / 32;                    // MFMAs per k-block
-  constexpr int KBC = KC / KB;                      // k-blocks per LDS chunk
   constexpr int NOUT = ACT ? NTW / 2 : NTW;         // output tiles per wave
   constexpr int WG_COLS = kWaves * NOUT * 16;
+  constexpr int VPR = KC / 8;                       // 16-byte vectors per activation row chunk
+  constexpr int R = kWaves * NTW * 16;              // weight rows of the workgroup
+  // decode regime: biased codes with MFMA-side bias removal (fewer VALU ops per weight); prefill:
+  // exact decoded weights, no extra MFMAs (the matrix cores are the bottleneck there)
+  constexpr bool BIASED = MT <= 2;
+  // uint4 scales and zero points: fetched per chunk by the whole workgroup (one item per row and
+  // pair of k-blocks: a dword of two scales and the byte of their two zero points) and packed into
+  // LDS as scale | zero << 16.  Per-lane loads of a 2-byte scale and a 1-byte zero every k-block
+  // would triple the memory instructions of the weight stream and cap it near 3.2 TB/s.
+  constexpr bool PAIRS = KBC >= 2;
+  constexpr int MITEMS = BITS == 4 ? (PAIRS ? R * KBC / 2 : R * KBC) : 0;
+  constexpr int MV = (MITEMS + kThreads - 1) / kThreads;
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[BM * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDA];
+  __shared__ uint32_t s_meta[2][BITS == 4 ? KBC * R : 1];
   __shared__ int s_slot[BM];
   __shared__ int s_row[BM];
 
@@ -190,130 +253,297 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   }
   __syncthreads();
 
-  // K range of this split, in k-blocks
+  // K range of this split, in k-blocks (the host keeps kb_beg even)
   const int kb_total = K / KB;
   const int kb_per = (kb_total + split - 1) / split;
   const int kb_beg = z * kb_per;
   const int kb_end = min(kb_total, kb_beg + kb_per);
+  const int kb_last = min(max(kb_beg, kb_end - 1), kb_total - 1);  // always a real k-block
 
-  // this lane's weight rows
+  // rows of the workgroup: local row lr = (wave * NTW + t) * 16 + r
+  auto col_of = [&](int w, int t) -> int {
+    if constexpr (ACT) {
+      const int g0 = nc * WG_COLS + w * NOUT * 16;
+      return t < NOUT ? g0 + t * 16 : N / 2 + g0 + (t - NOUT) * 16;
+    } else {
+      return nc * WG_COLS + w * NTW * 16 + t * 16;
+    }
+  };
   const int rsub = lane & 15;
   const int grp = lane >> 4;  // 16-byte slice of the 64-byte k-block
   int col[NTW];
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    if constexpr (ACT) {
-      const int g0 = nc * WG_COLS + wave * NOUT * 16;
-      col[t] = t < NOUT ? g0 + t * 16 : N / 2 + g0 + (t - NOUT) * 16;
-    } else {
-      col[t] = nc * WG_COLS + wave * NTW * 16 + t * 16;
-    }
-  }
-  const size_t row_bytes = BITS == 4 ? (size_t)K / 2 : (size_t)K;
-  const uint8_t* wrow[NTW];
-  const uint16_t* srow[NTW];
-  const uint8_t* zrow[NTW];
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    const size_t n = (size_t)e * N + col[t] + rsub;
-    wrow[t] = p.B + n * row_bytes + grp * 16;
-    if constexpr (BITS == 4) {
-      srow[t] = (const uint16_t*)p.scales + n * (K / 128);
-      zrow[t] = p.zeros + n * (K / 256);
-    } else {
-      srow[t] = (const uint16_t*)p.scales + n;
-      zrow[t] = nullptr;
-    }
-  }
+  for (int t = 0; t < NTW; ++t) col[t] = col_of(wave, t);
 
-  u32x4_t wq[PF][NTW];
-  uint32_t sq[PF][NTW];
-  uint32_t zq[PF][NTW];
-  auto load_kb = [&](int slot, int kb) {
+  // Every global load goes through a buffer descriptor: the expert's base address sits in scalar
+  // registers, per-lane offsets are fixed for the whole K loop and the k-block offset is a scalar,
+  // so no load needs vector address arithmetic and none is conditional (the compiler can then keep
+  // the prefetch in flight with exact vmcnt waits).
+  const uint32_t row_bytes = BITS == 4 ? (uint32_t)K / 2 : (uint32_t)K;
+  const uint32_t srow_bytes = BITS == 4 ? (uint32_t)(K / 128) * 2 : 2u;
+  const uint32_t zrow_bytes = (uint32_t)(K / 256);
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.B + (size_t)e * N * row_bytes), (short)0, (int)(N * row_bytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const uint8_t*)p.scales + (size_t)e * N * srow_bytes), (short)0, (int)(N * srow_bytes),
+      kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_z = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(BITS == 4 ? p.zeros + (size_t)e * N * zrow_bytes : p.zeros), (short)0,
+      BITS == 4 ? (int)(N * zrow_bytes) : 0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.A, (short)0, (int)((size_t)p.num_a_rows * K * 2), kRsrcWord3);
+  uint32_t vw[NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      wq[slot][t] = *(const u32x4_t*)(wrow[t] + (size_t)kb * 64);
+  for (int t = 0; t < NTW; ++t) vw[t] = (uint32_t)(col[t] + rsub) * row_bytes + grp * 16;
+
+  // ---- activation chunk c (KC columns of the block's BM rows): registers, then LDS.  Padding rows
+  // and columns past this split's K range read past the end of the buffer, which loads zeros.
+  uint32_t arow[AV], acol[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int idx = tid + i * kThreads;
+    const int r = idx / VPR;
+    const int row = s_row[r];
+    arow[i] = row >= 0 ? (uint32_t)row * K * 2 : 0x80000000u;
+    acol[i] = (uint32_t)(idx - r * VPR) * 8;
+  }
+  const uint32_t klim = (uint32_t)(kb_end * KB);
+  u32x4_t areg[AV];
+  auto load_a = [&](int c) {
+    const uint32_t kbase = (uint32_t)((kb_beg + c * KBC) * KB);
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const uint32_t k = kbase + acol[i];
+      const uint32_t off = (arow[i] < 0x80000000u && k < klim) ? arow[i] + k * 2 : 0x80000000u;
+      areg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, off, 0, 0));
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int idx = tid + i * kThreads;
+      const int r = idx / VPR;
+      const int c8 = idx - r * VPR;
+      u32x4_t v = areg[i];
       if constexpr (BITS == 4) {
-        sq[slot][t] = srow[t][kb];
-        zq[slot][t] = zrow[t][kb >> 1];
+        // (x0..x7) -> (x0,x4,x1,x5,x2,x6,x3,x7), the decode's k pairing
+        v = u32x4_t{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
+                    __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                    __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
+                    __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+      }
+      *(u32x4_t*)&s_a[buf][r * LDA + c8 * 8] = v;
+    }
+  };
+
+  // ---- uint4 metadata chunk c: item = (row lr, pair pp) or (row lr, k-block pp); k-blocks past
+  // the range are clamped to real ones (their activations are zero, the values only stay finite)
+  uint32_t ms_off[MV > 0 ? MV : 1], mz_off[MV > 0 ? MV : 1];
+  uint32_t ms[MV > 0 ? MV : 1], mz[MV > 0 ? MV : 1];
+#pragma unroll
+  for (int v = 0; v < MV; ++v) {
+    const int item = min(tid + v * kThreads, MITEMS - 1);
+    const int lr = item % R;
+    const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
+    ms_off[v] = n * srow_bytes;
+    mz_off[v] = n * zrow_bytes;
+  }
+  auto load_meta = [&](int c) {
+#pragma unroll
+    for (int v = 0; v < MV; ++v) {
+      const int pp = min(tid + v * kThreads, MITEMS - 1) / R;
+      if constexpr (PAIRS) {
+        const int kb = min(kb_beg + c * KBC + 2 * pp, kb_last & ~1);
+        ms[v] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, ms_off[v] + kb * 2, 0, 0);
+        mz[v] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, mz_off[v] + (kb >> 1), 0, 0);
+      } else {
+        const int kb = min(kb_beg + c * KBC + pp, kb_last);
+        ms[v] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, ms_off[v] + kb * 2, 0, 0);
+        mz[v] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, mz_off[v] + (kb >> 1), 0, 0) >>
+                ((kb & 1) * 4);
+      }
+    }
+  };
+  auto store_meta = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < MV; ++v) {
+      const int item = tid + v * kThreads;
+      if (item < MITEMS) {
+        const int lr = item % R;
+        const int pp = item / R;
+        if constexpr (PAIRS) {
+          s_meta[buf][(2 * pp) * R + lr] = (ms[v] & 0xFFFFu) | ((mz[v] & 0xFu) << 16);
+          s_meta[buf][(2 * pp + 1) * R + lr] = (ms[v] >> 16) | (((mz[v] >> 4) & 0xFu) << 16);
+        } else {
+          s_meta[buf][pp * R + lr] = (ms[v] & 0xFFFFu) | ((mz[v] & 0xFu) << 16);
+        }
       }
     }
   };
 
-  DecodeK dk8[NTW];
-  if constexpr (BITS == 8) {
+  // ---- weight stream: PF k-blocks in flight, 16 bytes per lane per tile
+  u32x4_t wq[PF][NTW];
+  auto load_kb = [&](int slot, int kb) {
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) dk8[t] = make_decode<DT, 8>(srow[t][0], 0);
-  }
+    for (int t = 0; t < NTW; ++t)
+      wq[slot][t] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_w, vw[t], kb * 64, 0));
+  };
 
   floatx4_t acc[MT][NTW];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
+  // biased-decode constants (registers: gfx950 VOP3 encodings take no literals)
+  const floatx4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t kMask = p.dec_mask;    // 0x000F000F
+  const uint32_t kMagic = p.dec_magic;  // fp16 1024 (0x6400) or bf16 128 (0x4300) in both halves
+  // fp16 -(1024 + z) = 0xE400 | z; bf16 -(128 + z) = 0xC300 | z
+  constexpr uint32_t kZeroBase = DT == 0 ? 0xE400u : 0xC300u;
+  const uint32_t one2 = DT == 0 ? 0x3C003C00u : 0x3F803F80u;
+  const u32x4_t ones = {one2, one2, one2, one2};
+  floatx4_t rsum[MT];
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
-    if (kb_beg + u < kb_end) load_kb(u, kb_beg + u);
-
-  for (int kb0 = kb_beg; kb0 < kb_end; kb0 += PF) {
+  for (int m = 0; m < MT; ++m) rsum[m] = zero4;
+  DecodeK dk8[NTW];
+  if constexpr (BITS == 8 && !BIASED) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int kb = kb0 + u;
-      if (kb >= kb_end) break;
-      const int kbl = (kb - kb_beg) % KBC;
-      if (kbl == 0) {
-        // gather the block's activation rows for the next KC columns into LDS
-        __syncthreads();
-        const int k0 = kb * KB;
-        const int kc_len = min(KC, (kb_end - kb) * KB);
-        const int vec_per_row = kc_len / 8;
-        for (int i = tid; i < BM * vec_per_row; i += kThreads) {
-          const int r = i / vec_per_row;
-          const int c8 = i - r * vec_per_row;
-          const int row = s_row[r];
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          if (row >= 0)
-            v = *(const u32x4_t*)((const uint16_t*)p.A + (size_t)row * K + k0 + c8 * 8);
-          if constexpr (BITS == 4) {
-            // (x0..x7) -> (x0,x4,x1,x5,x2,x6,x3,x7), the decode's k pairing
-            const u32x4_t o = {__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
-                               __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
-                               __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
-                               __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
-            v = o;
-          }
-          *(u32x4_t*)&s_a[r * LDA + c8 * 8] = v;
-        }
-        __syncthreads();
-      }
+    for (int t = 0; t < NTW; ++t)
+      dk8[t] = make_decode<DT, 8>(
+          __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)(col[t] + rsub) * 2, 0, 0), 0);
+  }
 
-      DecodeK dk[NTW];
+  // ---- prologue: chunk 0 in LDS, chunk 1 in flight, PF k-blocks of weights in flight.  Prefetch
+  // indices past the range are clamped to the last k-block (a redundant, in-bounds load), so the
+  // number of loads in flight is the same on every path.
+  load_a(0);
+  if constexpr (BITS == 4) load_meta(0);
+#pragma unroll
+  for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
+  store_a(0);
+  if constexpr (BITS == 4) store_meta(0);
+  barrier_lds();
+  load_a(1);
+  if constexpr (BITS == 4) load_meta(1);
+
+  // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
+  // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
+  // into the loop header and make the compiler drain the prefetch at the top of every iteration.
+  const int n_iter = (kb_end - kb_beg + U - 1) / U;
+  for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int kb = kb_beg + it * U + j;
+      const int slot = j % PF;
+      const int jc = j % KBC;
+      const int c = (it * U + j) / KBC;
+      const uint16_t* sa = s_a[c & 1];
+      const uint16_t* abase = sa + rsub * LDA + jc * KB + grp * (KB / 4);
+      uint32_t meta[NTW];
       if constexpr (BITS == 4) {
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
-          dk[t] = make_decode<DT, 4>(sq[u][t], (zq[u][t] >> ((kb & 1) * 4)) & 0xFu);
+        for (int t = 0; t < NTW; ++t) meta[t] = s_meta[c & 1][jc * R + (wave * NTW + t) * 16 + rsub];
       }
-      const uint16_t* abase = &s_a[rsub * LDA + kbl * KB + grp * (KB / 4)];
-#pragma unroll
-      for (int s = 0; s < STEPS; ++s) {
-        u32x4_t a[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
-        u32x4_t b[NTW];
+      if constexpr (BIASED && BITS == 4) {
+        // magic-biased codes, zero point and bias removed by a broadcast MFMA, scale per k-block
+        floatx4_t accg[MT][NTW];
+        u32x4_t bz[NTW];
+        float sf[NTW];
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          if constexpr (BITS == 4)
-            b[t] = decode_u4<DT>(wq[u][t][s], dk[t]);
-          else
-            b[t] = decode_s8<DT>(wq[u][t][2 * s], wq[u][t][2 * s + 1], dk8[t]);
+          const uint32_t zz = (kZeroBase | (meta[t] >> 16)) * 0x10001u;
+          bz[t] = u32x4_t{zz, zz, zz, zz};
+          sf[t] = bits_to_float<DT>((uint16_t)(meta[t] & 0xFFFFu));
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+          u32x4_t a[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
+          u32x4_t b[NTW];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) b[t] = bias_u4(wq[slot][t][s], kMask, kMagic);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+              accg[m][t] = Mfma<DT>::run(a[m], b[t], s == 0 ? zero4 : accg[m][t]);
+              accg[m][t] = Mfma<DT>::run(a[m], bz[t], accg[m][t]);
+            }
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) acc[m][t] = Mfma<DT>::run(a[m], b[t], acc[m][t]);
+          for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(sf[t], accg[m][t][i], acc[m][t][i]);
+      } else if constexpr (BIASED) {
+        // int8: biased codes accumulate over all of K; row sums (ones MFMA) remove the bias at the end
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+          u32x4_t a[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) rsum[m] = Mfma<DT>::run(a[m], ones, rsum[m]);
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) {
+            const u32x4_t b = bias_s8<DT>(wq[slot][t][2 * s], wq[slot][t][2 * s + 1]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m][t] = Mfma<DT>::run(a[m], b, acc[m][t]);
+          }
+        }
+      } else {
+        DecodeK dk[NTW];
+        if constexpr (BITS == 4) {
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) dk[t] = make_decode<DT, 4>(meta[t] & 0xFFFFu, meta[t] >> 16);
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+          u32x4_t a[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
+          u32x4_t b[NTW];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) {
+            if constexpr (BITS == 4)
+              b[t] = decode_u4<DT>(wq[slot][t][s], dk[t]);
+            else
+              b[t] = decode_s8<DT>(wq[slot][t][2 * s], wq[slot][t][2 * s + 1], dk8[t]);
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) acc[m][t] = Mfma<DT>::run(a[m], b[t], acc[m][t]);
+        }
       }
-      if (kb + PF < kb_end) load_kb(u, kb + PF);
+      load_kb(slot, min(kb + PF, kb_last));
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
+      if (jc == KBC - 1) {
+        // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+2
+        store_a((c + 1) & 1);
+        if constexpr (BITS == 4) store_meta((c + 1) & 1);
+        barrier_lds();
+        load_a(c + 2);
+        if constexpr (BITS == 4) load_meta(c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  if constexpr (BIASED && BITS == 8) {
+    // remove the +128 bias (fp16: +1152 with the 1024 magic) and apply the per-channel scale
+    const float bias = DT == 0 ? 1152.0f : 128.0f;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const float sc = bits_to_float<DT>(
+          (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)(col[t] + rsub) * 2, 0, 0));
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][t][i] = sc * __builtin_fmaf(-bias, rsum[m][i], acc[m][t][i]);
     }
   }
 
@@ -328,41 +558,45 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const float wscale = p.topk_w ? p.topk_w[slot] : 1.0f;
 #pragma unroll
       for (int t = 0; t < NOUT; ++t) {
-        const int c = col[t] + rsub;
+        const int cc = col[t] + rsub;
         if constexpr (ACT) {
           const float g = acc[m][t][i];
           const float up = acc[m][t + NOUT][i];
           const float v = g / (1.0f + __expf(-g)) * up * wscale;
-          ((uint16_t*)p.C)[(size_t)slot * (N / 2) + c] = float_to_bits<DT>(v);
+          ((uint16_t*)p.C)[(size_t)slot * (N / 2) + cc] = float_to_bits<DT>(v);
         } else if constexpr (OUTF32) {
-          ((float*)p.C)[((size_t)z * p.num_slots + slot) * N + c] = acc[m][t][i] * wscale;
+          ((float*)p.C)[((size_t)z * p.num_slots + slot) * N + cc] = acc[m][t][i] * wscale;
         } else {
-          ((uint16_t*)p.C)[(size_t)slot * N + c] = float_to_bits<DT>(acc[m][t][i] * wscale);
+          ((uint16_t*)p.C)[(size_t)slot * N + cc] = float_to_bits<DT>(acc[m][t][i] * wscale);
         }
       }
     }
   }
 }
 
-constexpr int kNTW = 2;
-
-template <int DT, int BITS, int MT>
-hipError_t launch_mt(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
+template <int DT, int BITS, int MT, int NTW>
+hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
   const int n_out = c.act ? p.N / 2 : p.N;
   const int n_chunks = n_out / gemm_wg_cols(c);
   const long long grid = (long long)n_chunks * p.num_blocks * p.split_k;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (c.act)
-    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, kNTW, 1, 0>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 1, 0>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, p);
   else if (c.out_f32)
-    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, kNTW, 0, 1>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 1>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, kNTW, 0, 0>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 0>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int DT, int BITS, int MT>
+hipError_t launch_mt(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
+  if (MT <= 2 && c.ntw == 4) return launch_ntw<DT, BITS, MT, (MT <= 2 ? 4 : 2)>(p, c, stream);
+  return launch_ntw<DT, BITS, MT, 2>(p, c, stream);
 }
 
 template <int DT, int BITS>
@@ -378,9 +612,19 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 
 }  // namespace
 
-int gemm_wg_cols(const GemmConfig& c) { return kWaves * (c.act ? kNTW / 2 : kNTW) * 16; }
+int gemm_wg_cols(const GemmConfig& c) {
+  const int ntw = (c.ntw == 4 && c.block_m <= 32) ? 4 : 2;
+  return kWaves * (c.act ? ntw / 2 : ntw) * 16;
+}
 
-hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
+hipError_t launch_gemm(const GemmParams& p_in, const GemmConfig& c, hipStream_t stream) {
+  GemmParams p = p_in;
+  // uint4 scales are fetched in pairs of k-blocks: every split must start on an even k-block
+  const int kb_total = p.K / (c.bits == 4 ? 128 : 64);
+  if (p.split_k < 1 || (p.split_k > 1 && (kb_total % p.split_k || (kb_total / p.split_k) % 2)))
+    return hipErrorInvalidValue;
+  p.dec_mask = 0x000F000Fu;
+  p.dec_magic = c.dtype == 0 ? 0x64006400u : 0x43004300u;
   if (c.dtype == 0)
     return c.bits == 4 ? launch_bits<0, 4>(p, c, stream) : launch_bits<0, 8>(p, c, stream);
   return c.bits == 4 ? launch_bits<1, 4>(p, c, stream) : launch_bits<1, 8>(p, c, stream);

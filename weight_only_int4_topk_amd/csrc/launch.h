@@ -23,7 +23,8 @@ hipError_t launch_align(const int32_t* topk_ids, int numel, int E, int block_m,
                         int64_t capacity, hipStream_t stream);
 
 struct GemmParams {
-  const void* A;              // dtype [rows, K]
+  const void* A;              // dtype [num_a_rows, K]
+  int num_a_rows;
   int a_row_div;
   const uint8_t* B;           // int4: uint8 [E, N, K/2]; int8: int8 [E, N, K]
   const void* scales;         // int4: [E, N, K/128]; int8: [E, N]
@@ -38,6 +39,8 @@ struct GemmParams {
   void* C;                    // act: dtype [num_slots, N/2]; out_f32: float [split, num_slots, N];
                               // else dtype [num_slots, N]
   int split_k;                // K split count (out_f32 only, else 1)
+  uint32_t dec_mask;          // set by launch_gemm: nibble-pair mask of the biased decode
+  uint32_t dec_magic;         // set by launch_gemm: magic bias in both 16-bit halves
 };
 
 struct GemmConfig {
@@ -46,6 +49,7 @@ struct GemmConfig {
   int block_m;   // 16, 32, 64, 128
   int act;       // 0 none, 1 silu-mul
   int out_f32;   // 1: float partials [split, num_slots, N]
+  int ntw;       // column tiles of 16 per wavefront: 2, or 4 (block_m <= 32 only)
 };
 
 // Columns of output one workgroup covers (N % this must be 0; act: gate columns).
