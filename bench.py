@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device-to-device copy (known bytes) so that "
+                         "profiler traffic counters can be scaled")
     return ap.parse_args()
 
 
@@ -237,6 +240,15 @@ def main():
                  "avg_launch_us": res["w13_us"],
                  "algorithmic_per_launch": (res["w13_bytes"] if roof["bound"] == "hbm"
                                             else 4.0 * wl.H * wl.I * M * wl.topk)})
+
+    if args.calibrate_copy:
+        import torch
+        src = torch.empty(512 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 5 x 512 MiB device-to-device")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -214,16 +214,15 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // decode regime: biased codes with MFMA-side bias removal (fewer VALU ops per weight); prefill:
   // exact decoded weights, no extra MFMAs (the matrix cores are the bottleneck there)
   constexpr bool BIASED = MT <= 2;
-  // uint4 scales and zero points: fetched per chunk by the whole workgroup (one item per row and
-  // pair of k-blocks: a dword of two scales and the byte of their two zero points) and packed into
-  // LDS as scale | zero << 16.  Per-lane loads of a 2-byte scale and a 1-byte zero every k-block
-  // would triple the memory instructions of the weight stream and cap it near 3.2 TB/s.
-  constexpr bool PAIRS = KBC >= 2;
-  constexpr int MITEMS = BITS == 4 ? (PAIRS ? R * KBC / 2 : R * KBC) : 0;
-  constexpr int MV = (MITEMS + kThreads - 1) / kThreads;
+  // uint4 scales and zero points of the workgroup's rows for its whole K range are staged once,
+  // before the weight stream starts, into dynamic LDS as meta[kb - kb_beg][row] = scale | zero << 16
+  // (the host sizes it: rows * k-blocks * 4 bytes).  Consecutive threads read consecutive pairs of
+  // k-blocks of one row, so each cache line of scales is touched once.  Per-lane loads of a 2-byte
+  // scale and a 1-byte zero point every k-block would triple the memory instructions of the weight
+  // stream and cap it near 3.2 TB/s.
+  extern __shared__ uint32_t s_meta[];
 
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDA];
-  __shared__ uint32_t s_meta[2][BITS == 4 ? KBC * R : 1];
   __shared__ int s_slot[BM];
   __shared__ int s_row[BM];
 
@@ -336,50 +335,21 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
     }
   };
 
-  // ---- uint4 metadata chunk c: item = (row lr, pair pp) or (row lr, k-block pp); k-blocks past
-  // the range are clamped to real ones (their activations are zero, the values only stay finite)
-  uint32_t ms_off[MV > 0 ? MV : 1], mz_off[MV > 0 ? MV : 1];
-  uint32_t ms[MV > 0 ? MV : 1], mz[MV > 0 ? MV : 1];
-#pragma unroll
-  for (int v = 0; v < MV; ++v) {
-    const int item = min(tid + v * kThreads, MITEMS - 1);
-    const int lr = item % R;
-    const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
-    ms_off[v] = n * srow_bytes;
-    mz_off[v] = n * zrow_bytes;
+  // ---- uint4 metadata for the whole K range of this split (kb_beg and the range length are even)
+  if constexpr (BITS == 4) {
+    const int npair = (kb_end - kb_beg + 1) >> 1;
+    for (int item = tid; item < R * npair; item += kThreads) {
+      const int lr = item / npair;
+      const int j = item - lr * npair;
+      const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
+      const int kb = kb_beg + 2 * j;
+      const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs_s, n * srow_bytes + kb * 2, 0, 0);
+      const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rs_z, n * zrow_bytes + (kb >> 1), 0, 0);
+      s_meta[(2 * j) * R + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
+      if (kb + 1 < kb_end) s_meta[(2 * j + 1) * R + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
+    }
+    __syncthreads();
   }
-  auto load_meta = [&](int c) {
-#pragma unroll
-    for (int v = 0; v < MV; ++v) {
-      const int pp = min(tid + v * kThreads, MITEMS - 1) / R;
-      if constexpr (PAIRS) {
-        const int kb = min(kb_beg + c * KBC + 2 * pp, kb_last & ~1);
-        ms[v] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, ms_off[v] + kb * 2, 0, 0);
-        mz[v] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, mz_off[v] + (kb >> 1), 0, 0);
-      } else {
-        const int kb = min(kb_beg + c * KBC + pp, kb_last);
-        ms[v] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, ms_off[v] + kb * 2, 0, 0);
-        mz[v] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, mz_off[v] + (kb >> 1), 0, 0) >>
-                ((kb & 1) * 4);
-      }
-    }
-  };
-  auto store_meta = [&](int buf) {
-#pragma unroll
-    for (int v = 0; v < MV; ++v) {
-      const int item = tid + v * kThreads;
-      if (item < MITEMS) {
-        const int lr = item % R;
-        const int pp = item / R;
-        if constexpr (PAIRS) {
-          s_meta[buf][(2 * pp) * R + lr] = (ms[v] & 0xFFFFu) | ((mz[v] & 0xFu) << 16);
-          s_meta[buf][(2 * pp + 1) * R + lr] = (ms[v] >> 16) | (((mz[v] >> 4) & 0xFu) << 16);
-        } else {
-          s_meta[buf][pp * R + lr] = (ms[v] & 0xFFFFu) | ((mz[v] & 0xFu) << 16);
-        }
-      }
-    }
-  };
 
   // ---- weight stream: PF k-blocks in flight, 16 bytes per lane per tile
   u32x4_t wq[PF][NTW];
@@ -418,14 +388,11 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // indices past the range are clamped to the last k-block (a redundant, in-bounds load), so the
   // number of loads in flight is the same on every path.
   load_a(0);
-  if constexpr (BITS == 4) load_meta(0);
 #pragma unroll
   for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
   store_a(0);
-  if constexpr (BITS == 4) store_meta(0);
   barrier_lds();
   load_a(1);
-  if constexpr (BITS == 4) load_meta(1);
 
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
   // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
@@ -443,7 +410,8 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       uint32_t meta[NTW];
       if constexpr (BITS == 4) {
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) meta[t] = s_meta[c & 1][jc * R + (wave * NTW + t) * 16 + rsub];
+        for (int t = 0; t < NTW; ++t)
+          meta[t] = s_meta[(min(kb, kb_last) - kb_beg) * R + (wave * NTW + t) * 16 + rsub];
       }
       if constexpr (BIASED && BITS == 4) {
         // magic-biased codes, zero point and bias removed by a broadcast MFMA, scale per k-block
@@ -524,10 +492,8 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       if (jc == KBC - 1) {
         // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+2
         store_a((c + 1) & 1);
-        if constexpr (BITS == 4) store_meta((c + 1) & 1);
         barrier_lds();
         load_a(c + 2);
-        if constexpr (BITS == 4) load_meta(c + 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -581,15 +547,16 @@ hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stre
   const long long grid = (long long)n_chunks * p.num_blocks * p.split_k;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const size_t lds = gemm_meta_lds_bytes(p, c);
   if (c.act)
     hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 1, 0>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), lds, stream, p);
   else if (c.out_f32)
     hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 1>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), lds, stream, p);
   else
     hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 0>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -611,6 +578,14 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 }
 
 }  // namespace
+
+size_t gemm_meta_lds_bytes(const GemmParams& p, const GemmConfig& c) {
+  if (c.bits != 4) return 0;
+  const int ntw = (c.ntw == 4 && c.block_m <= 32) ? 4 : 2;
+  const int kb_total = p.K / 128;
+  const int kb_per = (kb_total + p.split_k - 1) / p.split_k;
+  return (size_t)kWaves * ntw * 16 * kb_per * 4;
+}
 
 int gemm_wg_cols(const GemmConfig& c) {
   const int ntw = (c.ntw == 4 && c.block_m <= 32) ? 4 : 2;

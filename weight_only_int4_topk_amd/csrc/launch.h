@@ -54,6 +54,8 @@ struct GemmConfig {
 
 // Columns of output one workgroup covers (N % this must be 0; act: gate columns).
 int gemm_wg_cols(const GemmConfig& c);
+// Dynamic LDS of one workgroup for the staged uint4 scales and zero points.
+size_t gemm_meta_lds_bytes(const GemmParams& p, const GemmConfig& c);
 hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
 
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
