@@ -174,6 +174,30 @@ class Bench:
         return res, t_layer, wall, (x, lg)
 
 
+KERNEL_SOURCES = ("gemm.hip", "common.h", "launch.h", "api.cpp")
+
+
+def committed_traffic(workload, M):
+    """HBM bytes per launch of the dominant kernel from the committed profile summary, if that
+    summary was taken on the current kernel sources (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"w13_gemm_{workload}_m{M}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        k, _, v = line.partition(":")
+        fields[k.strip()] = v.strip()
+    csrc = os.path.join(ROOT, "weight_only_int4_topk_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in KERNEL_SOURCES)
+    if fields.get("traffic_kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(bench, M, x, lg, ntok):
     """The oracle as it stands on the first ntok tokens of the batch (host cores)."""
     import numpy as np
@@ -236,6 +260,10 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": res["w13_GBps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": None}
+    traffic = committed_traffic(wl.name, M)
+    if traffic is not None:
+        roof["traffic"] = round(traffic / (res["w13_us"] * 1e-6) / 1e9, 1)
+        roof["traffic_bytes_per_launch"] = traffic
     roof.update({"kernel": f"wna16_gemm_kernel (w13 + SiLU*up, block_m {res['block_m']})",
                  "avg_launch_us": res["w13_us"],
                  "algorithmic_per_launch": (res["w13_bytes"] if roof["bound"] == "hbm"
