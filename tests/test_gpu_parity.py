@@ -89,9 +89,11 @@ def test_align_golden(golden):
 # decoded weights (identity probe) and the grouped GEMM
 # ------------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("dt,bits", [("fp16", 4), ("bf16", 4), ("fp16", 8), ("bf16", 8)])
-def test_dequant_identity_probe(dt, bits):
+@pytest.mark.parametrize("bm", [16, 64])
+def test_dequant_identity_probe(dt, bits, bm):
     """One-hot activation rows routed to one expert with weight 1: GEMM row k is the decoded
-    column k of that expert, which must equal the oracle's correctly rounded (q - z) * s exactly."""
+    column k of that expert, which must equal the oracle's correctly rounded (q - z) * s exactly.
+    BLOCK_M 16 runs the decode-regime kernel (biased codes), 64 the exact-decode kernel."""
     wl = synth.Workload("p", E=3, H=512, I=256, topk=1, Ms=(1,), dtype=dt, bits=bits)
     layer = synth.make_layer(wl, seed=5)
     lay = cuda_layer(layer)
@@ -99,9 +101,9 @@ def test_dequant_identity_probe(dt, bits):
     eye = torch.eye(K, dtype=wl.torch_dtype, device="cuda")
     for e in range(wl.E):
         ids = torch.full((K, 1), e, dtype=torch.int32, device="cuda")
-        st, ex, npost = B.moe_align_block_size(ids, wl.E, 16)
+        st, ex, npost = B.moe_align_block_size(ids, wl.E, bm)
         C = B.moe_wna16_gemm(eye, 1, lay["w13"], lay["w13_scales"], lay["w13_zeros"], st, ex,
-                             npost, 16, K)
+                             npost, bm, K)
         src = O.ExpertSource(layer, bits)
         ref_bits = O.dequant_bits(src.w13(e), dt)          # [2I, K]
         got = C.view(torch.int16).cpu().numpy().view(np.uint16).T   # [N, K]

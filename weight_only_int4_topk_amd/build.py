@@ -23,6 +23,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the scale and epilogue arithmetic reads them directly
+    # instead of copying each one out of the accumulation registers first
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

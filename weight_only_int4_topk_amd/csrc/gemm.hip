@@ -24,9 +24,18 @@
 // mask decode yields.  The activation tile is stored in LDS with each run of 8 values permuted the
 // same way, so no weight ever moves between lanes.
 //
+// fp16 uint4: a nibble in bits 0..3 of a 16-bit half under the exponent of 1024 reads as 1024 + q,
+// and one in bits 4..7 reads as 1024 + 16 q; both are exact.  So the pairs (k0,k4) and (k2,k6) are
+// masked out of w and w >> 8 in place, and the pairs (k1,k5) and (k3,k7) in place with the high
+// nibble mask, scaled by 16.  The activations at those k offsets are stored in LDS divided by 16
+// (exact for normal fp16 values), so every product a * w is unchanged: one shift and four
+// and-or per 8 weights instead of three shifts.  bf16 has too few mantissa bits for 1024 + 16 q
+// under any exponent, so it keeps the three shifts.
+//
 // Decoding is exact: the MFMA sees the correctly rounded dtype value of (q - z) * s (fp16: the
-// subtraction of two exact half-precision integers 1024+q and 1024+z, then one rounded multiply;
-// bf16: an exact float32 fma of 128+q against s and -(128+z)*s, then one rounding to bf16).
+// subtraction of two exact half-precision integers 1024+q and 1024+z, then one rounded multiply,
+// or 16 times that value against an activation divided by 16; bf16: an exact float32 fma of 128+q
+// against s and -(128+z)*s, then one rounding to bf16).
 #include "common.h"
 #include "launch.h"
 
@@ -58,6 +67,7 @@ struct Mfma<1> {
 struct DecodeK {
   uint32_t s2;   // fp16: scale in both halves
   uint32_t zn2;  // fp16: -(1024 + z) in both halves
+  uint32_t zn2h; // fp16 uint4: -(1024 + 16 z) in both halves (the high-nibble pairs)
   float sf;      // bf16: scale as float
   float cf;      // bf16: -(magic + z) * scale (exact)
 };
@@ -69,9 +79,11 @@ __device__ __forceinline__ DecodeK make_decode(uint32_t sbits, uint32_t z) {
     d.s2 = (sbits & 0xFFFFu) * 0x10001u;
     if constexpr (BITS == 4) {
       d.zn2 = (0xE400u | z) * 0x10001u;  // fp16 -(1024 + z): sign, exponent of 1024, mantissa z
+      d.zn2h = (0xE400u | (z << 4)) * 0x10001u;
     } else {
       const uint32_t zb = __builtin_bit_cast(uint16_t, (_Float16)(-1152.0f));
       d.zn2 = zb | (zb << 16);
+      d.zn2h = d.zn2;
     }
     d.sf = 0.0f;
     d.cf = 0.0f;
@@ -80,6 +92,7 @@ __device__ __forceinline__ DecodeK make_decode(uint32_t sbits, uint32_t z) {
     d.cf = (BITS == 4) ? -(128.0f + (float)z) * d.sf : -128.0f * d.sf;
     d.s2 = 0;
     d.zn2 = 0;
+    d.zn2h = 0;
   }
   return d;
 }
@@ -90,16 +103,24 @@ __device__ __forceinline__ uint32_t h2_sub_mul(uint32_t t, uint32_t zn2, uint32_
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// uint4: 8 nibbles of one dword (nibble i = k offset i) -> B operand, pairs (0,4)(1,5)(2,6)(3,7)
+// (a & m) | c in one gfx950 v_bitop3_b32 (truth table 0xEA: S0 & S1 | S2).  Left to itself the
+// compiler splits this into an and plus an or, because VOP3 encodings take no literal operands.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
+}
+
+// uint4: 8 nibbles of one dword (nibble i = k offset i) -> B operand, pairs (0,4)(1,5)(2,6)(3,7);
+// fp16: the (1,5) and (3,7) pairs come out as 16 times the weight (their activations are / 16)
 template <int DT>
-__device__ __forceinline__ u32x4_t decode_u4(uint32_t w, const DecodeK& d) {
+__device__ __forceinline__ u32x4_t decode_u4(uint32_t w, const DecodeK& d, uint32_t mlo,
+                                             uint32_t mhi, uint32_t magic) {
   u32x4_t b;
   if constexpr (DT == 0) {
-    const uint32_t M = 0x64006400u;  // fp16 1024 in both halves
-    b[0] = h2_sub_mul((w & 0x000F000Fu) | M, d.zn2, d.s2);
-    b[1] = h2_sub_mul(((w >> 4) & 0x000F000Fu) | M, d.zn2, d.s2);
-    b[2] = h2_sub_mul(((w >> 8) & 0x000F000Fu) | M, d.zn2, d.s2);
-    b[3] = h2_sub_mul(((w >> 12) & 0x000F000Fu) | M, d.zn2, d.s2);
+    const uint32_t w8 = w >> 8;
+    b[0] = h2_sub_mul(and_or(w, mlo, magic), d.zn2, d.s2);
+    b[1] = h2_sub_mul(and_or(w, mhi, magic), d.zn2h, d.s2);
+    b[2] = h2_sub_mul(and_or(w8, mlo, magic), d.zn2, d.s2);
+    b[3] = h2_sub_mul(and_or(w8, mhi, magic), d.zn2h, d.s2);
   } else {
     const uint32_t M = 0x43000000u;  // float 128; nibble at bits 16..19 adds q
 #pragma unroll
@@ -139,19 +160,21 @@ __device__ __forceinline__ u32x4_t decode_s8(uint32_t lo, uint32_t hi, const Dec
   return b;
 }
 
-// (a & m) | c in one gfx950 v_bitop3_b32 (truth table 0xEA: S0 & S1 | S2).  Left to itself the
-// compiler splits this into an and plus an or, because VOP3 encodings take no literal operands.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
-}
-
-// Biased decode for the decode-regime kernels: the MFMA sees magic + q exactly (fp16 1024 + q, or
-// bf16 128 + q), pairs (k0,k4)(k1,k5)(k2,k6)(k3,k7) as in decode_u4.  The bias and the zero point
-// are removed by a second MFMA against -(magic + z) and the group scale is applied to the float32
-// partial sum of the k-block, so per 8 weights the VALU does 3 shifts and 4 and-or.
-__device__ __forceinline__ u32x4_t bias_u4(uint32_t w, uint32_t mask, uint32_t magic) {
-  return u32x4_t{and_or(w, mask, magic), and_or(w >> 4, mask, magic), and_or(w >> 8, mask, magic),
-                 and_or(w >> 12, mask, magic)};
+// Biased decode for the decode-regime kernels: the MFMA sees magic + q exactly (fp16 1024 + q and
+// 1024 + 16 q as in decode_u4, or bf16 128 + q), pairs (k0,k4)(k1,k5)(k2,k6)(k3,k7).  The bias and
+// the zero point are removed by a second MFMA against -(magic + z) (fp16: -(1024 + 16 z) on the
+// high-nibble pairs) and the group scale is applied to the float32 partial sum of the k-block, so
+// per 8 weights the VALU does 1 shift and 4 and-or (bf16: 3 shifts and 4 and-or).
+template <int DT>
+__device__ __forceinline__ u32x4_t bias_u4(uint32_t w, uint32_t mlo, uint32_t mhi, uint32_t magic) {
+  if constexpr (DT == 0) {
+    const uint32_t w8 = w >> 8;
+    return u32x4_t{and_or(w, mlo, magic), and_or(w, mhi, magic), and_or(w8, mlo, magic),
+                   and_or(w8, mhi, magic)};
+  } else {
+    return u32x4_t{and_or(w, mlo, magic), and_or(w >> 4, mlo, magic), and_or(w >> 8, mlo, magic),
+                   and_or(w >> 12, mlo, magic)};
+  }
 }
 
 // int8 biased decode: u = q + 128 in natural k order; fp16 as 1024 + u, bf16 as u itself (exact).
@@ -192,7 +215,13 @@ struct Shape {
   static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
   static constexpr int KBC = KC / KB;                         // k-blocks per chunk
   static constexpr int PF = MT <= 2 ? (NTW == 2 ? 4 : 2) : (NTW == 2 ? 2 : 1);
-  static constexpr int U = KBC / gcd_c(KBC, PF) * PF;         // unroll: lcm(KBC, PF)
+  // activation chunks in flight in registers: a chunk's loads must be issued at least PF k-blocks
+  // before it is stored to LDS, or the wait for it (memory counters complete in issue order) also
+  // waits for the newest weight prefetches and shortens the weight pipeline at every chunk edge
+  static constexpr int AQ0 = (PF + KBC - 1) / KBC;
+  static constexpr int AQ = (MT >= 8 && AQ0 > 1) ? 1 : AQ0;   // BM 128: registers are the limit
+  static constexpr int UA = KBC * AQ;
+  static constexpr int U = UA / gcd_c(UA, PF) * PF;           // unroll: lcm(KBC * AQ, PF)
 };
 
 template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32>
@@ -206,6 +235,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   constexpr int AV = S::AV;
   constexpr int KBC = S::KBC;
   constexpr int U = S::U;
+  constexpr int AQ = S::AQ;
   constexpr int STEPS = KB / 32;                    // MFMAs per k-block
   constexpr int NOUT = ACT ? NTW / 2 : NTW;         // output tiles per wave
   constexpr int WG_COLS = kWaves * NOUT * 16;
@@ -307,29 +337,40 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
     acol[i] = (uint32_t)(idx - r * VPR) * 8;
   }
   const uint32_t klim = (uint32_t)(kb_end * KB);
-  u32x4_t areg[AV];
-  auto load_a = [&](int c) {
+  // chunk c travels in areg[c % AQ] (the index is a compile-time constant at every use)
+  u32x4_t areg[AQ][AV];
+  auto load_a = [&](int q, int c) {
     const uint32_t kbase = (uint32_t)((kb_beg + c * KBC) * KB);
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const uint32_t k = kbase + acol[i];
       const uint32_t off = (arow[i] < 0x80000000u && k < klim) ? arow[i] + k * 2 : 0x80000000u;
-      areg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, off, 0, 0));
+      areg[q][i] =
+          __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, off, 0, 0));
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int q, int buf) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const int idx = tid + i * kThreads;
       const int r = idx / VPR;
       const int c8 = idx - r * VPR;
-      u32x4_t v = areg[i];
+      u32x4_t v = areg[q][i];
       if constexpr (BITS == 4) {
         // (x0..x7) -> (x0,x4,x1,x5,x2,x6,x3,x7), the decode's k pairing
         v = u32x4_t{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
                     __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
                     __builtin_amdgcn_perm(v[3], v[1], 0x05040100u),
                     __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+        if constexpr (DT == 0) {
+          // the (x1,x5) and (x3,x7) words meet weights decoded as 16 times their value.  The
+          // words are copied to scalars first: this compiler's __builtin_bit_cast of a vector
+          // element (bit_cast(half2_t, v[1])) reads element 0 whatever the index.
+          const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+          const uint32_t w1 = v[1], w3 = v[3];
+          v[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, w1) * sixteenth);
+          v[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, w3) * sixteenth);
+        }
       }
       *(u32x4_t*)&s_a[buf][r * LDA + c8 * 8] = v;
     }
@@ -367,7 +408,8 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
     for (int t = 0; t < NTW; ++t) acc[m][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   // biased-decode constants (registers: gfx950 VOP3 encodings take no literals)
   const floatx4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t kMask = p.dec_mask;    // 0x000F000F
+  const uint32_t kMask = p.dec_mask;      // 0x000F000F
+  const uint32_t kMaskHi = p.dec_mask_hi; // 0x00F000F0 (fp16 uint4) or 0x000F000F
   const uint32_t kMagic = p.dec_magic;  // fp16 1024 (0x6400) or bf16 128 (0x4300) in both halves
   // fp16 -(1024 + z) = 0xE400 | z; bf16 -(128 + z) = 0xC300 | z
   constexpr uint32_t kZeroBase = DT == 0 ? 0xE400u : 0xC300u;
@@ -384,15 +426,16 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)(col[t] + rsub) * 2, 0, 0), 0);
   }
 
-  // ---- prologue: chunk 0 in LDS, chunk 1 in flight, PF k-blocks of weights in flight.  Prefetch
-  // indices past the range are clamped to the last k-block (a redundant, in-bounds load), so the
-  // number of loads in flight is the same on every path.
-  load_a(0);
+  // ---- prologue: chunk 0 in LDS, chunks 1..AQ in flight, PF k-blocks of weights in flight.
+  // Prefetch indices past the range are clamped to the last k-block (a redundant, in-bounds load),
+  // so the number of loads in flight is the same on every path.
+  load_a(0, 0);
 #pragma unroll
   for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
-  store_a(0);
+  store_a(0, 0);
   barrier_lds();
-  load_a(1);
+#pragma unroll
+  for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
 
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
   // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
@@ -420,8 +463,10 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
         float sf[NTW];
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          const uint32_t zz = (kZeroBase | (meta[t] >> 16)) * 0x10001u;
-          bz[t] = u32x4_t{zz, zz, zz, zz};
+          const uint32_t z = meta[t] >> 16;
+          const uint32_t zz = (kZeroBase | z) * 0x10001u;
+          const uint32_t zh = DT == 0 ? (kZeroBase | (z << 4)) * 0x10001u : zz;
+          bz[t] = u32x4_t{zz, zh, zz, zh};
           sf[t] = bits_to_float<DT>((uint16_t)(meta[t] & 0xFFFFu));
         }
 #pragma unroll
@@ -431,7 +476,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
           u32x4_t b[NTW];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) b[t] = bias_u4(wq[slot][t][s], kMask, kMagic);
+          for (int t = 0; t < NTW; ++t) b[t] = bias_u4<DT>(wq[slot][t][s], kMask, kMaskHi, kMagic);
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -477,7 +522,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int t = 0; t < NTW; ++t) {
             if constexpr (BITS == 4)
-              b[t] = decode_u4<DT>(wq[slot][t][s], dk[t]);
+              b[t] = decode_u4<DT>(wq[slot][t][s], dk[t], kMask, kMaskHi, kMagic);
             else
               b[t] = decode_s8<DT>(wq[slot][t][2 * s], wq[slot][t][2 * s + 1], dk8[t]);
           }
@@ -490,10 +535,11 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       load_kb(slot, min(kb + PF, kb_last));
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
       if (jc == KBC - 1) {
-        // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+2
-        store_a((c + 1) & 1);
+        // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
+        const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
+        store_a(q, (c + 1) & 1);
         barrier_lds();
-        load_a(c + 2);
+        load_a(q, c + 1 + AQ);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -599,6 +645,7 @@ hipError_t launch_gemm(const GemmParams& p_in, const GemmConfig& c, hipStream_t 
   if (p.split_k < 1 || (p.split_k > 1 && (kb_total % p.split_k || (kb_total / p.split_k) % 2)))
     return hipErrorInvalidValue;
   p.dec_mask = 0x000F000Fu;
+  p.dec_mask_hi = (c.dtype == 0 && c.bits == 4) ? 0x00F000F0u : 0x000F000Fu;
   p.dec_magic = c.dtype == 0 ? 0x64006400u : 0x43004300u;
   if (c.dtype == 0)
     return c.bits == 4 ? launch_bits<0, 4>(p, c, stream) : launch_bits<0, 8>(p, c, stream);

@@ -39,7 +39,8 @@ struct GemmParams {
   void* C;                    // act: dtype [num_slots, N/2]; out_f32: float [split, num_slots, N];
                               // else dtype [num_slots, N]
   int split_k;                // K split count (out_f32 only, else 1)
-  uint32_t dec_mask;          // set by launch_gemm: nibble-pair mask of the biased decode
+  uint32_t dec_mask;          // set by launch_gemm: low nibble-pair mask of the decode
+  uint32_t dec_mask_hi;       // set by launch_gemm: high nibble-pair mask (fp16 uint4 decode)
   uint32_t dec_magic;         // set by launch_gemm: magic bias in both 16-bit halves
 };
 
