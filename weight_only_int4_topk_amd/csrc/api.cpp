@@ -119,6 +119,18 @@ int pick_ntw(int act, int N, int bm, int64_t est_blocks) {
   return N % 256 == 0 ? 4 : 2;
 }
 
+// The uint4 scales and zero points of a workgroup's whole K range are staged in LDS, so a long K
+// may not fit beside the activation tiles: fall back to two column tiles per wavefront (half the
+// rows per workgroup), and reject the shape if even that does not fit.
+int fit_lds(int K, int split, moe::GemmConfig& c, const char* what) {
+  if (moe::gemm_lds_bytes(K, split, c) > moe::kGemmLdsLimit) c.ntw = 2;
+  const size_t need = moe::gemm_lds_bytes(K, split, c);
+  if (need > moe::kGemmLdsLimit)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: K = %d needs %zu bytes of LDS per workgroup (limit %zu)",
+                what, K, need, moe::kGemmLdsLimit);
+  return MOE_OK;
+}
+
 int64_t estimate_blocks(int64_t slots, int E, int bm) {
   return std::max<int64_t>(std::min<int64_t>(E, slots), slots / bm);
 }
@@ -130,7 +142,8 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E);
   p.cap = align_capacity(slots, E, p.bm);
   p.nblk = (int)((p.cap + p.bm - 1) / p.bm);
-  // split the second GEMM (K = I) until there are enough workgroups to fill the chip
+  // split the second GEMM (K = I) until there are about two workgroups per compute unit: more,
+  // shorter workgroups pay their start-up more often and write more float32 partials
   const int kb = bits == 4 ? 128 : 64;
   const int kb_total = I / kb;
   const int64_t est_blocks = estimate_blocks(slots, E, p.bm);
@@ -140,7 +153,7 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   // each split must start on an even k-block (scales are fetched in pairs), so only split while
   // the per-split count stays even
   int split = 1;
-  while (kb_total % (4 * split) == 0 && wgs * split < 2048) split *= 2;
+  while (kb_total % (4 * split) == 0 && wgs * split < 512) split *= 2;
   p.split2 = split;
   size_t off = 0;
   p.off_w = off;      off += up256((size_t)slots * 4);
@@ -271,8 +284,9 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   p.topk_w = topk_weights;
   p.C = C;
   p.split_k = 1;
-  const moe::GemmConfig c{dtype, quant->bits, block_m, act, 0,
-                          pick_ntw(act, N, block_m, estimate_blocks(num_slots, E, block_m))};
+  moe::GemmConfig c{dtype, quant->bits, block_m, act, 0,
+                    pick_ntw(act, N, block_m, estimate_blocks(num_slots, E, block_m))};
+  if (int rc = fit_lds(K, 1, c, "gemm")) return rc;
   hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm launch");
 }
@@ -315,6 +329,10 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   const Plan pl = make_plan(M, H, I, E, topk, quant->bits, dtype, block_m);
   if (workspace_bytes < pl.total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.total);
+  moe::GemmConfig c1{dtype, quant->bits, pl.bm, 1, 0, pl.ntw1};
+  moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2};
+  if (int rc = fit_lds(H, 1, c1, "gemm1")) return rc;
+  if (int rc = fit_lds(I, pl.split2, c2, "gemm2")) return rc;
 
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -352,7 +370,7 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   g1.topk_w = nullptr;
   g1.C = inter;
   g1.split_k = 1;
-  e = moe::launch_gemm(g1, moe::GemmConfig{dtype, quant->bits, pl.bm, 1, 0, pl.ntw1}, st);
+  e = moe::launch_gemm(g1, c1, st);
   if (e != hipSuccess) return hip_fail(e, "gemm1 launch");
 
   moe::GemmParams g2 = g1;
@@ -366,7 +384,7 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   g2.K = I;
   g2.C = part;
   g2.split_k = pl.split2;
-  e = moe::launch_gemm(g2, moe::GemmConfig{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2}, st);
+  e = moe::launch_gemm(g2, c2, st);
   if (e != hipSuccess) return hip_fail(e, "gemm2 launch");
 
   e = moe::launch_combine(part, pl.split2, tw, M, topk, H, dtype, out, st);

@@ -97,6 +97,10 @@ __device__ __forceinline__ DecodeK make_decode(uint32_t sbits, uint32_t z) {
   return d;
 }
 
+__device__ __forceinline__ uint32_t h2_add(uint32_t x, uint32_t y) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x) + __builtin_bit_cast(half2_t, y));
+}
+
 __device__ __forceinline__ uint32_t h2_sub_mul(uint32_t t, uint32_t zn2, uint32_t s2) {
   const half2_t r = (__builtin_bit_cast(half2_t, t) + __builtin_bit_cast(half2_t, zn2)) *
                     __builtin_bit_cast(half2_t, s2);
@@ -241,12 +245,15 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   constexpr int WG_COLS = kWaves * NOUT * 16;
   constexpr int VPR = KC / 8;                       // 16-byte vectors per activation row chunk
   constexpr int R = kWaves * NTW * 16;              // weight rows of the workgroup
+  // metadata row pitch in dwords: consecutive staging threads write entries 2 * RP apart, and
+  // RP = 2 (mod 32) spreads them over the LDS banks
+  constexpr int RP = R + 2;
   // decode regime: biased codes with MFMA-side bias removal (fewer VALU ops per weight); prefill:
   // exact decoded weights, no extra MFMAs (the matrix cores are the bottleneck there)
   constexpr bool BIASED = MT <= 2;
   // uint4 scales and zero points of the workgroup's rows for its whole K range are staged once,
   // before the weight stream starts, into dynamic LDS as meta[kb - kb_beg][row] = scale | zero << 16
-  // (the host sizes it: rows * k-blocks * 4 bytes).  Consecutive threads read consecutive pairs of
+  // (the host sizes it: (rows + 2) * k-blocks * 4 bytes).  Consecutive threads read consecutive pairs of
   // k-blocks of one row, so each cache line of scales is touched once.  Per-lane loads of a 2-byte
   // scale and a 1-byte zero point every k-block would triple the memory instructions of the weight
   // stream and cap it near 3.2 TB/s.
@@ -386,8 +393,8 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const int kb = kb_beg + 2 * j;
       const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs_s, n * srow_bytes + kb * 2, 0, 0);
       const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rs_z, n * zrow_bytes + (kb >> 1), 0, 0);
-      s_meta[(2 * j) * R + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
-      if (kb + 1 < kb_end) s_meta[(2 * j + 1) * R + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
+      s_meta[(2 * j) * RP + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
+      if (kb + 1 < kb_end) s_meta[(2 * j + 1) * RP + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
     }
     __syncthreads();
   }
@@ -426,6 +433,34 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)(col[t] + rsub) * 2, 0, 0), 0);
   }
 
+  // ---- activation fragments and metadata of one k-block, read from LDS one k-block ahead of
+  // their use, so LDS latency is off the MFMA chain (fragments only for BM <= 32, where they
+  // fit in registers).  Fragment of step s, row tile m: 16 bytes of row m * 16 + rsub at k
+  // offset grp * (KB / 4) + s * 8 of the k-block.
+  constexpr bool FRAG_AHEAD = MT <= 2;
+  constexpr int FS = FRAG_AHEAD ? STEPS : 1;
+  constexpr int FM = FRAG_AHEAD ? MT : 1;
+  u32x4_t af[FS][FM];
+  uint32_t mf[NTW];
+  auto frag_base = [&](int idx) -> const uint16_t* {  // idx = k-block index relative to kb_beg
+    const int c = idx / KBC;
+    return s_a[c & 1] + rsub * LDA + (idx - c * KBC) * KB + grp * (KB / 4);
+  };
+  auto load_frag = [&](int idx) {
+    if constexpr (FRAG_AHEAD) {
+      const uint16_t* abase = frag_base(idx);
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) af[st][m] = *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
+    }
+    if constexpr (BITS == 4) {
+      const int mrow = min(kb_beg + idx, kb_last) - kb_beg;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) mf[t] = s_meta[mrow * RP + (wave * NTW + t) * 16 + rsub];
+    }
+  };
+
   // ---- prologue: chunk 0 in LDS, chunks 1..AQ in flight, PF k-blocks of weights in flight.
   // Prefetch indices past the range are clamped to the last k-block (a redundant, in-bounds load),
   // so the number of loads in flight is the same on every path.
@@ -436,6 +471,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   barrier_lds();
 #pragma unroll
   for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
+  load_frag(0);
 
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
   // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
@@ -444,20 +480,26 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   for (int it = 0; it < n_iter; ++it) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int kb = kb_beg + it * U + j;
+      const int idx = it * U + j;
+      const int kb = kb_beg + idx;
       const int slot = j % PF;
       const int jc = j % KBC;
-      const int c = (it * U + j) / KBC;
-      const uint16_t* sa = s_a[c & 1];
-      const uint16_t* abase = sa + rsub * LDA + jc * KB + grp * (KB / 4);
+      const int c = idx / KBC;
+      // this k-block's fragments (read during the previous one, or here for BM >= 64)
+      const uint16_t* abase = frag_base(idx);
+      auto a_s = [&](int st, int m) -> u32x4_t {
+        if constexpr (FRAG_AHEAD) return af[st][m];
+        else return *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
+      };
       uint32_t meta[NTW];
-      if constexpr (BITS == 4) {
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
-          meta[t] = s_meta[(min(kb, kb_last) - kb_beg) * R + (wave * NTW + t) * 16 + rsub];
-      }
+      for (int t = 0; t < NTW; ++t) meta[t] = mf[t];
       if constexpr (BIASED && BITS == 4) {
-        // magic-biased codes, zero point and bias removed by a broadcast MFMA, scale per k-block
+        // magic-biased codes; the bias and the zero point are removed either by a broadcast MFMA
+        // (BM 16: the matrix cores have room) or, for fp16 at BM 32, by one exact half-precision
+        // subtraction per two weights ((1024 + q) - (1024 + z) = q - z), which halves the MFMAs
+        // where they would otherwise bound the kernel.  The scale is applied per k-block.
+        constexpr bool SUBZ = DT == 0 && MT == 2;
         floatx4_t accg[MT][NTW];
         u32x4_t bz[NTW];
         float sf[NTW];
@@ -470,19 +512,24 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           sf[t] = bits_to_float<DT>((uint16_t)(meta[t] & 0xFFFFu));
         }
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-          u32x4_t a[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
+        for (int st = 0; st < STEPS; ++st) {
           u32x4_t b[NTW];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) b[t] = bias_u4<DT>(wq[slot][t][s], kMask, kMaskHi, kMagic);
+          for (int t = 0; t < NTW; ++t) {
+            b[t] = bias_u4<DT>(wq[slot][t][st], kMask, kMaskHi, kMagic);
+            if constexpr (SUBZ) {
+              // element copies first: a bit_cast of a vector element reads element 0
+              const uint32_t b0 = b[t][0], b1 = b[t][1], b2 = b[t][2], b3 = b[t][3];
+              const uint32_t zlo = bz[t][0], zhi = bz[t][1];
+              b[t] = u32x4_t{h2_add(b0, zlo), h2_add(b1, zhi), h2_add(b2, zlo), h2_add(b3, zhi)};
+            }
+          }
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int t = 0; t < NTW; ++t) {
-              accg[m][t] = Mfma<DT>::run(a[m], b[t], s == 0 ? zero4 : accg[m][t]);
-              accg[m][t] = Mfma<DT>::run(a[m], bz[t], accg[m][t]);
+              accg[m][t] = Mfma<DT>::run(a_s(st, m), b[t], st == 0 ? zero4 : accg[m][t]);
+              if constexpr (!SUBZ) accg[m][t] = Mfma<DT>::run(a_s(st, m), bz[t], accg[m][t]);
             }
         }
 #pragma unroll
@@ -494,17 +541,14 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       } else if constexpr (BIASED) {
         // int8: biased codes accumulate over all of K; row sums (ones MFMA) remove the bias at the end
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-          u32x4_t a[MT];
+        for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
-          for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
-#pragma unroll
-          for (int m = 0; m < MT; ++m) rsum[m] = Mfma<DT>::run(a[m], ones, rsum[m]);
+          for (int m = 0; m < MT; ++m) rsum[m] = Mfma<DT>::run(a_s(st, m), ones, rsum[m]);
 #pragma unroll
           for (int t = 0; t < NTW; ++t) {
-            const u32x4_t b = bias_s8<DT>(wq[slot][t][2 * s], wq[slot][t][2 * s + 1]);
+            const u32x4_t bb = bias_s8<DT>(wq[slot][t][2 * st], wq[slot][t][2 * st + 1]);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m][t] = Mfma<DT>::run(a[m], b, acc[m][t]);
+            for (int m = 0; m < MT; ++m) acc[m][t] = Mfma<DT>::run(a_s(st, m), bb, acc[m][t]);
           }
         }
       } else {
@@ -514,34 +558,31 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           for (int t = 0; t < NTW; ++t) dk[t] = make_decode<DT, 4>(meta[t] & 0xFFFFu, meta[t] >> 16);
         }
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-          u32x4_t a[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) a[m] = *(const u32x4_t*)(abase + m * 16 * LDA + s * 8);
+        for (int st = 0; st < STEPS; ++st) {
           u32x4_t b[NTW];
 #pragma unroll
           for (int t = 0; t < NTW; ++t) {
             if constexpr (BITS == 4)
-              b[t] = decode_u4<DT>(wq[slot][t][s], dk[t], kMask, kMaskHi, kMagic);
+              b[t] = decode_u4<DT>(wq[slot][t][st], dk[t], kMask, kMaskHi, kMagic);
             else
-              b[t] = decode_s8<DT>(wq[slot][t][2 * s], wq[slot][t][2 * s + 1], dk8[t]);
+              b[t] = decode_s8<DT>(wq[slot][t][2 * st], wq[slot][t][2 * st + 1], dk8[t]);
           }
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int t = 0; t < NTW; ++t) acc[m][t] = Mfma<DT>::run(a[m], b[t], acc[m][t]);
+            for (int t = 0; t < NTW; ++t) acc[m][t] = Mfma<DT>::run(a_s(st, m), b[t], acc[m][t]);
         }
       }
       load_kb(slot, min(kb + PF, kb_last));
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is issued
       if (jc == KBC - 1) {
         // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
         const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
         store_a(q, (c + 1) & 1);
         barrier_lds();
         load_a(q, c + 1 + AQ);
-        __builtin_amdgcn_sched_barrier(0);
       }
+      load_frag(idx + 1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetches where they are issued
     }
   }
 
@@ -593,7 +634,8 @@ hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stre
   const long long grid = (long long)n_chunks * p.num_blocks * p.split_k;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const size_t lds = gemm_meta_lds_bytes(p, c);
+  const size_t lds = gemm_meta_lds_bytes(p.K, p.split_k, c);
+  if (gemm_lds_bytes(p.K, p.split_k, c) > kGemmLdsLimit) return hipErrorInvalidValue;
   if (c.act)
     hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 1, 0>), dim3((unsigned)grid),
                        dim3(kThreads), lds, stream, p);
@@ -625,12 +667,30 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 
 }  // namespace
 
-size_t gemm_meta_lds_bytes(const GemmParams& p, const GemmConfig& c) {
+size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c) {
   if (c.bits != 4) return 0;
   const int ntw = (c.ntw == 4 && c.block_m <= 32) ? 4 : 2;
-  const int kb_total = p.K / 128;
-  const int kb_per = (kb_total + p.split_k - 1) / p.split_k;
-  return (size_t)kWaves * ntw * 16 * kb_per * 4;
+  const int kb_total = K / 128;
+  const int kb_per = (kb_total + split_k - 1) / split_k;
+  return (size_t)(kWaves * ntw * 16 + 2) * kb_per * 4;  // row pitch R + 2 dwords
+}
+
+template <int BITS, int MT>
+constexpr size_t static_lds_bytes() {
+  using S = Shape<BITS, MT, 2>;  // the activation tiles do not depend on the column tiles
+  return sizeof(uint16_t) * 2 * S::BM * S::LDA + 2 * sizeof(int) * S::BM;
+}
+
+size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c) {
+  size_t st = 0;
+  const bool b4 = c.bits == 4;
+  switch (c.block_m) {
+    case 16: st = b4 ? static_lds_bytes<4, 1>() : static_lds_bytes<8, 1>(); break;
+    case 32: st = b4 ? static_lds_bytes<4, 2>() : static_lds_bytes<8, 2>(); break;
+    case 64: st = b4 ? static_lds_bytes<4, 4>() : static_lds_bytes<8, 4>(); break;
+    default: st = b4 ? static_lds_bytes<4, 8>() : static_lds_bytes<8, 8>(); break;
+  }
+  return st + gemm_meta_lds_bytes(K, split_k, c);
 }
 
 int gemm_wg_cols(const GemmConfig& c) {

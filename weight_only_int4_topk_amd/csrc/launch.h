@@ -55,8 +55,11 @@ struct GemmConfig {
 
 // Columns of output one workgroup covers (N % this must be 0; act: gate columns).
 int gemm_wg_cols(const GemmConfig& c);
-// Dynamic LDS of one workgroup for the staged uint4 scales and zero points.
-size_t gemm_meta_lds_bytes(const GemmParams& p, const GemmConfig& c);
+// Dynamic LDS of one workgroup for the staged uint4 scales and zero points of its K range.
+size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c);
+// All LDS of one workgroup (activation tiles + staged metadata); at most kGemmLdsLimit.
+size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c);
+constexpr size_t kGemmLdsLimit = 160 * 1024;
 hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
 
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
