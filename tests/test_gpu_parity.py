@@ -168,6 +168,9 @@ SMALL = {
     "no_renorm": synth.Workload("nr", E=32, H=512, I=256, topk=4, Ms=(40,), renormalize=False),
     "dense_single_expert": synth.Workload("d1", E=1, H=512, I=512, topk=1, Ms=(33,)),
     "all_experts": synth.Workload("ae", E=4, H=256, I=256, topk=4, Ms=(21,)),
+    # few workgroups: the first GEMM is split over K (14 k-blocks into 2 x 7, the second split
+    # starting on an odd k-block) and SiLU(gate) * up runs after the float32 partials are summed
+    "split_odd_start": synth.Workload("so", E=8, H=1792, I=768, topk=2, Ms=(3,)),
 }
 
 

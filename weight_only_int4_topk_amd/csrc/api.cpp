@@ -93,6 +93,7 @@ struct Plan {
   int bm;
   int64_t cap;
   int nblk;
+  int split1;  // > 1: the first GEMM writes float32 partials, a second pass applies SiLU(gate) * up
   int split2;
   int ntw1, ntw2;
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
@@ -131,6 +132,19 @@ int fit_lds(int K, int split, moe::GemmConfig& c, const char* what) {
   return MOE_OK;
 }
 
+// Split count over K for a grouped GEMM with `wgs` workgroups per split: the smallest divisor of
+// the k-block count that reaches target_wgs workgroups while leaving every split at least min_kb
+// k-blocks (start-up is paid per workgroup), else the largest such divisor.
+int pick_split(int kb_total, int64_t wgs, int min_kb, int64_t target_wgs) {
+  int best = 1;
+  for (int d = 1; d <= kb_total; ++d) {
+    if (kb_total % d || kb_total / d < min_kb) continue;
+    best = d;
+    if (wgs * d >= target_wgs) break;
+  }
+  return best;
+}
+
 int64_t estimate_blocks(int64_t slots, int E, int bm) {
   return std::max<int64_t>(std::min<int64_t>(E, slots), slots / bm);
 }
@@ -142,19 +156,20 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E);
   p.cap = align_capacity(slots, E, p.bm);
   p.nblk = (int)((p.cap + p.bm - 1) / p.bm);
-  // split the second GEMM (K = I) until there are about two workgroups per compute unit: more,
-  // shorter workgroups pay their start-up more often and write more float32 partials
   const int kb = bits == 4 ? 128 : 64;
-  const int kb_total = I / kb;
   const int64_t est_blocks = estimate_blocks(slots, E, p.bm);
   p.ntw1 = pick_ntw(1, 2 * I, p.bm, est_blocks);
   p.ntw2 = pick_ntw(0, H, p.bm, est_blocks);
-  const int64_t wgs = est_blocks * (H / (p.ntw2 * 64));
-  // each split must start on an even k-block (scales are fetched in pairs), so only split while
-  // the per-split count stays even
-  int split = 1;
-  while (kb_total % (4 * split) == 0 && wgs * split < 512) split *= 2;
-  p.split2 = split;
+  // The first GEMM (K = H) keeps SiLU in its epilogue unless it has fewer workgroups than compute
+  // units (few experts and a narrow I, as in a tensor-parallel share of many small experts): then
+  // it is split over K into float32 partials.  Measured: with a few hundred workgroups the extra
+  // pass costs what the split gains.
+  const int64_t wgs1 = est_blocks * (I / 64);
+  p.split1 = wgs1 < 256 ? pick_split(H / kb, wgs1, 4, 512) : 1;
+  // The second GEMM (K = I) writes float32 partials anyway; split it to about two workgroups per
+  // compute unit (more, shorter workgroups pay their start-up more often and write more partials)
+  const int64_t wgs2 = est_blocks * (H / (p.ntw2 * 64));
+  p.split2 = pick_split(I / kb, wgs2, 4, 512);
   size_t off = 0;
   p.off_w = off;      off += up256((size_t)slots * 4);
   p.off_ids = off;    off += up256((size_t)slots * 4);
@@ -162,7 +177,8 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   p.off_eids = off;   off += up256((size_t)p.nblk * 4);
   p.off_npost = off;  off += 256;
   p.off_inter = off;  off += up256((size_t)slots * I * 2);
-  p.off_part = off;   off += up256((size_t)split * slots * H * 4);
+  p.off_part = off;
+  off += up256(std::max((size_t)p.split1 * slots * 2 * I, (size_t)p.split2 * slots * H) * 4);
   p.total = off;
   return p;
 }
@@ -329,9 +345,13 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   const Plan pl = make_plan(M, H, I, E, topk, quant->bits, dtype, block_m);
   if (workspace_bytes < pl.total)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.total);
-  moe::GemmConfig c1{dtype, quant->bits, pl.bm, 1, 0, pl.ntw1};
+  const bool split1 = pl.split1 > 1;
+  // split: plain columns (gate rows, then up rows) into float32 partials, 2 column tiles per
+  // wavefront so the workgroup count matches the estimate the split was chosen for
+  moe::GemmConfig c1{dtype, quant->bits, pl.bm, split1 ? 0 : 1, split1 ? 1 : 0,
+                     split1 ? 2 : pl.ntw1};
   moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2};
-  if (int rc = fit_lds(H, 1, c1, "gemm1")) return rc;
+  if (int rc = fit_lds(H, pl.split1, c1, "gemm1")) return rc;
   if (int rc = fit_lds(I, pl.split2, c2, "gemm2")) return rc;
 
   hipStream_t st = (hipStream_t)stream;
@@ -368,10 +388,14 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   g1.num_blocks = (int)(pl.cap / pl.bm);
   g1.num_slots = slots;
   g1.topk_w = nullptr;
-  g1.C = inter;
-  g1.split_k = 1;
+  g1.C = split1 ? (void*)part : inter;
+  g1.split_k = pl.split1;
   e = moe::launch_gemm(g1, c1, st);
   if (e != hipSuccess) return hip_fail(e, "gemm1 launch");
+  if (split1) {
+    e = moe::launch_act_combine(part, pl.split1, slots, I, dtype, inter, st);
+    if (e != hipSuccess) return hip_fail(e, "gemm1 combine launch");
+  }
 
   moe::GemmParams g2 = g1;
   g2.A = inter;

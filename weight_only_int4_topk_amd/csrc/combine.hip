@@ -1,4 +1,5 @@
-// Top-k weighted combine on gfx950: out[m, h] = sum_j w[m,j] * sum_z partial[z, m*topk + j, h].
+// Top-k weighted combine on gfx950: out[m, h] = sum_j w[m,j] * sum_z partial[z, m*topk + j, h];
+// and, when the first GEMM is split over K, the sum of its partials followed by SiLU(gate) * up.
 //
 // The second grouped GEMM leaves one float32 row per token-slot (split over K into `split`
 // partials); each token's topk slots are adjacent rows, so this is a short streaming reduction in a
@@ -10,6 +11,57 @@
 namespace moe {
 namespace {
 
+// Streaming sums over float32 partials, issued in batches of kBatch independent 16-byte loads so
+// that a long reduction costs a few memory round trips instead of one per term.  Terms are added in
+// a fixed order, so results do not depend on the batching.
+constexpr int kBatch = 16;
+
+// sum_z src[z * stride .. + 3], z ascending
+__device__ __forceinline__ floatx4_t sum_splits(const float* src, int split, size_t stride) {
+  floatx4_t v = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < split; z0 += kBatch) {
+    floatx4_t t[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (z0 + q < split) t[q] = *(const floatx4_t*)(src + (size_t)(z0 + q) * stride);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (z0 + q < split) v = (z0 + q == 0) ? t[q] : v + t[q];
+  }
+  return v;
+}
+
+// sum_j w[j] * (sum_z src[j * H + z * stride .. + 3]) with z ascending inside j ascending; the
+// (j, z) terms are loaded kBatch at a time across slot boundaries
+__device__ __forceinline__ floatx4_t sum_weighted_slots(const float* src, const float* w, int topk,
+                                                        int split, int H, size_t stride) {
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  floatx4_t v = {0.f, 0.f, 0.f, 0.f};
+  const int n = topk * split;
+  for (int t0 = 0; t0 < n; t0 += kBatch) {
+    floatx4_t t[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int k = t0 + q;
+      if (k < n) {
+        const int j = k / split;
+        t[q] = *(const floatx4_t*)(src + (size_t)j * H + (size_t)(k - j * split) * stride);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int k = t0 + q;
+      if (k < n) {
+        const int j = k / split;
+        const int zz = k - j * split;
+        v = zz == 0 ? t[q] : v + t[q];
+        if (zz == split - 1) acc += w[j] * v;
+      }
+    }
+  }
+  return acc;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partial, int split,
                                                       size_t split_stride,
@@ -20,20 +72,52 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   if (idx >= (size_t)M * h4) return;
   const int m = (int)(idx / h4);
   const int c = (int)(idx - (size_t)m * h4) * 4;
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const size_t slot = (size_t)m * topk + j;
-    const float* src = partial + slot * H + c;
-    floatx4_t v = *(const floatx4_t*)src;
-    for (int zz = 1; zz < split; ++zz) v += *(const floatx4_t*)(src + zz * split_stride);
-    acc += topk_w[slot] * v;
-  }
+  const size_t slot0 = (size_t)m * topk;
+  const floatx4_t acc = sum_weighted_slots(partial + slot0 * H + c, topk_w + slot0, topk, split, H,
+                                           split_stride);
   const uint32_t lo = DT == 0 ? f32x2_to_f16x2(acc[0], acc[1]) : f32x2_to_bf16x2(acc[0], acc[1]);
   const uint32_t hi = DT == 0 ? f32x2_to_f16x2(acc[2], acc[3]) : f32x2_to_bf16x2(acc[2], acc[3]);
   *(uint2*)(out + (size_t)m * H + c) = make_uint2(lo, hi);
 }
 
+// First GEMM split over K: inter[s, i] = SiLU(g) * u with g = sum_z partial[z, s, i] and
+// u = sum_z partial[z, s, I + i] (z ascending), rounded to dtype; four columns per thread.
+template <int DT>
+__global__ void __launch_bounds__(256) act_combine_kernel(const float* __restrict__ partial,
+                                                          int split, size_t split_stride, int slots,
+                                                          int I, uint16_t* __restrict__ inter) {
+  const int i4 = I / 4;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)slots * i4) return;
+  const int s = (int)(idx / i4);
+  const int c = (int)(idx - (size_t)s * i4) * 4;
+  const float* src = partial + (size_t)s * 2 * I + c;
+  const floatx4_t g = sum_splits(src, split, split_stride);
+  const floatx4_t u = sum_splits(src + I, split, split_stride);
+  floatx4_t a;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) a[q] = g[q] / (1.0f + __expf(-g[q])) * u[q];
+  const uint32_t lo = DT == 0 ? f32x2_to_f16x2(a[0], a[1]) : f32x2_to_bf16x2(a[0], a[1]);
+  const uint32_t hi = DT == 0 ? f32x2_to_f16x2(a[2], a[3]) : f32x2_to_bf16x2(a[2], a[3]);
+  *(uint2*)(inter + (size_t)s * I + c) = make_uint2(lo, hi);
+}
+
 }  // namespace
+
+hipError_t launch_act_combine(const float* partial, int split, int slots, int I, int dtype,
+                              void* inter, hipStream_t stream) {
+  if (slots == 0) return hipSuccess;
+  const size_t total = (size_t)slots * (I / 4);
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  const size_t stride = (size_t)slots * 2 * I;
+  if (dtype == 0)
+    hipLaunchKernelGGL(act_combine_kernel<0>, dim3(grid), dim3(256), 0, stream, partial, split,
+                       stride, slots, I, (uint16_t*)inter);
+  else
+    hipLaunchKernelGGL(act_combine_kernel<1>, dim3(grid), dim3(256), 0, stream, partial, split,
+                       stride, slots, I, (uint16_t*)inter);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream) {

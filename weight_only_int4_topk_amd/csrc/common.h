@@ -23,23 +23,66 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Wave-wide arg-best over (value, index) pairs; every lane returns the winner.
-__device__ __forceinline__ void wave_argbest(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off, kWave);
-    int oi = __shfl_xor(i, off, kWave);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
+// DPP lane movements inside a 16-lane row (no LDS round trip): partner = lane ^ 1, lane ^ 2, the
+// mirror lane in the 8-lane half row, the mirror lane in the row.  After the four steps of a
+// butterfly every lane of a row holds the row's result.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argbest_step(float& v, int& i) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+// Wave-wide arg-best over (value, index) pairs; every lane returns the winner (wave-uniform).
+// Rows of 16 lanes reduce with DPP, the four row winners are compared in scalar registers.
+__device__ __forceinline__ void wave_argbest(float& v, int& i) {
+  argbest_step<kDppXor1>(v, i);
+  argbest_step<kDppXor2>(v, i);
+  argbest_step<kDppHalfMirror>(v, i);
+  argbest_step<kDppMirror>(v, i);
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  for (int r = 16; r < kWave; r += 16) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r));
+    const int ri = __builtin_amdgcn_readlane(i, r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
+    }
+  }
+  v = bv;
+  i = bi;
+}
+
+// Wave-wide sum in a fixed order (rows by DPP, then rows 0 + 1 + 2 + 3); every lane returns it.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }

@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   }
   __syncthreads();
 
-  // K range of this split, in k-blocks (the host keeps kb_beg even)
+  // K range of this split, in k-blocks (a split past the end has an empty range and writes zeros)
   const int kb_total = K / KB;
   const int kb_per = (kb_total + split - 1) / split;
   const int kb_beg = z * kb_per;
@@ -383,18 +383,22 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
     }
   };
 
-  // ---- uint4 metadata for the whole K range of this split (kb_beg and the range length are even)
+  // ---- uint4 metadata for the whole K range of this split, fetched in even-aligned pairs of
+  // k-blocks (one 4-byte load holds two scales, one byte two zero points); a pair straddling either
+  // end of the range writes only its in-range half
   if constexpr (BITS == 4) {
-    const int npair = (kb_end - kb_beg + 1) >> 1;
+    const int kb0 = kb_beg & ~1;
+    const int npair = (kb_end - kb0 + 1) >> 1;
     for (int item = tid; item < R * npair; item += kThreads) {
       const int lr = item / npair;
       const int j = item - lr * npair;
       const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
-      const int kb = kb_beg + 2 * j;
+      const int kb = kb0 + 2 * j;
       const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs_s, n * srow_bytes + kb * 2, 0, 0);
       const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rs_z, n * zrow_bytes + (kb >> 1), 0, 0);
-      s_meta[(2 * j) * RP + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
-      if (kb + 1 < kb_end) s_meta[(2 * j + 1) * RP + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
+      if (kb >= kb_beg) s_meta[(kb - kb_beg) * RP + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
+      if (kb + 1 < kb_end)
+        s_meta[(kb + 1 - kb_beg) * RP + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
     }
     __syncthreads();
   }
@@ -700,9 +704,8 @@ int gemm_wg_cols(const GemmConfig& c) {
 
 hipError_t launch_gemm(const GemmParams& p_in, const GemmConfig& c, hipStream_t stream) {
   GemmParams p = p_in;
-  // uint4 scales are fetched in pairs of k-blocks: every split must start on an even k-block
   const int kb_total = p.K / (c.bits == 4 ? 128 : 64);
-  if (p.split_k < 1 || (p.split_k > 1 && (kb_total % p.split_k || (kb_total / p.split_k) % 2)))
+  if (p.split_k < 1 || p.split_k > kb_total || (p.split_k > 1 && !c.out_f32))
     return hipErrorInvalidValue;
   p.dec_mask = 0x000F000Fu;
   p.dec_mask_hi = (c.dtype == 0 && c.bits == 4) ? 0x00F000F0u : 0x000F000Fu;

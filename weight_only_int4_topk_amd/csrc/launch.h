@@ -64,5 +64,8 @@ hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t str
 
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);
+// inter[s, i] = SiLU(sum_z partial[z, s, i]) * sum_z partial[z, s, I + i] (first GEMM split over K)
+hipError_t launch_act_combine(const float* partial, int split, int slots, int I, int dtype,
+                              void* inter, hipStream_t stream);
 
 }  // namespace moe

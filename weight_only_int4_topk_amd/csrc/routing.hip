@@ -133,6 +133,7 @@ __global__ void __launch_bounds__(256) routing_kernel(const float* __restrict__ 
     float gscore = kNone;
     if (lane < ng) {
       float b1 = kNone, b2 = kNone;
+#pragma unroll 8
       for (int t = 0; t < gs; ++t) {
         const float s = sc[lane * gs + t];
         if (s > b1) {
