@@ -30,12 +30,13 @@
 // nibble mask, scaled by 16.  The activations at those k offsets are stored in LDS divided by 16
 // (exact for normal fp16 values), so every product a * w is unchanged: one shift and four
 // and-or per 8 weights instead of three shifts.  bf16 has too few mantissa bits for 1024 + 16 q
-// under any exponent, so it keeps the three shifts.
+// under any exponent, so its biased codes keep the three shifts, and its exact decode converts
+// each nibble from a byte of its own in natural k order (no activation permutation then).
 //
 // Decoding is exact: the MFMA sees the correctly rounded dtype value of (q - z) * s (fp16: the
 // subtraction of two exact half-precision integers 1024+q and 1024+z, then one rounded multiply,
-// or 16 times that value against an activation divided by 16; bf16: an exact float32 fma of 128+q
-// against s and -(128+z)*s, then one rounding to bf16).
+// or 16 times that value against an activation divided by 16; bf16: an exact float32 fma of q
+// against s and -z*s, then one rounding to bf16).
 #include "common.h"
 #include "launch.h"
 
@@ -89,7 +90,7 @@ __device__ __forceinline__ DecodeK make_decode(uint32_t sbits, uint32_t z) {
     d.cf = 0.0f;
   } else {
     d.sf = __uint_as_float(sbits << 16);
-    d.cf = (BITS == 4) ? -(128.0f + (float)z) * d.sf : -128.0f * d.sf;
+    d.cf = (BITS == 4) ? -(float)z * d.sf : -128.0f * d.sf;  // exact: 4- or 8-bit times 8-bit
     d.s2 = 0;
     d.zn2 = 0;
     d.zn2h = 0;
@@ -113,8 +114,9 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);
 }
 
-// uint4: 8 nibbles of one dword (nibble i = k offset i) -> B operand, pairs (0,4)(1,5)(2,6)(3,7);
-// fp16: the (1,5) and (3,7) pairs come out as 16 times the weight (their activations are / 16)
+// uint4: 8 nibbles of one dword (nibble i = k offset i) -> B operand.  fp16: pairs (0,4)(1,5)(2,6)
+// (3,7), the (1,5) and (3,7) pairs as 16 times the weight (their activations are / 16); bf16:
+// natural order.
 template <int DT>
 __device__ __forceinline__ u32x4_t decode_u4(uint32_t w, const DecodeK& d, uint32_t mlo,
                                              uint32_t mhi, uint32_t magic) {
@@ -126,12 +128,16 @@ __device__ __forceinline__ u32x4_t decode_u4(uint32_t w, const DecodeK& d, uint3
     b[2] = h2_sub_mul(and_or(w8, mlo, magic), d.zn2, d.s2);
     b[3] = h2_sub_mul(and_or(w8, mhi, magic), d.zn2h, d.s2);
   } else {
-    const uint32_t M = 0x43000000u;  // float 128; nibble at bits 16..19 adds q
+    // bf16, natural k order (k0,k1)(k2,k3)(k4,k5)(k6,k7): every nibble in a byte of its own, one
+    // byte-to-float conversion each, then (q - z) * s exactly in one float32 fma (4-bit times 8-bit
+    // operands) and one rounding to bf16
+    const uint32_t even = w & 0x0F0F0F0Fu;
+    const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(((w << (16 - 4 * i)) & 0x000F0000u) | M);
-      const float hi = __uint_as_float(((w >> (4 * i)) & 0x000F0000u) | M);
-      b[i] = f32x2_to_bf16x2(__builtin_fmaf(lo, d.sf, d.cf), __builtin_fmaf(hi, d.sf, d.cf));
+      const float q0 = (float)((even >> (8 * i)) & 0xFFu);
+      const float q1 = (float)((odd >> (8 * i)) & 0xFFu);
+      b[i] = f32x2_to_bf16x2(__builtin_fmaf(q0, d.sf, d.cf), __builtin_fmaf(q1, d.sf, d.cf));
     }
   }
   return b;
@@ -251,6 +257,9 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // decode regime: biased codes with MFMA-side bias removal (fewer VALU ops per weight); prefill:
   // exact decoded weights, no extra MFMAs (the matrix cores are the bottleneck there)
   constexpr bool BIASED = MT <= 2;
+  // the activation k order in LDS follows the weight decode: permuted for the shift-and-mask
+  // decodes (fp16, and bf16 biased codes), natural for the bf16 exact decode and for int8
+  constexpr bool PERM_A = BITS == 4 && (DT == 0 || BIASED);
   // uint4 scales and zero points of the workgroup's rows for its whole K range are staged once,
   // before the weight stream starts, into dynamic LDS as meta[kb - kb_beg][row] = scale | zero << 16
   // (the host sizes it: (rows + 2) * k-blocks * 4 bytes).  Consecutive threads read consecutive pairs of
@@ -363,7 +372,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const int r = idx / VPR;
       const int c8 = idx - r * VPR;
       u32x4_t v = areg[q][i];
-      if constexpr (BITS == 4) {
+      if constexpr (PERM_A) {
         // (x0..x7) -> (x0,x4,x1,x5,x2,x6,x3,x7), the decode's k pairing
         v = u32x4_t{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u),
                     __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
