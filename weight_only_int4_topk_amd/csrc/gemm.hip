@@ -204,6 +204,14 @@ __device__ __forceinline__ u32x4_t bias_s8(uint32_t lo, uint32_t hi) {
   }
 }
 
+// Wait until at most N vector-memory loads of this wave are outstanding (loads complete in issue
+// order); the other counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // LDS-only workgroup barrier: waits for this wave's LDS traffic, not for its global loads, so the
 // weight prefetch stays in flight across it.
 __device__ __forceinline__ void barrier_lds() {
@@ -239,7 +247,6 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   using S = Shape<BITS, MT, NTW>;
   constexpr int BM = S::BM;
   constexpr int KC = S::KC;
-  constexpr int LDA = S::LDA;
   constexpr int PF = S::PF;
   constexpr int KB = S::KB;
   constexpr int AV = S::AV;
@@ -260,6 +267,16 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // the activation k order in LDS follows the weight decode: permuted for the shift-and-mask
   // decodes (fp16, and bf16 biased codes), natural for the bf16 exact decode and for int8
   constexpr bool PERM_A = BITS == 4 && (DT == 0 || BIASED);
+  // BM >= 64 with natural k order: activation chunks go from memory straight into LDS (buffer loads
+  // with an LDS destination), an unpadded tile whose row-major order is the threads' load order;
+  // no registers or instructions spent staging them
+  constexpr bool DIRECT = !PERM_A && MT >= 4;
+  constexpr int LDA = DIRECT ? KC : S::LDA;
+  // The unpadded tile is swizzled instead: 16-byte chunk j of row r sits at chunk j ^ swz(r), so
+  // the 16 rows of a fragment read (same logical chunk) fall on 16 different bank groups
+  // (64 banks; 16 or 8 chunks per row).  swz(row) depends only on row % 16 = rsub.
+  static_assert(!DIRECT || KC / 8 == 16 || KC / 8 == 8, "swizzle covers 8 or 16 chunks per row");
+  auto swz = [](int r) -> int { return KC / 8 == 16 ? (r & 15) : ((r >> 1) & 7); };
   // uint4 scales and zero points of the workgroup's rows for its whole K range are staged once,
   // before the weight stream starts, into dynamic LDS as meta[kb - kb_beg][row] = scale | zero << 16
   // (the host sizes it: (rows + 2) * k-blocks * 4 bytes).  Consecutive threads read consecutive pairs of
@@ -350,11 +367,27 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
     const int r = idx / VPR;
     const int row = s_row[r];
     arow[i] = row >= 0 ? (uint32_t)row * K * 2 : 0x80000000u;
-    acol[i] = (uint32_t)(idx - r * VPR) * 8;
+    // DIRECT: this thread's LDS slot (r, idx % VPR) holds logical chunk (idx % VPR) ^ swz(r)
+    acol[i] = (uint32_t)(DIRECT ? ((idx - r * VPR) ^ swz(r)) : (idx - r * VPR)) * 8;
   }
   const uint32_t klim = (uint32_t)(kb_end * KB);
   // chunk c travels in areg[c % AQ] (the index is a compile-time constant at every use)
-  u32x4_t areg[AQ][AV];
+  u32x4_t areg[DIRECT ? 1 : AQ][DIRECT ? 1 : AV];
+  // DIRECT: chunk c into LDS buffer buf; lane l of wave w writes the 16 bytes of thread
+  // w * 64 + l + i * kThreads, which in an unpadded tile is that thread's (row, 8-column group)
+  auto dma_a = [&](int c, int buf) {
+    const uint32_t kbase = (uint32_t)((kb_beg + c * KBC) * KB);
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const uint32_t k = kbase + acol[i];
+      const uint32_t off = (arow[i] < 0x80000000u && k < klim) ? arow[i] + k * 2 : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_a,
+          (__attribute__((address_space(3))) void*)((uint8_t*)s_a[buf] +
+                                                    (size_t)(wave * kWave + i * kThreads) * 16),
+          16, off, 0, 0, 0);
+    }
+  };
   auto load_a = [&](int q, int c) {
     const uint32_t kbase = (uint32_t)((kb_beg + c * KBC) * KB);
 #pragma unroll
@@ -477,13 +510,22 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // ---- prologue: chunk 0 in LDS, chunks 1..AQ in flight, PF k-blocks of weights in flight.
   // Prefetch indices past the range are clamped to the last k-block (a redundant, in-bounds load),
   // so the number of loads in flight is the same on every path.
-  load_a(0, 0);
+  if constexpr (DIRECT) {
+    dma_a(0, 0);
 #pragma unroll
-  for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
-  store_a(0, 0);
-  barrier_lds();
+    for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
+    wait_vmcnt<PF * NTW>();  // chunk 0 has landed (only the weight loads behind it may be pending)
+    barrier_lds();
+    dma_a(1, 1);
+  } else {
+    load_a(0, 0);
 #pragma unroll
-  for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
+    for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
+    store_a(0, 0);
+    barrier_lds();
+#pragma unroll
+    for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
+  }
   load_frag(0);
 
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
@@ -502,6 +544,10 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const uint16_t* abase = frag_base(idx);
       auto a_s = [&](int st, int m) -> u32x4_t {
         if constexpr (FRAG_AHEAD) return af[st][m];
+        else if constexpr (DIRECT) {
+          const int cl = jc * (KB / 8) + grp * (KB / 32) + st;  // logical chunk within the row
+          return *(const u32x4_t*)(s_a[c & 1] + (m * 16 + rsub) * LDA + ((cl ^ swz(rsub)) * 8));
+        }
         else return *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
       };
       uint32_t meta[NTW];
@@ -570,8 +616,23 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int t = 0; t < NTW; ++t) dk[t] = make_decode<DT, 4>(meta[t] & 0xFFFFu, meta[t] >> 16);
         }
+        // fragments of step s + 1 are read while step s decodes and multiplies (where the
+        // registers allow: not for fp16 BM 128, whose activation staging needs them)
+        constexpr bool STEP_AHEAD = DIRECT || MT <= 4;
+        u32x4_t acur[MT];
+        if constexpr (STEP_AHEAD) {
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acur[m] = a_s(0, m);
+        }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
+          u32x4_t anext[MT];
+          if constexpr (STEP_AHEAD) {
+            if (st + 1 < STEPS) {
+#pragma unroll
+              for (int m = 0; m < MT; ++m) anext[m] = a_s(st + 1, m);
+            }
+          }
           u32x4_t b[NTW];
 #pragma unroll
           for (int t = 0; t < NTW; ++t) {
@@ -583,21 +644,40 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
 #pragma unroll
           for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int t = 0; t < NTW; ++t) acc[m][t] = Mfma<DT>::run(a_s(st, m), b[t], acc[m][t]);
+            for (int t = 0; t < NTW; ++t)
+              acc[m][t] = Mfma<DT>::run(STEP_AHEAD ? acur[m] : a_s(st, m), b[t], acc[m][t]);
+          if constexpr (STEP_AHEAD) {
+            if (st + 1 < STEPS) {
+#pragma unroll
+              for (int m = 0; m < MT; ++m) acur[m] = anext[m];
+            }
+          }
         }
       }
       load_kb(slot, min(kb + PF, kb_last));
       if (jc == KBC - 1) {
-        // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
-        const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
-        store_a(q, (c + 1) & 1);
-        barrier_lds();
-        load_a(q, c + 1 + AQ);
+        if constexpr (DIRECT) {
+          // end of chunk c: chunk c+1 was requested before this chunk's KBC weight prefetches, so
+          // waiting for all but those leaves it in LDS; then chunk c+2 into the buffer of chunk c
+          wait_vmcnt<KBC * NTW>();
+          barrier_lds();
+          dma_a(c + 2, c & 1);
+        } else {
+          // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
+          const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
+          store_a(q, (c + 1) & 1);
+          barrier_lds();
+          load_a(q, c + 1 + AQ);
+        }
       }
       load_frag(idx + 1);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetches where they are issued
     }
   }
+
+  // LDS-destination loads still in flight (chunks past the range) must land before the workgroup's
+  // LDS can be handed to another workgroup
+  if constexpr (DIRECT) wait_vmcnt<0>();
 
   if constexpr (BIASED && BITS == 8) {
     // remove the +128 bias (fp16: +1152 with the 1024 magic) and apply the per-channel scale
