@@ -226,8 +226,10 @@ template <int BITS, int MT, int NTW>
 struct Shape {
   static constexpr int BM = 16 * MT;
   static constexpr int KB = BITS == 4 ? 128 : 64;            // k per k-block
-  // activation chunk: four 16-byte vectors per thread, at least one k-block
-  static constexpr int KC0 = 4 * 8 * kThreads / BM;
+  // activation chunk: four 16-byte vectors per thread, at least one k-block; two for BLOCK_M 16
+  // with 4 column tiles (256 columns: a short K, as in a tensor-parallel share with I = 256, is
+  // then a whole number of unrolled iterations instead of half of one spent on virtual k-blocks)
+  static constexpr int KC0 = (MT == 1 && NTW == 4 ? 2 : 4) * 8 * kThreads / BM;
   static constexpr int KC = KC0 < KB ? KB : KC0;
   static constexpr int AV = BM * KC / 8 / kThreads;           // 16-byte vectors per thread
   static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
@@ -287,7 +289,6 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
 
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDA];
   __shared__ int s_slot[BM];
-  __shared__ int s_row[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -307,13 +308,11 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   const int e = p.expert_ids[blk];
   if ((unsigned)e >= (unsigned)p.E) return;
 
+  // slot of each block row, for the epilogue (published by the prologue's barrier)
   if (tid < BM) {
     const int s = p.sorted_ids[blk * BM + tid];
-    const bool ok = (unsigned)s < (unsigned)p.num_slots;
-    s_slot[tid] = ok ? s : -1;
-    s_row[tid] = ok ? s / p.a_row_div : -1;
+    s_slot[tid] = (unsigned)s < (unsigned)p.num_slots ? s : -1;
   }
-  __syncthreads();
 
   // K range of this split, in k-blocks (a split past the end has an empty range and writes zeros)
   const int kb_total = K / KB;
@@ -365,7 +364,10 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   for (int i = 0; i < AV; ++i) {
     const int idx = tid + i * kThreads;
     const int r = idx / VPR;
-    const int row = s_row[r];
+    // each thread reads the slot ids it needs itself: the activation loads then leave without
+    // waiting for a workgroup barrier, under the same memory latency as weights and scales
+    const int sl = p.sorted_ids[blk * BM + r];
+    const int row = (unsigned)sl < (unsigned)p.num_slots ? (p.a_row_div == 1 ? sl : sl / p.a_row_div) : -1;
     arow[i] = row >= 0 ? (uint32_t)row * K * 2 : 0x80000000u;
     // DIRECT: this thread's LDS slot (r, idx % VPR) holds logical chunk (idx % VPR) ^ swz(r)
     acol[i] = (uint32_t)(DIRECT ? ((idx - r * VPR) ^ swz(r)) : (idx - r * VPR)) * 8;
@@ -424,26 +426,6 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       *(u32x4_t*)&s_a[buf][r * LDA + c8 * 8] = v;
     }
   };
-
-  // ---- uint4 metadata for the whole K range of this split, fetched in even-aligned pairs of
-  // k-blocks (one 4-byte load holds two scales, one byte two zero points); a pair straddling either
-  // end of the range writes only its in-range half
-  if constexpr (BITS == 4) {
-    const int kb0 = kb_beg & ~1;
-    const int npair = (kb_end - kb0 + 1) >> 1;
-    for (int item = tid; item < R * npair; item += kThreads) {
-      const int lr = item / npair;
-      const int j = item - lr * npair;
-      const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
-      const int kb = kb0 + 2 * j;
-      const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs_s, n * srow_bytes + kb * 2, 0, 0);
-      const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rs_z, n * zrow_bytes + (kb >> 1), 0, 0);
-      if (kb >= kb_beg) s_meta[(kb - kb_beg) * RP + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
-      if (kb + 1 < kb_end)
-        s_meta[(kb + 1 - kb_beg) * RP + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
-    }
-    __syncthreads();
-  }
 
   // ---- weight stream: PF k-blocks in flight, 16 bytes per lane per tile
   u32x4_t wq[PF][NTW];
@@ -510,19 +492,39 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // ---- prologue: chunk 0 in LDS, chunks 1..AQ in flight, PF k-blocks of weights in flight.
   // Prefetch indices past the range are clamped to the last k-block (a redundant, in-bounds load),
   // so the number of loads in flight is the same on every path.
-  if constexpr (DIRECT) {
-    dma_a(0, 0);
+  // The first weight k-blocks, then the first activation chunk (whose addresses wait on the slot
+  // ids), are requested before the scales are staged, so one memory latency covers them all (the
+  // staging waits for its own loads, issued last).
 #pragma unroll
-    for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
-    wait_vmcnt<PF * NTW>();  // chunk 0 has landed (only the weight loads behind it may be pending)
-    barrier_lds();
+  for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
+  if constexpr (DIRECT) dma_a(0, 0);
+  else load_a(0, 0);
+
+  // ---- uint4 metadata for the whole K range of this split, fetched in even-aligned pairs of
+  // k-blocks (one 4-byte load holds two scales, one byte two zero points); a pair straddling either
+  // end of the range writes only its in-range half
+  if constexpr (BITS == 4) {
+    const int kb0 = kb_beg & ~1;
+    const int npair = (kb_end - kb0 + 1) >> 1;
+    for (int item = tid; item < R * npair; item += kThreads) {
+      const int lr = item / npair;
+      const int j = item - lr * npair;
+      const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
+      const int kb = kb0 + 2 * j;
+      const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs_s, n * srow_bytes + kb * 2, 0, 0);
+      const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rs_z, n * zrow_bytes + (kb >> 1), 0, 0);
+      if (kb >= kb_beg) s_meta[(kb - kb_beg) * RP + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
+      if (kb + 1 < kb_end)
+        s_meta[(kb + 1 - kb_beg) * RP + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
+    }
+  }
+
+  if constexpr (DIRECT) wait_vmcnt<0>();  // chunk 0 has landed (behind the first weights)
+  else store_a(0, 0);
+  barrier_lds();  // publishes the staged scales and chunk 0
+  if constexpr (DIRECT) {
     dma_a(1, 1);
   } else {
-    load_a(0, 0);
-#pragma unroll
-    for (int u = 0; u < PF; ++u) load_kb(u, min(kb_beg + u, kb_last));
-    store_a(0, 0);
-    barrier_lds();
 #pragma unroll
     for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
   }
