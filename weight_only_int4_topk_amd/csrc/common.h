@@ -50,39 +50,57 @@ __device__ __forceinline__ void argbest_step(float& v, int& i) {
   }
 }
 
-// Wave-wide arg-best over (value, index) pairs; every lane returns the winner (wave-uniform).
-// Rows of 16 lanes reduce with DPP, the four row winners are compared in scalar registers.
+// Exchange between 16-lane rows (r0<->r1, r2<->r3) and between the 32-lane halves, gfx950
+// v_permlane16_swap / v_permlane32_swap: with both operands = x, the two results hold x of both
+// rows (halves) of the lane's pair, in every lane.
+template <bool HALVES>
+__device__ __forceinline__ void swap_pair(uint32_t x, uint32_t& a, uint32_t& b) {
+  if constexpr (HALVES) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+
+template <bool HALVES>
+__device__ __forceinline__ void argbest_swap(float& v, int& i) {
+  uint32_t va, vb, ia, ib;
+  swap_pair<HALVES>(__float_as_uint(v), va, vb);
+  swap_pair<HALVES>((uint32_t)i, ia, ib);
+  const float fa = __uint_as_float(va), fb = __uint_as_float(vb);
+  const bool a_wins = better(fa, (int)ia, fb, (int)ib);
+  v = a_wins ? fa : fb;
+  i = a_wins ? (int)ia : (int)ib;
+}
+
+// Wave-wide arg-best over (value, index) pairs; every lane returns the winner.  Rows of 16 lanes
+// reduce with DPP, then rows pair up and halves pair up through lane swaps, all in vector
+// registers (the order is total, so the result does not depend on the reduction order).
 __device__ __forceinline__ void wave_argbest(float& v, int& i) {
   argbest_step<kDppXor1>(v, i);
   argbest_step<kDppXor2>(v, i);
   argbest_step<kDppHalfMirror>(v, i);
   argbest_step<kDppMirror>(v, i);
-  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 16; r < kWave; r += 16) {
-    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r));
-    const int ri = __builtin_amdgcn_readlane(i, r);
-    if (better(rv, ri, bv, bi)) {
-      bv = rv;
-      bi = ri;
-    }
-  }
-  v = bv;
-  i = bi;
+  argbest_swap<false>(v, i);
+  argbest_swap<true>(v, i);
 }
 
-// Wave-wide sum in a fixed order (rows by DPP, then rows 0 + 1 + 2 + 3); every lane returns it.
+// Wave-wide sum in a fixed order (rows by DPP, then (row0 + row1) + (row2 + row3)); every lane
+// returns the same value.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<kDppXor1>(v);
   v += dpp_f<kDppXor2>(v);
   v += dpp_f<kDppHalfMirror>(v);
   v += dpp_f<kDppMirror>(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return ((r0 + r1) + r2) + r3;
+  uint32_t a, b;
+  swap_pair<false>(__float_as_uint(v), a, b);
+  v = __uint_as_float(a) + __uint_as_float(b);
+  swap_pair<true>(__float_as_uint(v), a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }

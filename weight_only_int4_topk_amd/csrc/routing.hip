@@ -44,6 +44,17 @@ __device__ float sigmoid_spec(float x) {
   return 1.0f / (1.0f + e);  // correctly rounded division (HIP default)
 }
 
+// Merge (t1 >= t2) with the partner lane's pair into the two largest of the four values.
+__device__ __forceinline__ void top2_merge(float& t1, float& t2, float o1, float o2) {
+  const float n2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+  t1 = fmaxf(t1, o1);
+  t2 = n2;
+}
+template <int CTRL>
+__device__ __forceinline__ void top2_step(float& t1, float& t2) {
+  top2_merge(t1, t2, dpp_f<CTRL>(t1), dpp_f<CTRL>(t2));
+}
+
 template <int EPL>
 __global__ void __launch_bounds__(256) routing_kernel(const float* __restrict__ logits, int M, int E,
                                                       int topk, RoutingParams p,
@@ -121,7 +132,39 @@ __global__ void __launch_bounds__(256) routing_kernel(const float* __restrict__ 
   const int ng = p.num_groups;
   const int gs = E / ng;
   uint64_t kept = ~0ull;
-  if (p.topk_groups < ng) {
+  if (EPL == 4 && E == 256 && ng == 8 && p.topk_groups < ng) {
+    // 8 groups of 32 (the DeepSeek-V3 layout): group 2i + h holds the experts of v[i] in half h
+    // of the wave, so a butterfly inside each half (DPP in rows, a row swap across them) leaves
+    // every lane with the two largest scores of its half's four groups; one half swap then gives
+    // every lane all eight group scores, which it ranks by itself (ties -> lower group id).
+    float gsc[8];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float t1 = v[i], t2 = kNone;
+      top2_step<kDppXor1>(t1, t2);
+      top2_step<kDppXor2>(t1, t2);
+      top2_step<kDppHalfMirror>(t1, t2);
+      top2_step<kDppMirror>(t1, t2);
+      uint32_t a1, b1, a2, b2;
+      swap_pair<false>(__float_as_uint(t1), a1, b1);
+      swap_pair<false>(__float_as_uint(t2), a2, b2);
+      t1 = __uint_as_float(a1);
+      t2 = __uint_as_float(a2);
+      top2_merge(t1, t2, __uint_as_float(b1), __uint_as_float(b2));
+      uint32_t lo, hi;
+      swap_pair<true>(__float_as_uint(t1 + t2), lo, hi);
+      gsc[2 * i] = __uint_as_float(lo);
+      gsc[2 * i + 1] = __uint_as_float(hi);
+    }
+    kept = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      int rank = 0;
+#pragma unroll
+      for (int o = 0; o < 8; ++o) rank += (o != g && better(gsc[o], o, gsc[g], g)) ? 1 : 0;
+      if (rank < p.topk_groups) kept |= 1ull << g;
+    }
+  } else if (p.topk_groups < ng) {
     // publish scores to LDS; lane g < ng scores group g by the sum of its two largest values
     float* sc = s_score[wid];
 #pragma unroll
