@@ -367,10 +367,17 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
 
   const moe::RoutingParams rp{routing->score, routing->renormalize, routing->num_groups,
                               routing->topk_groups, routing->scale};
-  hipError_t e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
-  if (e != hipSuccess) return hip_fail(e, "routing launch");
-  e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
-  if (e != hipSuccess) return hip_fail(e, "align launch");
+  hipError_t e;
+  if (moe::route_align_fits(M, E)) {
+    e = moe::launch_route_align(router_logits, M, E, topk, rp, tw, ids, pl.bm, sorted, eids, npost,
+                                pl.cap, st);
+    if (e != hipSuccess) return hip_fail(e, "routing + align launch");
+  } else {
+    e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
+    if (e != hipSuccess) return hip_fail(e, "routing launch");
+    e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
+    if (e != hipSuccess) return hip_fail(e, "align launch");
+  }
 
   moe::GemmParams g1{};
   g1.A = x;

@@ -18,6 +18,12 @@ struct RoutingParams {
 hipError_t launch_routing(const float* logits, int M, int E, int topk, const RoutingParams& p,
                           float* topk_w, int32_t* topk_ids, hipStream_t stream);
 
+// Routing and align in one launch for small batches (route_align_fits(M, E): M <= 4, E <= 256).
+bool route_align_fits(int M, int E);
+hipError_t launch_route_align(const float* logits, int M, int E, int topk, const RoutingParams& p,
+                              float* topk_w, int32_t* topk_ids, int block_m, int32_t* sorted_ids,
+                              int32_t* expert_ids, int32_t* num_post, int64_t capacity,
+                              hipStream_t stream);
 hipError_t launch_align(const int32_t* topk_ids, int numel, int E, int block_m,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post,
                         int64_t capacity, hipStream_t stream);
