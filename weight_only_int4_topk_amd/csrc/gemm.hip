@@ -234,7 +234,10 @@ struct Shape {
   static constexpr int AV = BM * KC / 8 / kThreads;           // 16-byte vectors per thread
   static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
   static constexpr int KBC = KC / KB;                         // k-blocks per chunk
-  static constexpr int PF = MT <= 2 ? (NTW == 2 ? 4 : 2) : (NTW == 2 ? 2 : 1);
+  // weight k-blocks in flight per wavefront.  BM 32 keeps 2, not 4: that brings its kernel under
+  // 168 registers, three wavefronts per SIMD instead of two, which streams faster (measured on the
+  // Mixtral-shaped w13 at M = 64: 141 -> 127 us)
+  static constexpr int PF = MT == 1 ? (NTW == 2 ? 4 : 2) : MT == 2 ? 2 : (NTW == 2 ? 2 : 1);
   // activation chunks in flight in registers: a chunk's loads must be issued at least PF k-blocks
   // before it is stored to LDS, or the wait for it (memory counters complete in issue order) also
   // waits for the newest weight prefetches and shortens the weight pipeline at every chunk edge
@@ -462,10 +465,11 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   }
 
   // ---- activation fragments and metadata of one k-block, read from LDS one k-block ahead of
-  // their use, so LDS latency is off the MFMA chain (fragments only for BM <= 32, where they
-  // fit in registers).  Fragment of step s, row tile m: 16 bytes of row m * 16 + rsub at k
-  // offset grp * (KB / 4) + s * 8 of the k-block.
-  constexpr bool FRAG_AHEAD = MT <= 2;
+  // their use, so LDS latency is off the MFMA chain (fragments only for BM 16; at BM 32 the
+  // 32 registers they take would cost a wavefront per SIMD, which hides more than they do).
+  // Fragment of step s, row tile m: 16 bytes of row m * 16 + rsub at k offset
+  // grp * (KB / 4) + s * 8 of the k-block.
+  constexpr bool FRAG_AHEAD = MT == 1;
   constexpr int FS = FRAG_AHEAD ? STEPS : 1;
   constexpr int FM = FRAG_AHEAD ? MT : 1;
   u32x4_t af[FS][FM];
@@ -745,7 +749,7 @@ hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stre
 
 template <int DT, int BITS, int MT>
 hipError_t launch_mt(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
-  if (MT <= 2 && c.ntw == 4) return launch_ntw<DT, BITS, MT, (MT <= 2 ? 4 : 2)>(p, c, stream);
+  if (MT == 1 && c.ntw == 4) return launch_ntw<DT, BITS, MT, (MT == 1 ? 4 : 2)>(p, c, stream);
   return launch_ntw<DT, BITS, MT, 2>(p, c, stream);
 }
 
@@ -764,7 +768,7 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 
 size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c) {
   if (c.bits != 4) return 0;
-  const int ntw = (c.ntw == 4 && c.block_m <= 32) ? 4 : 2;
+  const int ntw = (c.ntw == 4 && c.block_m == 16) ? 4 : 2;
   const int kb_total = K / 128;
   const int kb_per = (kb_total + split_k - 1) / split_k;
   return (size_t)(kWaves * ntw * 16 + 2) * kb_per * 4;  // row pitch R + 2 dwords
@@ -789,7 +793,7 @@ size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c) {
 }
 
 int gemm_wg_cols(const GemmConfig& c) {
-  const int ntw = (c.ntw == 4 && c.block_m <= 32) ? 4 : 2;
+  const int ntw = (c.ntw == 4 && c.block_m == 16) ? 4 : 2;
   return kWaves * (c.act ? ntw / 2 : ntw) * 16;
 }
 

@@ -56,7 +56,7 @@ struct GemmConfig {
   int block_m;   // 16, 32, 64, 128
   int act;       // 0 none, 1 silu-mul
   int out_f32;   // 1: float partials [split, num_slots, N]
-  int ntw;       // column tiles of 16 per wavefront: 2, or 4 (block_m <= 32 only)
+  int ntw;       // column tiles of 16 per wavefront: 2, or 4 (block_m 16 only)
 };
 
 // Columns of output one workgroup covers (N % this must be 0; act: gate columns).
