@@ -125,7 +125,7 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
  * Limits: K % 256 == 0, N % 128 == 0, block_m in
  * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots.  uint4: a workgroup stages the scales
  * and zero points of its whole K range in LDS beside its activation tiles (160 KiB in all), which
- * allows K up to 32,000 at block_m 16 and 22,784 at block_m 128; longer K returns
+ * allows K up to 36,096 at block_m 16 and 22,784 at block_m 128; longer K returns
  * MOE_ERR_UNSUPPORTED before any launch. */
 int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, const void* scales,
                    const void* zeros, const moe_quant_t* quant, int E, int N, int K, int dtype,

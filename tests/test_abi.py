@@ -124,7 +124,7 @@ def test_gemm_validation(lib):
     assert _gemm(lib, Bw=NULL) == INVALID
     assert _gemm(lib, slots=0) == OK                           # nothing to do, no launch
     # uint4 scales of the whole K range must fit in LDS beside the activation tiles
-    assert _gemm(lib, K=32000 + 256, bm=16) == UNSUPPORTED
+    assert _gemm(lib, K=36096 + 256, bm=16) == UNSUPPORTED
     assert b"LDS" in lib.moe_last_error()
     assert _gemm(lib, K=22784 + 256, bm=128, rows=64, slots=32) == UNSUPPORTED
 

@@ -227,17 +227,19 @@ struct Shape {
   static constexpr int BM = 16 * MT;
   static constexpr int KB = BITS == 4 ? 128 : 64;            // k per k-block
   // activation chunk: four 16-byte vectors per thread, at least one k-block; two for BLOCK_M 16
-  // with 4 column tiles (256 columns: a short K, as in a tensor-parallel share with I = 256, is
-  // then a whole number of unrolled iterations instead of half of one spent on virtual k-blocks)
-  static constexpr int KC0 = (MT == 1 && NTW == 4 ? 2 : 4) * 8 * kThreads / BM;
+  // (256 columns: a short K, as in a tensor-parallel share with I = 256, is then a whole number of
+  // unrolled iterations instead of half of one spent on virtual k-blocks, and the smaller tile
+  // leaves LDS for more workgroups per compute unit)
+  static constexpr int KC0 = (MT == 1 ? 2 : 4) * 8 * kThreads / BM;
   static constexpr int KC = KC0 < KB ? KB : KC0;
   static constexpr int AV = BM * KC / 8 / kThreads;           // 16-byte vectors per thread
   static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
   static constexpr int KBC = KC / KB;                         // k-blocks per chunk
-  // weight k-blocks in flight per wavefront.  BM 32 keeps 2, not 4: that brings its kernel under
-  // 168 registers, three wavefronts per SIMD instead of two, which streams faster (measured on the
-  // Mixtral-shaped w13 at M = 64: 141 -> 127 us)
-  static constexpr int PF = MT == 1 ? (NTW == 2 ? 4 : 2) : MT == 2 ? 2 : (NTW == 2 ? 2 : 1);
+  // weight k-blocks in flight per wavefront.  The decode kernels keep 2, not 4: fewer registers
+  // per wavefront and more wavefronts per SIMD stream faster than a deeper prefetch (measured on
+  // the Mixtral-shaped w13 at M = 64, BM 32: 217 -> 140 registers, two wavefronts per SIMD ->
+  // three, 141 -> 127 us)
+  static constexpr int PF = MT <= 2 ? 2 : (NTW == 2 ? 2 : 1);
   // activation chunks in flight in registers: a chunk's loads must be issued at least PF k-blocks
   // before it is stored to LDS, or the wait for it (memory counters complete in issue order) also
   // waits for the newest weight prefetches and shortens the weight pipeline at every chunk edge
@@ -464,28 +466,16 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           __builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)(col[t] + rsub) * 2, 0, 0), 0);
   }
 
-  // ---- activation fragments and metadata of one k-block, read from LDS one k-block ahead of
-  // their use, so LDS latency is off the MFMA chain (fragments only for BM 16; at BM 32 the
-  // 32 registers they take would cost a wavefront per SIMD, which hides more than they do).
-  // Fragment of step s, row tile m: 16 bytes of row m * 16 + rsub at k offset
-  // grp * (KB / 4) + s * 8 of the k-block.
-  constexpr bool FRAG_AHEAD = MT == 1;
-  constexpr int FS = FRAG_AHEAD ? STEPS : 1;
-  constexpr int FM = FRAG_AHEAD ? MT : 1;
-  u32x4_t af[FS][FM];
+  // ---- metadata of one k-block, read from LDS one k-block ahead of its use.  Activation
+  // fragments are read where they are used (step s, row tile m: 16 bytes of row m * 16 + rsub at
+  // k offset grp * (KB / 4) + s * 8 of the k-block): holding a k-block of them ahead would take
+  // 4 * MT * 4 registers, and a wavefront per SIMD more hides their latency better (measured).
   uint32_t mf[NTW];
   auto frag_base = [&](int idx) -> const uint16_t* {  // idx = k-block index relative to kb_beg
     const int c = idx / KBC;
     return s_a[c & 1] + rsub * LDA + (idx - c * KBC) * KB + grp * (KB / 4);
   };
-  auto load_frag = [&](int idx) {
-    if constexpr (FRAG_AHEAD) {
-      const uint16_t* abase = frag_base(idx);
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) af[st][m] = *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
-    }
+  auto load_meta = [&](int idx) {
     if constexpr (BITS == 4) {
       const int mrow = min(kb_beg + idx, kb_last) - kb_beg;
 #pragma unroll
@@ -532,7 +522,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
   }
-  load_frag(0);
+  load_meta(0);
 
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
   // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
@@ -546,11 +536,10 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const int slot = j % PF;
       const int jc = j % KBC;
       const int c = idx / KBC;
-      // this k-block's fragments (read during the previous one, or here for BM >= 64)
+      // this k-block's activation fragments
       const uint16_t* abase = frag_base(idx);
       auto a_s = [&](int st, int m) -> u32x4_t {
-        if constexpr (FRAG_AHEAD) return af[st][m];
-        else if constexpr (DIRECT) {
+        if constexpr (DIRECT) {
           const int cl = jc * (KB / 8) + grp * (KB / 32) + st;  // logical chunk within the row
           return *(const u32x4_t*)(s_a[c & 1] + (m * 16 + rsub) * LDA + ((cl ^ swz(rsub)) * 8));
         }
@@ -676,7 +665,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           load_a(q, c + 1 + AQ);
         }
       }
-      load_frag(idx + 1);
+      load_meta(idx + 1);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetches where they are issued
     }
   }
