@@ -133,11 +133,13 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
                    const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
                    int num_slots, const float* topk_weights, int act, void* C, void* stream);
 
-/* The block_m fused_moe_wna16 uses when called with block_m = 0: the smallest of {16, 32, 64, 128}
- * that holds 1.5x the average number of slots per active expert (min(E, M*topk) experts), so a
- * typical expert's slots share one block and its weights are streamed once.  Returns -1 for
- * non-positive sizes. */
-int moe_pick_block_m(int M, int E, int topk);
+/* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
+ * bits: the smallest of {16, 32, 64, 128} that holds 1.5x the average number of slots per active
+ * expert (min(E, M*topk) experts), so a typical expert's slots share one block and its weights
+ * are streamed once; uint4 stops at 64 (a 128-row block leaves too little LDS for a second
+ * workgroup per compute unit beside its staged scales).  Returns -1 for non-positive sizes or
+ * other bit widths. */
+int moe_pick_block_m(int M, int E, int topk, int bits);
 
 /* Workspace bytes fused_moe_wna16 needs for these sizes (block_m 0 = library's choice). */
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, const moe_quant_t* quant,

@@ -68,11 +68,14 @@ def test_routing_validation(lib):
 
 
 def test_pick_block_m(lib):
-    assert lib.moe_pick_block_m(16, 8, 2) == 16       # 4 slots per expert
-    assert lib.moe_pick_block_m(64, 8, 2) == 32       # 16 per expert -> 24 needed
-    assert lib.moe_pick_block_m(1024, 256, 8) == 64
-    assert lib.moe_pick_block_m(4096, 256, 8) == 128
-    assert lib.moe_pick_block_m(0, 8, 2) == -1
+    assert lib.moe_pick_block_m(16, 8, 2, 4) == 16       # 4 slots per expert
+    assert lib.moe_pick_block_m(64, 8, 2, 4) == 32       # 16 per expert -> 24 needed
+    assert lib.moe_pick_block_m(1024, 256, 8, 4) == 64
+    assert lib.moe_pick_block_m(4096, 256, 8, 4) == 64   # uint4 stops at 64
+    assert lib.moe_pick_block_m(4096, 256, 8, 8) == 128
+    assert lib.moe_pick_block_m(1024, 256, 8, 8) == 64
+    assert lib.moe_pick_block_m(0, 8, 2, 4) == -1
+    assert lib.moe_pick_block_m(16, 8, 2, 3) == -1
 
 
 def test_align_capacity_formula(lib):
