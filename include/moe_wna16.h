@@ -123,10 +123,11 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
  *     with the same block_m; capacity = length of sorted_token_ids.
  * Rows of C whose slot is not listed are not written.
  * Limits: K % 256 == 0, N % 128 == 0, block_m in
- * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots.  uint4: a workgroup stages the scales
- * and zero points of its whole K range in LDS beside its activation tiles (160 KiB in all), which
- * allows K up to 36,096 at block_m 16 and 22,784 at block_m 128; longer K returns
- * MOE_ERR_UNSUPPORTED before any launch. */
+ * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots.  uint4 at block_m 16 and 32: a
+ * workgroup stages the scales and zero points of its whole K range in LDS beside its activation
+ * tiles (160 KiB in all), which allows K up to 36,096 at block_m 16 and 31,744 at block_m 32;
+ * longer K returns MOE_ERR_UNSUPPORTED before any launch (block_m 64 and 128 hold two k-blocks of
+ * them at a time and have no such limit). */
 int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, const void* scales,
                    const void* zeros, const moe_quant_t* quant, int E, int N, int K, int dtype,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,

@@ -99,10 +99,9 @@ struct Plan {
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
 };
 
-// uint4 stops at 64: a 128-row workgroup stages its scales and zero points for the whole K range
-// beside 64 KiB of activation tiles, which leaves one workgroup per compute unit, and two 64-row
-// blocks stream faster (measured: Qwen2-shaped layer at M = 512, GEMMs 798 -> 497 us; DeepSeek-V3
-// expert at M = 4096, w13 5039 -> 3664 us).  int8 has no per-group metadata and keeps 128.
+// uint4 stops at 64: the fp16 128-row kernel stages activations through registers and runs at two
+// wavefronts per SIMD (Qwen2-shaped layer at M = 512: GEMMs 798 us at 128 rows, 497 us at 64); in
+// bf16 the two are within a few percent (DeepSeek-V3 expert at M = 4096).  int8 keeps 128.
 int pick_block_m(int M, int topk, int E, int bits) {
   const int64_t slots = (int64_t)M * topk;
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, slots));

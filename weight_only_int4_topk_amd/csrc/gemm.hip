@@ -246,7 +246,9 @@ struct Shape {
   static constexpr int AQ0 = (PF + KBC - 1) / KBC;
   static constexpr int AQ = (MT >= 8 && AQ0 > 1) ? 1 : AQ0;   // BM 128: registers are the limit
   static constexpr int UA = KBC * AQ;
-  static constexpr int U = UA / gcd_c(UA, PF) * PF;           // unroll: lcm(KBC * AQ, PF)
+  static constexpr int U0 = UA / gcd_c(UA, PF) * PF;          // lcm(KBC * AQ, PF)
+  // unroll; BM >= 64 also a multiple of 2 * KBC (each activation buffer once per iteration)
+  static constexpr int U = MT >= 4 ? U0 / gcd_c(U0, 2 * KBC) * (2 * KBC) : U0;
 };
 
 template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32>
@@ -268,6 +270,12 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // metadata row pitch in dwords: consecutive staging threads write entries 2 * RP apart, and
   // RP = 2 (mod 32) spreads them over the LDS banks
   constexpr int RP = R + 2;
+  // BM >= 64 (one k-block per activation chunk, a workgroup barrier after every k-block): the
+  // uint4 metadata goes through a two-slot LDS ring refilled at each barrier from loads issued two
+  // k-blocks ahead, instead of the whole K range staged up front.  Its 1 KiB instead of up to
+  // 29 KiB (K = 7168) lets 64-row workgroups share a compute unit four at a time.
+  constexpr bool RING = BITS == 4 && MT >= 4;
+  static_assert(!RING || (S::KBC == 1 && S::U % 2 == 0), "ring: one k-block per chunk, even unroll");
   // decode regime: biased codes with MFMA-side bias removal (fewer VALU ops per weight); prefill:
   // exact decoded weights, no extra MFMAs (the matrix cores are the bottleneck there)
   constexpr bool BIASED = MT <= 2;
@@ -284,15 +292,24 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // (64 banks; 16 or 8 chunks per row).  swz(row) depends only on row % 16 = rsub.
   static_assert(!DIRECT || KC / 8 == 16 || KC / 8 == 8, "swizzle covers 8 or 16 chunks per row");
   auto swz = [](int r) -> int { return KC / 8 == 16 ? (r & 15) : ((r >> 1) & 7); };
-  // uint4 scales and zero points of the workgroup's rows for its whole K range are staged once,
-  // before the weight stream starts, into dynamic LDS as meta[kb - kb_beg][row] = scale | zero << 16
-  // (the host sizes it: (rows + 2) * k-blocks * 4 bytes).  Consecutive threads read consecutive pairs of
-  // k-blocks of one row, so each cache line of scales is touched once.  Per-lane loads of a 2-byte
-  // scale and a 1-byte zero point every k-block would triple the memory instructions of the weight
-  // stream and cap it near 3.2 TB/s.
+  // uint4 scales and zero points of the workgroup's rows, in dynamic LDS as
+  // meta[slot][row] = scale | zero << 16.  BM <= 32: the whole K range, staged once before the
+  // weight stream starts (slot = kb - kb_beg; the host sizes it (rows + 2) * k-blocks * 4 bytes);
+  // consecutive threads read consecutive pairs of k-blocks of one row, so each cache line of scales
+  // is touched once.  Per-lane loads of a 2-byte scale and a 1-byte zero point every k-block would
+  // triple the memory instructions of the weight stream and cap it near 3.2 TB/s.  BM >= 64: a
+  // two-slot ring (slot = k-block & 1), one load pair per row and k-block spread over the threads.
   extern __shared__ uint32_t s_meta[];
 
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDA];
+  // The two activation buffers are separate LDS variables: with one array the compiler cannot
+  // tell that an LDS-destination load into one buffer leaves the other alone, and waits for every
+  // outstanding load (weight prefetch included) before reading fragments after it.
+  __shared__ __attribute__((aligned(16))) uint16_t s_a0[BM * LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a1[BM * LDA];
+  auto abuf = [&](int b) -> uint16_t* { return b ? s_a1 : s_a0; };
+  // DIRECT: in the unrolled loop the buffer of every chunk is a compile-time constant (an even
+  // number of chunks per unrolled iteration), so each access names its variable
+  static_assert(!DIRECT || (U / KBC) % 2 == 0, "even number of chunks per unrolled iteration");
   __shared__ int s_slot[BM];
 
   const int tid = threadIdx.x;
@@ -390,7 +407,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const uint32_t off = (arow[i] < 0x80000000u && k < klim) ? arow[i] + k * 2 : 0x80000000u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs_a,
-          (__attribute__((address_space(3))) void*)((uint8_t*)s_a[buf] +
+          (__attribute__((address_space(3))) void*)((uint8_t*)abuf(buf) +
                                                     (size_t)(wave * kWave + i * kThreads) * 16),
           16, off, 0, 0, 0);
     }
@@ -428,7 +445,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           v[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, w3) * sixteenth);
         }
       }
-      *(u32x4_t*)&s_a[buf][r * LDA + c8 * 8] = v;
+      *(u32x4_t*)&abuf(buf)[r * LDA + c8 * 8] = v;
     }
   };
 
@@ -471,16 +488,33 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // k offset grp * (KB / 4) + s * 8 of the k-block): holding a k-block of them ahead would take
   // 4 * MT * 4 registers, and a wavefront per SIMD more hides their latency better (measured).
   uint32_t mf[NTW];
-  auto frag_base = [&](int idx) -> const uint16_t* {  // idx = k-block index relative to kb_beg
-    const int c = idx / KBC;
-    return s_a[c & 1] + rsub * LDA + (idx - c * KBC) * KB + grp * (KB / 4);
+  // jc = k-block within its chunk, b = buffer of the chunk
+  auto frag_base = [&](int jc, int b) -> const uint16_t* {
+    return abuf(b) + rsub * LDA + jc * KB + grp * (KB / 4);
   };
   auto load_meta = [&](int idx) {
     if constexpr (BITS == 4) {
-      const int mrow = min(kb_beg + idx, kb_last) - kb_beg;
+      const int mrow = RING ? (idx & 1) : min(kb_beg + idx, kb_last) - kb_beg;
 #pragma unroll
       for (int t = 0; t < NTW; ++t) mf[t] = s_meta[mrow * RP + (wave * NTW + t) * 16 + rsub];
     }
+  };
+  // RING: thread tid fetches the scale and zero-point byte of workgroup row tid % R for one k-block
+  // (every thread loads, so no load is conditional; threads below R store), in register set X % 2
+  // for k-block X (relative to kb_beg; past the range, the last real k-block)
+  const uint32_t m_lr = (uint32_t)(tid % R);
+  const uint32_t m_n = (uint32_t)(col_of(m_lr / (NTW * 16), (m_lr / 16) % NTW) + (m_lr % 16));
+  uint32_t m_sc[2], m_zb[2];
+  auto ring_load = [&](int set, int X) {
+    const int kb = min(kb_beg + X, kb_last);
+    m_sc[set] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, m_n * srow_bytes + kb * 2, 0, 0);
+    m_zb[set] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, m_n * zrow_bytes + (kb >> 1), 0, 0);
+  };
+  auto ring_store = [&](int set, int X) {
+    const int kb = min(kb_beg + X, kb_last);
+    if (tid < R)
+      s_meta[(X & 1) * RP + m_lr] =
+          (m_sc[set] & 0xFFFFu) | (((m_zb[set] >> ((kb & 1) * 4)) & 0xFu) << 16);
   };
 
   // ---- prologue: chunk 0 in LDS, chunks 1..AQ in flight, PF k-blocks of weights in flight.
@@ -494,10 +528,16 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   if constexpr (DIRECT) dma_a(0, 0);
   else load_a(0, 0);
 
-  // ---- uint4 metadata for the whole K range of this split, fetched in even-aligned pairs of
-  // k-blocks (one 4-byte load holds two scales, one byte two zero points); a pair straddling either
-  // end of the range writes only its in-range half
-  if constexpr (BITS == 4) {
+  // ---- uint4 metadata.  BM <= 32: the whole K range of this split, fetched in even-aligned pairs
+  // of k-blocks (one 4-byte load holds two scales, one byte two zero points); a pair straddling
+  // either end of the range writes only its in-range half.  BM >= 64: the ring's first k-blocks.
+  if constexpr (RING) {
+    // k-block 0 into slot 0 now; k-blocks 1 and 2 in flight
+    ring_load(0, 0);
+    ring_load(1, 1);
+    ring_store(0, 0);
+    ring_load(0, 2);
+  } else if constexpr (BITS == 4) {
     const int kb0 = kb_beg & ~1;
     const int npair = (kb_end - kb0 + 1) >> 1;
     for (int item = tid; item < R * npair; item += kThreads) {
@@ -536,12 +576,14 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       const int slot = j % PF;
       const int jc = j % KBC;
       const int c = idx / KBC;
+      // buffer of chunk c: a constant where U / KBC is even (always for DIRECT)
+      const int cb = (U / KBC) % 2 == 0 ? (j / KBC) & 1 : c & 1;
       // this k-block's activation fragments
-      const uint16_t* abase = frag_base(idx);
+      const uint16_t* abase = frag_base(jc, cb);
       auto a_s = [&](int st, int m) -> u32x4_t {
         if constexpr (DIRECT) {
           const int cl = jc * (KB / 8) + grp * (KB / 32) + st;  // logical chunk within the row
-          return *(const u32x4_t*)(s_a[c & 1] + (m * 16 + rsub) * LDA + ((cl ^ swz(rsub)) * 8));
+          return *(const u32x4_t*)(abuf(cb) + (m * 16 + rsub) * LDA + ((cl ^ swz(rsub)) * 8));
         }
         else return *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
       };
@@ -655,13 +697,17 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
           // end of chunk c: chunk c+1 was requested before this chunk's KBC weight prefetches, so
           // waiting for all but those leaves it in LDS; then chunk c+2 into the buffer of chunk c
           wait_vmcnt<KBC * NTW>();
+          if constexpr (RING) ring_store((j + 1) & 1, idx + 1);
           barrier_lds();
-          dma_a(c + 2, c & 1);
+          if constexpr (RING) ring_load((j + 1) & 1, idx + 3);
+          dma_a(c + 2, cb);
         } else {
           // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
           const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
-          store_a(q, (c + 1) & 1);
+          store_a(q, cb ^ 1);
+          if constexpr (RING) ring_store((j + 1) & 1, idx + 1);
           barrier_lds();
+          if constexpr (RING) ring_load((j + 1) & 1, idx + 3);
           load_a(q, c + 1 + AQ);
         }
       }
@@ -758,6 +804,7 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c) {
   if (c.bits != 4) return 0;
   const int ntw = (c.ntw == 4 && c.block_m == 16) ? 4 : 2;
+  if (c.block_m >= 64) return (size_t)(kWaves * ntw * 16 + 2) * 2 * 4;  // two-slot ring
   const int kb_total = K / 128;
   const int kb_per = (kb_total + split_k - 1) / split_k;
   return (size_t)(kWaves * ntw * 16 + 2) * kb_per * 4;  // row pitch R + 2 dwords
