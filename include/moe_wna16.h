@@ -125,7 +125,7 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
  * Limits: K % 256 == 0, N % 128 == 0, block_m in
  * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots.  uint4 at block_m 16 and 32: a
  * workgroup stages the scales and zero points of its whole K range in LDS beside its activation
- * tiles (160 KiB in all), which allows K up to 36,096 at block_m 16 and 31,744 at block_m 32;
+ * tiles (160 KiB in all), which allows K up to 36,096 at block_m 16 and 35,840 at block_m 32;
  * longer K returns MOE_ERR_UNSUPPORTED before any launch (block_m 64 and 128 hold two k-blocks of
  * them at a time and have no such limit). */
 int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, const void* scales,

@@ -129,7 +129,7 @@ def test_gemm_validation(lib):
     # uint4 scales of the whole K range must fit in LDS beside the activation tiles
     assert _gemm(lib, K=36096 + 256, bm=16) == UNSUPPORTED
     assert b"LDS" in lib.moe_last_error()
-    assert _gemm(lib, K=31744 + 256, bm=32) == UNSUPPORTED
+    assert _gemm(lib, K=35840 + 256, bm=32) == UNSUPPORTED
     # block_m 64 and 128 keep two k-blocks of scales in LDS: a long K passes validation (a capacity
     # below one block leaves no block to launch, so nothing runs)
     assert _gemm(lib, K=65536, bm=128, rows=64, slots=32, cap=8) == OK

@@ -227,10 +227,10 @@ struct Shape {
   static constexpr int BM = 16 * MT;
   static constexpr int KB = BITS == 4 ? 128 : 64;            // k per k-block
   // activation chunk: four 16-byte vectors per thread, at least one k-block; two for BLOCK_M 16
-  // (256 columns: a short K, as in a tensor-parallel share with I = 256, is then a whole number of
-  // unrolled iterations instead of half of one spent on virtual k-blocks, and the smaller tile
-  // leaves LDS for more workgroups per compute unit)
-  static constexpr int KC0 = (MT == 1 ? 2 : 4) * 8 * kThreads / BM;
+  // and 32 (256 and 128 columns: a short K, as in a tensor-parallel share with I = 256, is then a
+  // whole number of unrolled iterations instead of half of one spent on virtual k-blocks, and the
+  // smaller tile and staging registers leave room for four workgroups per compute unit)
+  static constexpr int KC0 = (MT <= 2 ? 2 : 4) * 8 * kThreads / BM;
   static constexpr int KC = KC0 < KB ? KB : KC0;
   static constexpr int AV = BM * KC / 8 / kThreads;           // 16-byte vectors per thread
   static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
