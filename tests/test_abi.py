@@ -117,6 +117,7 @@ def test_gemm_validation(lib):
     assert _gemm(lib, q=_q(8, 0, 1)) == UNSUPPORTED            # int8 is symmetric
     assert _gemm(lib, q=_q(8, 0, 0)) == INVALID                # zeros given with has_zero = 0
     assert _gemm(lib, Z=NULL) == INVALID                       # zeros missing with has_zero = 1
+    assert _gemm(lib, Z=ctypes.c_void_p(0x100001)) == INVALID  # zeros not 2-byte aligned
     assert _gemm(lib, dt=2) == UNSUPPORTED
     assert _gemm(lib, K=300) == UNSUPPORTED
     assert _gemm(lib, N=1000) == UNSUPPORTED

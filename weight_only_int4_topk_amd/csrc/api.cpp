@@ -252,6 +252,7 @@ static int check_weights(const void* B, const void* scales, const void* zeros,
     return fail(MOE_ERR_INVALID_ARG, "zeros given but has_zero = 0 (both or neither)");
   if (!aligned(B, 16)) return fail(MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
   if (!aligned(scales, 2)) return fail(MOE_ERR_INVALID_ARG, "scales must be 2-byte aligned");
+  if (zeros && !aligned(zeros, 2)) return fail(MOE_ERR_INVALID_ARG, "zeros must be 2-byte aligned");
   return MOE_OK;
 }
 

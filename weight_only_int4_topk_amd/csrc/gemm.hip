@@ -314,7 +314,9 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // wavefront-uniform (a scalar: the LDS destination of a direct load is a scalar register, and a
+  // per-lane value there costs a loop that makes it uniform)
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int N = p.N;
   const int K = p.K;
   const int n_out = ACT ? N / 2 : N;
@@ -499,22 +501,29 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       for (int t = 0; t < NTW; ++t) mf[t] = s_meta[mrow * RP + (wave * NTW + t) * 16 + rsub];
     }
   };
-  // RING: thread tid fetches the scale and zero-point byte of workgroup row tid % R for one k-block
-  // (every thread loads, so no load is conditional; threads below R store), in register set X % 2
-  // for k-block X (relative to kb_beg; past the range, the last real k-block)
+  // RING: thread tid serves workgroup row tid % R for one k-block, in register set X % 2 for
+  // k-block X (relative to kb_beg; past the range, the last real k-block).  The first R / 64
+  // wavefronts fetch the rows' 2-byte scales, the others the 2-byte words holding their zero
+  // points (even-aligned; a zero-point block of N rows is N * K / 256 bytes, even as N is), and
+  // each writes its 16-bit half of the LDS entry: one memory instruction per wavefront and k-block
+  // (the address unit, not the bytes, is what these loads cost), the same instruction in both
+  // roles, so no branch.
+  static_assert(!RING || 2 * R == kThreads, "ring: two wavefront roles over the workgroup's rows");
   const uint32_t m_lr = (uint32_t)(tid % R);
   const uint32_t m_n = (uint32_t)(col_of(m_lr / (NTW * 16), (m_lr / 16) % NTW) + (m_lr % 16));
-  uint32_t m_sc[2], m_zb[2];
+  const int m_zero = wave >= R / kWave ? 1 : 0;
+  const __amdgpu_buffer_rsrc_t rs_m = m_zero ? rs_z : rs_s;
+  uint32_t m_v[2];
   auto ring_load = [&](int set, int X) {
     const int kb = min(kb_beg + X, kb_last);
-    m_sc[set] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, m_n * srow_bytes + kb * 2, 0, 0);
-    m_zb[set] = __builtin_amdgcn_raw_buffer_load_b8(rs_z, m_n * zrow_bytes + (kb >> 1), 0, 0);
+    const uint32_t off = m_zero ? ((m_n * zrow_bytes + (kb >> 1)) & ~1u) : m_n * srow_bytes + kb * 2;
+    m_v[set] = __builtin_amdgcn_raw_buffer_load_b16(rs_m, off, 0, 0);
   };
   auto ring_store = [&](int set, int X) {
     const int kb = min(kb_beg + X, kb_last);
-    if (tid < R)
-      s_meta[(X & 1) * RP + m_lr] =
-          (m_sc[set] & 0xFFFFu) | (((m_zb[set] >> ((kb & 1) * 4)) & 0xFu) << 16);
+    const uint32_t zbit = (((m_n * zrow_bytes + (kb >> 1)) & 1u) << 3) | ((kb & 1) << 2);
+    const uint32_t v = m_zero ? (m_v[set] >> zbit) & 0xFu : m_v[set] & 0xFFFFu;
+    reinterpret_cast<uint16_t*>(s_meta)[2 * ((X & 1) * RP + m_lr) + m_zero] = (uint16_t)v;
   };
 
   // ---- prologue: chunk 0 in LDS, chunks 1..AQ in flight, PF k-blocks of weights in flight.
