@@ -171,6 +171,13 @@ SMALL = {
     # few workgroups: the first GEMM is split over K (14 k-blocks into 2 x 7, the second split
     # starting on an odd k-block) and SiLU(gate) * up runs after the float32 partials are summed
     "split_odd_start": synth.Workload("so", E=8, H=1792, I=768, topk=2, Ms=(3,)),
+    # BLOCK_M 64 (scales and zero points through the two-slot ring): zero-point rows of an odd
+    # number of bytes (K / 256 = 7 and 5, so rows start on odd bytes and the 2-byte words the
+    # kernel reads straddle rows), and the second GEMM split over K into 2 x 5 k-blocks, the second
+    # split starting on an odd k-block (the other nibble of its zero-point bytes)
+    "prefill_odd_rows_bf16": synth.Workload("pob", E=16, H=1792, I=1280, topk=4, Ms=(300,),
+                                            dtype="bf16"),
+    "prefill_odd_rows_fp16": synth.Workload("pof", E=16, H=1792, I=1280, topk=4, Ms=(300,)),
 }
 
 
