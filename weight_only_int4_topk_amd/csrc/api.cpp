@@ -95,7 +95,7 @@ struct Plan {
   int nblk;
   int split1;  // > 1: the first GEMM writes float32 partials, a second pass applies SiLU(gate) * up
   int split2;
-  int ntw1, ntw2;
+  int ntw1, ntw2, wv1, wv2;
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
 };
 
@@ -126,11 +126,24 @@ int pick_ntw(int act, int N, int bm, int64_t est_blocks) {
   return N % 256 == 0 ? 4 : 2;
 }
 
+// Wavefronts per workgroup: 8 for the second GEMM at block_m 32 (2 column tiles) where N divides
+// the wider workgroup.  The 8 wavefronts share one activation tile, so each issues half the
+// activation loads per weight byte of a 4-wavefront workgroup (measured on the fused layer: Mixtral
+// shape at M = 64 -2.2 %, Qwen2 shape at M = 128 -1.3 %); for the first GEMM it measured neutral
+// to slower, and it keeps 4.
+int pick_waves(int act, int N, int bm, int ntw) {
+  if (act || bm != 32 || ntw != 2) return 4;
+  return N % 256 == 0 ? 8 : 4;
+}
+
 // The uint4 scales and zero points of a workgroup's whole K range are staged in LDS, so a long K
-// may not fit beside the activation tiles: fall back to two column tiles per wavefront (half the
-// rows per workgroup), and reject the shape if even that does not fit.
+// may not fit beside the activation tiles: fall back to two column tiles per wavefront and four
+// wavefronts (fewer rows per workgroup), and reject the shape if even that does not fit.
 int fit_lds(int K, int split, moe::GemmConfig& c, const char* what) {
-  if (moe::gemm_lds_bytes(K, split, c) > moe::kGemmLdsLimit) c.ntw = 2;
+  if (moe::gemm_lds_bytes(K, split, c) > moe::kGemmLdsLimit) {
+    c.ntw = 2;
+    c.waves = 4;
+  }
   const size_t need = moe::gemm_lds_bytes(K, split, c);
   if (need > moe::kGemmLdsLimit)
     return fail(MOE_ERR_UNSUPPORTED, "%s: K = %d needs %zu bytes of LDS per workgroup (limit %zu)",
@@ -166,6 +179,8 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   const int64_t est_blocks = estimate_blocks(slots, E, p.bm);
   p.ntw1 = pick_ntw(1, 2 * I, p.bm, est_blocks);
   p.ntw2 = pick_ntw(0, H, p.bm, est_blocks);
+  p.wv1 = pick_waves(1, 2 * I, p.bm, p.ntw1);
+  p.wv2 = pick_waves(0, H, p.bm, p.ntw2);
   // The first GEMM (K = H) keeps SiLU in its epilogue unless it has fewer workgroups than compute
   // units (few experts and a narrow I, as in a tensor-parallel share of many small experts): then
   // it is split over K into float32 partials.  Measured: with a few hundred workgroups the extra
@@ -174,7 +189,7 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   p.split1 = wgs1 < 256 ? pick_split(H / kb, wgs1, 4, 512) : 1;
   // The second GEMM (K = I) writes float32 partials anyway; split it to about two workgroups per
   // compute unit (more, shorter workgroups pay their start-up more often and write more partials)
-  const int64_t wgs2 = est_blocks * (H / (p.ntw2 * 64));
+  const int64_t wgs2 = est_blocks * (H / (p.ntw2 * 16 * p.wv2));
   p.split2 = pick_split(I / kb, wgs2, 4, 512);
   size_t off = 0;
   p.off_w = off;      off += up256((size_t)slots * 4);
@@ -307,8 +322,8 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   p.topk_w = topk_weights;
   p.C = C;
   p.split_k = 1;
-  moe::GemmConfig c{dtype, quant->bits, block_m, act, 0,
-                    pick_ntw(act, N, block_m, estimate_blocks(num_slots, E, block_m))};
+  const int ntw = pick_ntw(act, N, block_m, estimate_blocks(num_slots, E, block_m));
+  moe::GemmConfig c{dtype, quant->bits, block_m, act, 0, ntw, pick_waves(act, N, block_m, ntw)};
   if (int rc = fit_lds(K, 1, c, "gemm")) return rc;
   hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm launch");
@@ -356,8 +371,8 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   // split: plain columns (gate rows, then up rows) into float32 partials, 2 column tiles per
   // wavefront so the workgroup count matches the estimate the split was chosen for
   moe::GemmConfig c1{dtype, quant->bits, pl.bm, split1 ? 0 : 1, split1 ? 1 : 0,
-                     split1 ? 2 : pl.ntw1};
-  moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2};
+                     split1 ? 2 : pl.ntw1, split1 ? 4 : pl.wv1};
+  moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2, pl.wv2};
   if (int rc = fit_lds(H, pl.split1, c1, "gemm1")) return rc;
   if (int rc = fit_lds(I, pl.split2, c2, "gemm2")) return rc;
 

@@ -222,7 +222,7 @@ __device__ __forceinline__ void barrier_lds() {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-template <int BITS, int MT, int NTW>
+template <int BITS, int MT, int NTW, int THREADS = kThreads>
 struct Shape {
   static constexpr int BM = 16 * MT;
   static constexpr int KB = BITS == 4 ? 128 : 64;            // k per k-block
@@ -232,7 +232,8 @@ struct Shape {
   // smaller tile and staging registers leave room for four workgroups per compute unit)
   static constexpr int KC0 = (MT <= 2 ? 2 : 4) * 8 * kThreads / BM;
   static constexpr int KC = KC0 < KB ? KB : KC0;
-  static constexpr int AV = BM * KC / 8 / kThreads;           // 16-byte vectors per thread
+  static constexpr int AV = BM * KC / 8 / THREADS;           // 16-byte vectors per thread
+  static_assert(AV >= 1 && BM * KC / 8 % THREADS == 0, "whole activation vectors per thread");
   static constexpr int LDA = KC + 8;                          // LDS row stride (16-byte pad)
   static constexpr int KBC = KC / KB;                         // k-blocks per chunk
   // weight k-blocks in flight per wavefront.  The decode kernels keep 2, not 4: fewer registers
@@ -251,9 +252,10 @@ struct Shape {
   static constexpr int U = MT >= 4 ? U0 / gcd_c(U0, 2 * KBC) * (2 * KBC) : U0;
 };
 
-template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32>
-__global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
-  using S = Shape<BITS, MT, NTW>;
+template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32, int WAVES>
+__global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p) {
+  constexpr int THREADS = WAVES * kWave;
+  using S = Shape<BITS, MT, NTW, THREADS>;
   constexpr int BM = S::BM;
   constexpr int KC = S::KC;
   constexpr int PF = S::PF;
@@ -264,9 +266,9 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   constexpr int AQ = S::AQ;
   constexpr int STEPS = KB / 32;                    // MFMAs per k-block
   constexpr int NOUT = ACT ? NTW / 2 : NTW;         // output tiles per wave
-  constexpr int WG_COLS = kWaves * NOUT * 16;
+  constexpr int WG_COLS = WAVES * NOUT * 16;
   constexpr int VPR = KC / 8;                       // 16-byte vectors per activation row chunk
-  constexpr int R = kWaves * NTW * 16;              // weight rows of the workgroup
+  constexpr int R = WAVES * NTW * 16;               // weight rows of the workgroup
   // metadata row pitch in dwords: consecutive staging threads write entries 2 * RP apart, and
   // RP = 2 (mod 32) spreads them over the LDS banks
   constexpr int RP = R + 2;
@@ -386,7 +388,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   uint32_t arow[AV], acol[AV];
 #pragma unroll
   for (int i = 0; i < AV; ++i) {
-    const int idx = tid + i * kThreads;
+    const int idx = tid + i * THREADS;
     const int r = idx / VPR;
     // each thread reads the slot ids it needs itself: the activation loads then leave without
     // waiting for a workgroup barrier, under the same memory latency as weights and scales
@@ -400,7 +402,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // chunk c travels in areg[c % AQ] (the index is a compile-time constant at every use)
   u32x4_t areg[DIRECT ? 1 : AQ][DIRECT ? 1 : AV];
   // DIRECT: chunk c into LDS buffer buf; lane l of wave w writes the 16 bytes of thread
-  // w * 64 + l + i * kThreads, which in an unpadded tile is that thread's (row, 8-column group)
+  // w * 64 + l + i * THREADS, which in an unpadded tile is that thread's (row, 8-column group)
   auto dma_a = [&](int c, int buf) {
     const uint32_t kbase = (uint32_t)((kb_beg + c * KBC) * KB);
 #pragma unroll
@@ -410,7 +412,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs_a,
           (__attribute__((address_space(3))) void*)((uint8_t*)abuf(buf) +
-                                                    (size_t)(wave * kWave + i * kThreads) * 16),
+                                                    (size_t)(wave * kWave + i * THREADS) * 16),
           16, off, 0, 0, 0);
     }
   };
@@ -427,7 +429,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   auto store_a = [&](int q, int buf) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int idx = tid + i * kThreads;
+      const int idx = tid + i * THREADS;
       const int r = idx / VPR;
       const int c8 = idx - r * VPR;
       u32x4_t v = areg[q][i];
@@ -508,7 +510,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   // each writes its 16-bit half of the LDS entry: one memory instruction per wavefront and k-block
   // (the address unit, not the bytes, is what these loads cost), the same instruction in both
   // roles, so no branch.
-  static_assert(!RING || 2 * R == kThreads, "ring: two wavefront roles over the workgroup's rows");
+  static_assert(!RING || 2 * R == THREADS, "ring: two wavefront roles over the workgroup's rows");
   const uint32_t m_lr = (uint32_t)(tid % R);
   const uint32_t m_n = (uint32_t)(col_of(m_lr / (NTW * 16), (m_lr / 16) % NTW) + (m_lr % 16));
   const int m_zero = wave >= R / kWave ? 1 : 0;
@@ -549,7 +551,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   } else if constexpr (BITS == 4) {
     const int kb0 = kb_beg & ~1;
     const int npair = (kb_end - kb0 + 1) >> 1;
-    for (int item = tid; item < R * npair; item += kThreads) {
+    for (int item = tid; item < R * npair; item += THREADS) {
       const int lr = item / npair;
       const int j = item - lr * npair;
       const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
@@ -770,7 +772,7 @@ __global__ void __launch_bounds__(kThreads) wna16_gemm_kernel(GemmParams p) {
   }
 }
 
-template <int DT, int BITS, int MT, int NTW>
+template <int DT, int BITS, int MT, int NTW, int WV>
 hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
   const int n_out = c.act ? p.N / 2 : p.N;
   const int n_chunks = n_out / gemm_wg_cols(c);
@@ -780,21 +782,22 @@ hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stre
   const size_t lds = gemm_meta_lds_bytes(p.K, p.split_k, c);
   if (gemm_lds_bytes(p.K, p.split_k, c) > kGemmLdsLimit) return hipErrorInvalidValue;
   if (c.act)
-    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 1, 0>), dim3((unsigned)grid),
-                       dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 1, 0, WV>), dim3((unsigned)grid),
+                       dim3(WV * kWave), lds, stream, p);
   else if (c.out_f32)
-    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 1>), dim3((unsigned)grid),
-                       dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 1, WV>), dim3((unsigned)grid),
+                       dim3(WV * kWave), lds, stream, p);
   else
-    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 0>), dim3((unsigned)grid),
-                       dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 0, WV>), dim3((unsigned)grid),
+                       dim3(WV * kWave), lds, stream, p);
   return hipGetLastError();
 }
 
 template <int DT, int BITS, int MT>
 hipError_t launch_mt(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
-  if (MT == 1 && c.ntw == 4) return launch_ntw<DT, BITS, MT, (MT == 1 ? 4 : 2)>(p, c, stream);
-  return launch_ntw<DT, BITS, MT, 2>(p, c, stream);
+  if (MT == 1 && c.ntw == 4) return launch_ntw<DT, BITS, MT, (MT == 1 ? 4 : 2), 4>(p, c, stream);
+  if (MT == 2 && c.waves == 8) return launch_ntw<DT, BITS, MT, 2, (MT == 2 ? 8 : 4)>(p, c, stream);
+  return launch_ntw<DT, BITS, MT, 2, 4>(p, c, stream);
 }
 
 template <int DT, int BITS>
@@ -810,13 +813,17 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 
 }  // namespace
 
+// wavefronts per workgroup the launch uses (8 only where the kernel is built with 8)
+static int gemm_waves(const GemmConfig& c) { return c.waves == 8 && c.block_m == 32 ? 8 : 4; }
+
 size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c) {
   if (c.bits != 4) return 0;
   const int ntw = (c.ntw == 4 && c.block_m == 16) ? 4 : 2;
-  if (c.block_m >= 64) return (size_t)(kWaves * ntw * 16 + 2) * 2 * 4;  // two-slot ring
+  const int waves = gemm_waves(c);
+  if (c.block_m >= 64) return (size_t)(waves * ntw * 16 + 2) * 2 * 4;  // two-slot ring
   const int kb_total = K / 128;
   const int kb_per = (kb_total + split_k - 1) / split_k;
-  return (size_t)(kWaves * ntw * 16 + 2) * kb_per * 4;  // row pitch R + 2 dwords
+  return (size_t)(waves * ntw * 16 + 2) * kb_per * 4;  // row pitch R + 2 dwords
 }
 
 template <int BITS, int MT>
@@ -839,7 +846,7 @@ size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c) {
 
 int gemm_wg_cols(const GemmConfig& c) {
   const int ntw = (c.ntw == 4 && c.block_m == 16) ? 4 : 2;
-  return kWaves * (c.act ? ntw / 2 : ntw) * 16;
+  return gemm_waves(c) * (c.act ? ntw / 2 : ntw) * 16;
 }
 
 hipError_t launch_gemm(const GemmParams& p_in, const GemmConfig& c, hipStream_t stream) {

@@ -57,6 +57,7 @@ struct GemmConfig {
   int act;       // 0 none, 1 silu-mul
   int out_f32;   // 1: float partials [split, num_slots, N]
   int ntw;       // column tiles of 16 per wavefront: 2, or 4 (block_m 16 only)
+  int waves = 4; // wavefronts per workgroup: 4, or 8 (block_m 32 with 2 tiles only; honoured there)
 };
 
 // Columns of output one workgroup covers (N % this must be 0; act: gate columns).
