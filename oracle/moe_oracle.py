@@ -37,7 +37,7 @@ __all__ = [
     "GROUP", "unpack_uint4", "dequant_uint4", "dequant_int8", "dequant_bits",
     "exp_f32_spec", "sigmoid_f32_spec", "route_softmax", "route_sigmoid_grouped", "route",
     "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
-    "grouped_gemm", "to_numpy",
+    "grouped_gemm", "dense_gemm", "to_numpy",
 ]
 
 
@@ -330,3 +330,21 @@ def grouped_gemm(A, a_row_div: int, weight_of, sorted_token_ids, expert_ids, num
             h = h * tw[s]
         out[s] = h
     return out
+
+
+def dense_gemm(A, qweight, scales, zeros=None):
+    """The dense weight-only GEMM, as a definition: C = A @ W^T in float64, W the exact decoded
+    weights of one weight matrix (uint4 g128 with integer zero points when zeros are given, int8
+    with one scale per row otherwise).
+
+    This is the one-expert, every-row-routed case of the grouped GEMM, and the operation the small-n
+    GEMM benchmark of "[Kernel] optimize performance of gptq marlin kernel when n is small" times
+    (benchmark script and table: m 16, k 8192, n 128 ... 32768, uint4, group 128, integer zero point).
+    A [M, K]; qweight uint8 [N, K/2] or int8 [N, K]; scales [N, K/128] or [N]; returns [M, N]."""
+    A64 = np.asarray(to_numpy(A), dtype=np.float64)
+    if zeros is not None:
+        W = dequant_uint4(to_numpy(qweight), to_numpy(scales), to_numpy(zeros))
+    else:
+        W = dequant_int8(to_numpy(qweight), to_numpy(scales))
+    assert A64.shape[1] == W.shape[1], (A64.shape, W.shape)
+    return A64 @ W.T

@@ -84,7 +84,7 @@ WORKLOADS = {
 # ----------------------------------------------------------------------------------------------
 # seeded streams
 # ----------------------------------------------------------------------------------------------
-_TAGS = {"w13": 1, "w2": 2, "x": 3, "logits": 4, "bias": 5}
+_TAGS = {"w13": 1, "w2": 2, "x": 3, "logits": 4, "bias": 5, "dense_w": 6, "dense_x": 7}
 
 
 def stream_seed(seed: int, tag: str, idx: int = 0) -> int:
@@ -225,3 +225,21 @@ def w13_bytes_per_expert(wl: Workload) -> int:
     if wl.bits == 4:
         return N * K // 2 + 2 * N * (K // GROUP) + N * (K // (2 * GROUP))
     return N * K + 2 * N
+
+
+# ----------------------------------------------------------------------------------------------
+# dense GEMM inputs (one weight matrix): the small-n benchmark's shapes, m 16, k 8192, n 128..32768
+# ----------------------------------------------------------------------------------------------
+def make_dense(M: int, N: int, K: int, bits: int = 4, dtype: str = "fp16", seed: int = 0,
+               device="cpu") -> dict:
+    """A [M, K] = N(0, 0.1^2) rounded to dtype (the benchmark's activations, randn / 10); weights
+    N(0, 0.02^2) [N, K] encoded as the layer's experts (uint4 g128 asymmetric, or int8 per row)."""
+    dt = _DT[dtype]
+    A = (_randn((M, K), seed, "dense_x", 0, device) * 0.1).to(dt)
+    w = _randn((N, K), seed, "dense_w", 0, device) * 0.02
+    if bits == 4:
+        qw, sc, zp = encode_uint4_g128(w, dt)
+    else:
+        qw, sc = encode_int8_channel(w, dt)
+        zp = None
+    return {"A": A, "B": qw, "scales": sc, "zeros": zp}

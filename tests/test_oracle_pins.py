@@ -343,3 +343,67 @@ def test_grouped_gemm_definition_matches_layer():
         for j in range(wl.topk):
             out[m] += y[m * wl.topk + j]
     np.testing.assert_allclose(out, O.moe_layer(x, ids, w, src), rtol=1e-12, atol=1e-16)
+
+
+# ---- dense GEMM (one weight matrix, every row routed) -------------------------------------------
+def _pack_nibbles(v):
+    """uint4 codes [R, 2n] -> bytes [R, n], even index in bits 0-3 (written here, not the oracle's)."""
+    v = np.asarray(v, dtype=np.uint8)
+    return (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_dense_gemm_uint4_equals_matmul_of_grid_weights():
+    """Integer codes, zero points and power-of-two-ish scales chosen here: C must be A @ W^T of the
+    weights (q - z) * s built directly from them.  N != K != M, so a transposed operand fails."""
+    rng = np.random.default_rng(11)
+    M, N, K = 5, 24, 512
+    ng = K // 128
+    q = rng.integers(0, 16, size=(N, K))
+    z = rng.integers(0, 16, size=(N, ng))
+    s = 2.0 ** -rng.integers(3, 9, size=(N, ng)).astype(np.float64)
+    W = ((q.reshape(N, ng, 128) - z[..., None]) * s[..., None]).reshape(N, K)
+    A = rng.standard_normal((M, K))
+    C = O.dense_gemm(A, _pack_nibbles(q), s, _pack_nibbles(z))
+    assert C.shape == (M, N)
+    np.testing.assert_allclose(C, A @ W.T, rtol=1e-12, atol=1e-15)
+
+
+def test_dense_gemm_int8_equals_matmul_of_grid_weights():
+    rng = np.random.default_rng(12)
+    M, N, K = 3, 40, 256
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s = 2.0 ** -rng.integers(5, 12, size=N).astype(np.float64)
+    A = rng.standard_normal((M, K))
+    np.testing.assert_allclose(O.dense_gemm(A, q, s), A @ (q.astype(np.float64) * s[:, None]).T,
+                               rtol=1e-12, atol=1e-15)
+
+
+def test_dense_gemm_one_hot_rows_read_back_weight_columns():
+    """A = one-hot rows selecting k_i: row i of C is column k_i of the decoded weights, exactly."""
+    rng = np.random.default_rng(13)
+    N, K = 16, 256
+    q = rng.integers(0, 16, size=(N, K))
+    z = rng.integers(0, 16, size=(N, K // 128))
+    s = rng.uniform(0.01, 0.1, size=(N, K // 128))
+    ks = np.array([0, 1, 127, 128, 200, 255])
+    A = np.zeros((len(ks), K))
+    A[np.arange(len(ks)), ks] = 1.0
+    C = O.dense_gemm(A, _pack_nibbles(q), s, _pack_nibbles(z))
+    expect = (q[:, ks] - z[:, ks // 128]) * s[:, ks // 128]
+    assert np.array_equal(C, expect.T)
+
+
+def test_dense_gemm_is_the_one_expert_grouped_gemm():
+    """The dense case of the grouped GEMM: one expert, every row its own slot (align of all-zero ids)."""
+    rng = np.random.default_rng(14)
+    M, N, K = 20, 32, 256
+    q = rng.integers(0, 16, size=(1, N, K))
+    z = rng.integers(0, 16, size=(1, N, K // 128))
+    s = rng.uniform(0.01, 0.1, size=(1, N, K // 128))
+    qp, zp = _pack_nibbles(q[0]), _pack_nibbles(z[0])
+    A = rng.standard_normal((M, K))
+    st, ex, T = O.align_block_size(np.zeros(M, dtype=np.int32), 1, 16)
+    rows = O.grouped_gemm(A, 1, lambda e: O.dequant_uint4(qp, s[0], zp), st, ex, T, 16, M)
+    dense = O.dense_gemm(A, qp, s[0], zp)
+    for r in range(M):
+        np.testing.assert_allclose(rows[r], dense[r], rtol=1e-13, atol=1e-15)
