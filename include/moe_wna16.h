@@ -134,6 +134,30 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
                    const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
                    int num_slots, const float* topk_weights, int act, void* C, void* stream);
 
+/* Dense GEMM with weights decoded in the kernel: the one-expert, every-row-routed case of
+ * moe_wna16_gemm without the align arrays.  "[Kernel] optimize performance of gptq marlin kernel when
+ * n is small" benchmarks this operation for uint4 g128 with integer zero points at m = 16,
+ * k = 8192, n = 128 ... 32768 (its benchmark script and table), where n alone gives too few
+ * workgroups to stream the weights; that PR adds an atomic-add reduction for it.  Here the K range
+ * is split across workgroups into float32 partials that a second launch sums in a fixed order
+ * (deterministic), and the split is chosen so that about 512 workgroups stream the weights.
+ *   C[m, 0:N] = A[m, :] . W^T  (float32 accumulation of the decoded weights), rounded to dtype
+ *   A         device dtype [M, K]
+ *   B, scales, zeros: weight storage of one expert (E = 1) with N rows and K columns (zeros NULL
+ *             for int8)
+ *   workspace device buffer of at least moe_wna16_dense_gemm_workspace_size(M, N, K, quant, dtype)
+ *             bytes, 256-byte aligned (may be NULL when that size is 0: no split)
+ *   C         device dtype [M, N]; every element is written
+ * Limits: K % 256 == 0, N % 128 == 0, and the uint4 K limits of moe_wna16_gemm (rows per block:
+ * the smallest of 16, 32, 64 (int8: 128) that holds M; larger M runs several blocks). */
+int moe_wna16_dense_gemm(const void* A, int M, int K, const void* B, const void* scales,
+                         const void* zeros, const moe_quant_t* quant, int N, int dtype,
+                         void* workspace, size_t workspace_bytes, void* C, void* stream);
+
+/* Workspace bytes moe_wna16_dense_gemm needs (0 when it does not split K; 0 for invalid sizes). */
+size_t moe_wna16_dense_gemm_workspace_size(int M, int N, int K, const moe_quant_t* quant,
+                                           int dtype);
+
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits: the smallest of {16, 32, 64, 128} that holds 1.5x the average number of slots per active
  * expert (min(E, M*topk) experts), so a typical expert's slots share one block and its weights

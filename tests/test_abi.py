@@ -166,6 +166,39 @@ def test_fused_validation_and_workspace(lib):
     assert fused(M=0) == OK
 
 
+def test_dense_gemm_validation_and_workspace(lib):
+    q4, q8 = _q(4, 128, 1), _q(8, 0, 0)
+    # the small-n benchmark shape (m 16, k 8192): n = 4096 splits K into float32 partials, n = 32768
+    # has enough column chunks to split less, and a split never leaves fewer than 4 k-blocks
+    ws4096 = lib.moe_wna16_dense_gemm_workspace_size(16, 4096, 8192, q4, 0)
+    assert ws4096 > 0 and ws4096 % (16 * 4096 * 4) == 0
+    assert ws4096 // (16 * 4096 * 4) <= 8192 // 128 // 4
+    ws32k = lib.moe_wna16_dense_gemm_workspace_size(16, 32768, 8192, q4, 0)
+    assert ws32k // (16 * 32768 * 4) < ws4096 // (16 * 4096 * 4)
+    assert lib.moe_wna16_dense_gemm_workspace_size(16, 4096, 8192, _q(5, 128, 1), 0) == 0
+    assert lib.moe_wna16_dense_gemm_workspace_size(0, 4096, 8192, q4, 0) == 0
+
+    def dense(**kw):
+        a = dict(A=FAKE, M=16, K=8192, Bw=FAKE, S=FAKE, Z=FAKE, q=q4, N=4096, dt=0, ws=FAKE,
+                 wsb=ws4096, C=FAKE)
+        a.update(kw)
+        return lib.moe_wna16_dense_gemm(a["A"], a["M"], a["K"], a["Bw"], a["S"], a["Z"], a["q"],
+                                        a["N"], a["dt"], a["ws"], a["wsb"], a["C"], NULL)
+
+    assert dense(wsb=ws4096 - 1) == WORKSPACE
+    assert dense(ws=NULL) == INVALID                            # a split needs the workspace
+    assert dense(ws=ctypes.c_void_p(0x100010)) == INVALID       # 256-byte alignment
+    assert dense(K=8000) == UNSUPPORTED
+    assert dense(N=4000) == UNSUPPORTED
+    assert dense(q=q8) == INVALID                               # int8 takes no zero points
+    assert dense(Z=NULL) == INVALID
+    assert dense(dt=3) == UNSUPPORTED
+    assert dense(C=NULL) == INVALID
+    assert dense(A=ctypes.c_void_p(0x100008)) == INVALID
+    assert dense(M=-1) == INVALID
+    assert dense(M=0) == OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(B, "_lib", None)

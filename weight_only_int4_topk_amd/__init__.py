@@ -52,6 +52,10 @@ _SIGS = {
     "moe_align_block_size": ([_P, _I, _I, _I, _P, _P, _P, _I64, _P], _I),
     "moe_wna16_gemm": ([_P, _I, _I, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _I, _I,
                         _P, _P, _P, _I64, _I, _I, _P, _I, _P, _P], _I),
+    "moe_wna16_dense_gemm": ([_P, _I, _I, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _P,
+                              ctypes.c_size_t, _P, _P], _I),
+    "moe_wna16_dense_gemm_workspace_size": ([_I, _I, _I, ctypes.POINTER(MoeQuant), _I],
+                                            ctypes.c_size_t),
     "fused_moe_wna16_workspace_size": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I],
                                        ctypes.c_size_t),
     "fused_moe_wna16": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P, _P,
@@ -163,6 +167,28 @@ def moe_wna16_gemm(A, a_row_div, B, scales, zeros, sorted_ids, expert_ids, num_p
                                 _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post),
                                 sorted_ids.numel(), block_m, num_slots, _ptr(topk_weights), act,
                                 _ptr(C), _stream(stream)))
+    return C
+
+
+def moe_wna16_dense_gemm_workspace_size(M, N, K, quant: MoeQuant, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().moe_wna16_dense_gemm_workspace_size(M, N, K, ctypes.byref(quant), code))
+
+
+def moe_wna16_dense_gemm(A, B, scales, zeros=None, workspace=None, C=None, stream=None):
+    """C [M, N] = A [M, K] . W^T for one weight matrix B ([N, K/2] uint8 or [N, K] int8)."""
+    quant = _quant_of(B, zeros)
+    M, K = A.shape
+    N = B.shape[0]
+    need = moe_wna16_dense_gemm_workspace_size(M, N, K, quant, A.dtype)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=A.device)
+    if C is None:
+        C = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    _check(lib().moe_wna16_dense_gemm(_ptr(A), M, K, _ptr(B), _ptr(scales), _ptr(zeros),
+                                      ctypes.byref(quant), N, _dtype_code(A.dtype),
+                                      _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                      _ptr(C), _stream(stream)))
     return C
 
 

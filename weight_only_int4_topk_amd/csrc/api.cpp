@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -168,6 +169,15 @@ int64_t estimate_blocks(int64_t slots, int E, int bm) {
   return std::max<int64_t>(std::min<int64_t>(E, slots), slots / bm);
 }
 
+// Blocks a batch of M tokens is expected to fill when each token picks topk of E experts evenly:
+// E * (1 - (1 - topk/E)^M) distinct experts, at least M * topk / bm blocks.  min(E, M * topk)
+// overestimates at small M (Mixtral shape, M = 4: 8 assumed, 5.5 expected), which left the split
+// second GEMM with about one workgroup per compute unit (measured: 4 % slower layer).
+int64_t estimate_active_blocks(int64_t M, int topk, int E, int bm) {
+  const double act = E * (1.0 - std::pow(1.0 - (double)topk / E, (double)M));
+  return std::max<int64_t>(std::max<int64_t>(1, (int64_t)(act + 0.5)), M * topk / bm);
+}
+
 Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int block_m) {
   (void)dtype;
   Plan p{};
@@ -189,7 +199,7 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   p.split1 = wgs1 < 256 ? pick_split(H / kb, wgs1, 4, 512) : 1;
   // The second GEMM (K = I) writes float32 partials anyway; split it to about two workgroups per
   // compute unit (more, shorter workgroups pay their start-up more often and write more partials)
-  const int64_t wgs2 = est_blocks * (H / (p.ntw2 * 16 * p.wv2));
+  const int64_t wgs2 = estimate_active_blocks(M, topk, E, p.bm) * (H / (p.ntw2 * 16 * p.wv2));
   p.split2 = pick_split(I / kb, wgs2, 4, 512);
   size_t off = 0;
   p.off_w = off;      off += up256((size_t)slots * 4);
@@ -202,6 +212,39 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   off += up256(std::max((size_t)p.split1 * slots * 2 * I, (size_t)p.split2 * slots * H) * 4);
   p.total = off;
   return p;
+}
+
+// ------------------------------------------------------------------------------------------------
+// dense GEMM (one expert, every row a slot)
+// ------------------------------------------------------------------------------------------------
+struct DensePlan {
+  moe::GemmConfig c;
+  int nblk;
+  int split;
+  size_t ws;  // float32 partials [split, M, N] when split > 1
+};
+
+// Rows per block: the smallest of {16, 32, 64} (int8: up to 128) that holds M, so short batches
+// stream every weight once.  Column tiles and split as for the grouped GEMM: four tiles at 16 rows
+// only while four-tile workgroups can still reach ~512 with splits of >= 4 k-blocks (a short N, as in
+// n = 4096 at k = 8192, keeps two tiles and so twice the workgroups), then split K to ~512
+// workgroups.
+DensePlan make_dense_plan(int M, int N, int K, int bits, int dtype) {
+  DensePlan d{};
+  int bm = 16;
+  const int top = bits == 4 ? 64 : 128;
+  while (bm < M && bm < top) bm *= 2;
+  d.nblk = (M + bm - 1) / bm;
+  const int kb_total = K / (bits == 4 ? 128 : 64);
+  int ntw = 2;
+  if (bm == 16 && N % 256 == 0 && (int64_t)(N / 256) * d.nblk * std::max(1, kb_total / 4) >= 512)
+    ntw = 4;
+  const int wv = pick_waves(0, N, bm, ntw);
+  const int64_t wgs = (int64_t)d.nblk * (N / (ntw * 16 * wv));
+  d.split = pick_split(kb_total, wgs, 4, 512);
+  d.c = moe::GemmConfig{dtype, bits, bm, 0, d.split > 1 ? 1 : 0, ntw, wv};
+  d.ws = d.split > 1 ? up256((size_t)d.split * M * N * 4) : 0;
+  return d;
 }
 
 }  // namespace
@@ -327,6 +370,59 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   if (int rc = fit_lds(K, 1, c, "gemm")) return rc;
   hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm launch");
+}
+
+size_t moe_wna16_dense_gemm_workspace_size(int M, int N, int K, const moe_quant_t* quant,
+                                           int dtype) {
+  if (M <= 0 || N <= 0 || K <= 0 || !quant || (quant->bits != 4 && quant->bits != 8)) return 0;
+  return make_dense_plan(M, N, K, quant->bits, dtype).ws;
+}
+
+int moe_wna16_dense_gemm(const void* A, int M, int K, const void* B, const void* scales,
+                         const void* zeros, const moe_quant_t* quant, int N, int dtype,
+                         void* workspace, size_t workspace_bytes, void* C, void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (int rc = check_quant(quant)) return rc;
+  if (M < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d N=%d K=%d", M, N, K);
+  if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
+  if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
+  if ((int64_t)M * K * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)N * (quant->bits == 4 ? K / 2 : K) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "A or the weights exceed 2 GiB");
+  if (int rc = check_weights(B, scales, zeros, quant)) return rc;
+  if (M == 0) return MOE_OK;
+  if (!A || !C) return fail(MOE_ERR_INVALID_ARG, "NULL A / C");
+  if (!aligned(A, 16) || !aligned(C, 16))
+    return fail(MOE_ERR_INVALID_ARG, "A and C must be 16-byte aligned");
+  DensePlan d = make_dense_plan(M, N, K, quant->bits, dtype);
+  if (workspace_bytes < d.ws)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, d.ws);
+  if (d.ws && (!workspace || !aligned(workspace, 256)))
+    return fail(MOE_ERR_INVALID_ARG, "workspace must be a 256-byte aligned device buffer");
+  if (int rc = fit_lds(K, d.split, d.c, "dense gemm")) return rc;
+  moe::GemmParams p{};
+  p.A = A;
+  p.num_a_rows = M;
+  p.a_row_div = 1;
+  p.B = (const uint8_t*)B;
+  p.scales = scales;
+  p.zeros = (const uint8_t*)zeros;
+  p.E = 1;
+  p.N = N;
+  p.K = K;
+  p.num_blocks = d.nblk;
+  p.num_slots = M;
+  p.C = d.split > 1 ? workspace : C;
+  p.split_k = d.split;
+  p.dense = 1;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = moe::launch_gemm(p, d.c, st);
+  if (e != hipSuccess) return hip_fail(e, "dense gemm launch");
+  if (d.split > 1) {
+    e = moe::launch_split_reduce((const float*)workspace, d.split, M, N, dtype, C, st);
+    if (e != hipSuccess) return hip_fail(e, "dense split reduce launch");
+  }
+  return MOE_OK;
 }
 
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,

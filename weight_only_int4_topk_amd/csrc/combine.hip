@@ -102,7 +102,32 @@ __global__ void __launch_bounds__(256) act_combine_kernel(const float* __restric
   *(uint2*)(inter + (size_t)s * I + c) = make_uint2(lo, hi);
 }
 
+// Dense GEMM split over K: out[r, c] = sum_z partial[z, r, c], z ascending; four columns per thread.
+template <int DT>
+__global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restrict__ partial,
+                                                           int split, size_t split_stride,
+                                                           size_t total4, uint16_t* __restrict__ out) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total4) return;
+  store4<DT>(out + idx * 4, sum_splits(partial + idx * 4, split, split_stride));
+}
+
 }  // namespace
+
+hipError_t launch_split_reduce(const float* partial, int split, int rows, int cols, int dtype,
+                               void* out, hipStream_t stream) {
+  const size_t total4 = (size_t)rows * cols / 4;
+  if (total4 == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((total4 + 255) / 256);
+  const size_t stride = (size_t)rows * cols;
+  if (dtype == 0)
+    hipLaunchKernelGGL(split_reduce_kernel<0>, dim3(grid), dim3(256), 0, stream, partial, split,
+                       stride, total4, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(split_reduce_kernel<1>, dim3(grid), dim3(256), 0, stream, partial, split,
+                       stride, total4, (uint16_t*)out);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_combine(const float* partial, int split, int slots, int I, int dtype,
                               void* inter, hipStream_t stream) {

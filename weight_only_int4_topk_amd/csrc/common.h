@@ -139,4 +139,12 @@ __device__ __forceinline__ float bits_to_float(uint16_t b) {
   }
 }
 
+// four float32 values rounded to dtype (0 fp16, 1 bf16) and stored as 8 bytes
+template <int DT>
+__device__ __forceinline__ void store4(uint16_t* dst, floatx4_t v) {
+  const uint32_t lo = DT == 0 ? f32x2_to_f16x2(v[0], v[1]) : f32x2_to_bf16x2(v[0], v[1]);
+  const uint32_t hi = DT == 0 ? f32x2_to_f16x2(v[2], v[3]) : f32x2_to_bf16x2(v[2], v[3]);
+  *(uint2*)dst = make_uint2(lo, hi);
+}
+
 }  // namespace moe

@@ -330,13 +330,17 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   bid /= split;
   const int nc = bid % n_chunks;
   const int blk = bid / n_chunks;
-  if (blk * BM >= p.num_post[0]) return;
-  const int e = p.expert_ids[blk];
+  // dense: rows are slots 0..num_slots-1 in order, one expert, no align arrays
+  if (blk * BM >= (p.dense ? p.num_slots : p.num_post[0])) return;
+  const int e = p.dense ? 0 : p.expert_ids[blk];
   if ((unsigned)e >= (unsigned)p.E) return;
+  auto slot_at = [&](int i) -> int {
+    return p.dense ? (i < p.num_slots ? i : -1) : p.sorted_ids[i];
+  };
 
   // slot of each block row, for the epilogue (published by the prologue's barrier)
   if (tid < BM) {
-    const int s = p.sorted_ids[blk * BM + tid];
+    const int s = slot_at(blk * BM + tid);
     s_slot[tid] = (unsigned)s < (unsigned)p.num_slots ? s : -1;
   }
 
@@ -392,7 +396,7 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
     const int r = idx / VPR;
     // each thread reads the slot ids it needs itself: the activation loads then leave without
     // waiting for a workgroup barrier, under the same memory latency as weights and scales
-    const int sl = p.sorted_ids[blk * BM + r];
+    const int sl = slot_at(blk * BM + r);
     const int row = (unsigned)sl < (unsigned)p.num_slots ? (p.a_row_div == 1 ? sl : sl / p.a_row_div) : -1;
     arow[i] = row >= 0 ? (uint32_t)row * K * 2 : 0x80000000u;
     // DIRECT: this thread's LDS slot (r, idx % VPR) holds logical chunk (idx % VPR) ^ swz(r)

@@ -45,6 +45,8 @@ struct GemmParams {
   void* C;                    // act: dtype [num_slots, N/2]; out_f32: float [split, num_slots, N];
                               // else dtype [num_slots, N]
   int split_k;                // K split count (out_f32 only, else 1)
+  int dense;                  // 1: slot r of block b is row b * block_m + r (< num_slots), expert
+                              // 0; sorted_ids, expert_ids and num_post are not read
   uint32_t dec_mask;          // set by launch_gemm: low nibble-pair mask of the decode
   uint32_t dec_mask_hi;       // set by launch_gemm: high nibble-pair mask (fp16 uint4 decode)
   uint32_t dec_magic;         // set by launch_gemm: magic bias in both 16-bit halves
@@ -69,6 +71,9 @@ size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c);
 constexpr size_t kGemmLdsLimit = 160 * 1024;
 hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
 
+// out[r, c] = sum_z partial[z, r, c] (z ascending) over rows x cols, rounded to dtype.
+hipError_t launch_split_reduce(const float* partial, int split, int rows, int cols, int dtype,
+                               void* out, hipStream_t stream);
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);
 // inter[s, i] = SiLU(sum_z partial[z, s, i]) * sum_z partial[z, s, I + i] (first GEMM split over K)
