@@ -9,8 +9,9 @@ Infinity Cache by the time the same copy comes round again.  Steps are replayed 
 that hold several consecutive layer calls.
 
 Also reported: the roofline of the dominant kernel (the w13 grouped GEMM with the SiLU epilogue),
-timed alone with HIP events on the stream it is launched on; an M sweep of the workload; and the
-CPU oracle's throughput on a bounded sample of the same batch.
+timed alone with HIP events on the stream it is launched on; an M sweep of the workload; the CPU
+oracle's throughput on a bounded sample of the same batch; and the dense uint4 GEMM at the small-n
+benchmark's shapes (m 16, k 8192, n 128 ... 32768).
 """
 from __future__ import annotations
 
@@ -46,10 +47,54 @@ def parse():
     ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense uint4 GEMM sweep (m 16, k 8192, n 128 ... 32768)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device-to-device copy (known bytes) so that "
                          "profiler traffic counters can be scaled")
     return ap.parse_args()
+
+
+def graph_replay(fns, steps, warmup):
+    """Replay `steps` calls cycling through fns (one per weight copy), in graphs of G calls.
+    Returns (seconds of the timed steps by HIP events on the current stream, wall seconds, G)."""
+    import torch
+    L = len(fns)
+    G = L * max(1, 16 // L)
+    for f in fns:                          # compile/warm every code path eagerly first
+        f()
+    torch.cuda.synchronize()
+    chunk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chunk):
+        for i in range(G):
+            fns[i % L]()
+    singles = []
+    for f in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        singles.append(g)
+
+    def run(n):
+        done = 0
+        while n - done >= G:
+            chunk.replay()
+            done += G
+        while done < n:
+            singles[done % L].replay()
+            done += 1
+
+    run(warmup)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    t0 = time.perf_counter()
+    run(steps)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3, wall, G
 
 
 class Bench:
@@ -82,46 +127,6 @@ class Bench:
         cap = max(2, int((64 << 30) // self.layer_bytes))
         return min(L, cap)
 
-    def _graph_steps(self, fns, steps, warmup):
-        """Replay `steps` calls cycling through fns (one per layer copy), in graphs of G calls."""
-        torch = self.torch
-        L = len(fns)
-        G = L * max(1, 16 // L)
-        for f in fns:                          # compile/warm every code path eagerly first
-            f()
-        torch.cuda.synchronize()
-        chunk = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(chunk):
-            for i in range(G):
-                fns[i % L]()
-        singles = []
-        for f in fns:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                f()
-            singles.append(g)
-
-        def run(n):
-            done = 0
-            while n - done >= G:
-                chunk.replay()
-                done += G
-            while done < n:
-                singles[done % L].replay()
-                done += 1
-
-        run(warmup)
-        torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        t0 = time.perf_counter()
-        run(steps)
-        end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return start.elapsed_time(end) / 1e3, wall, G
-
     def measure(self, M, steps, warmup):
         torch, synth, B, wl = self.torch, self.synth, self.B, self.wl
         x = synth.make_x(wl, M, seed=self.seed, device="cuda")
@@ -145,7 +150,7 @@ class Bench:
                                              c["w13_zeros"], c["w2"], c["w2_scales"],
                                              c["w2_zeros"], block_m=0, workspace=ws, out=out)
 
-        t_layer, wall, G = self._graph_steps([layer_fn(c) for c in self.copies[:L]], steps, warmup)
+        t_layer, wall, G = graph_replay([layer_fn(c) for c in self.copies[:L]], steps, warmup)
 
         # the dominant kernel alone: w13 grouped GEMM with the SiLU epilogue, same tiles
         st, ex, npost = B.moe_align_block_size(ti, wl.E, bm)
@@ -155,7 +160,7 @@ class Bench:
             return lambda: B.moe_wna16_gemm(x, wl.topk, c["w13"], c["w13_scales"], c["w13_zeros"],
                                             st, ex, npost, bm, M * wl.topk, act=1, C=inter)
 
-        t_g1, _, _ = self._graph_steps([gemm1_fn(c) for c in self.copies[:L]], steps, warmup)
+        t_g1, _, _ = graph_replay([gemm1_fn(c) for c in self.copies[:L]], steps, warmup)
         us_layer = t_layer / steps * 1e6
         us_g1 = t_g1 / steps * 1e6
         flops_layer = 6.0 * wl.H * wl.I * M * wl.topk
@@ -172,6 +177,62 @@ class Bench:
             active_weight_bytes=act_bytes, w13_bytes=w13_bytes,
         )
         return res, t_layer, wall, (x, lg)
+
+
+DENSE_NS = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+def _decode_uint4_fp16(qw, scales, zeros):
+    """[N, K/2] uint4 storage -> fp16 [N, K] decoded weights (q - z) * s, for the fp16 reference."""
+    import torch
+    N = qw.shape[0]
+    q = torch.stack([qw & 15, qw >> 4], dim=-1).reshape(N, -1).float()
+    z = torch.stack([zeros & 15, zeros >> 4], dim=-1).reshape(N, -1).float()
+    K = q.shape[1]
+    w = (q.view(N, K // 128, 128) - z[..., None]) * scales.float()[..., None]
+    return w.reshape(N, K).to(torch.float16).contiguous()
+
+
+def dense_sweep(steps, warmup, m=16, k=8192, seed=0):
+    """The dense uint4 g128 GEMM (moe_wna16_dense_gemm) at the small-n benchmark's shapes: m 16,
+    k 8192, fp16, n 128 ... 32768.  Time per call from graph replays cycling through copies of the
+    weights (as the layer's copies), and the weight bytes streamed per second."""
+    import torch
+
+    import synth
+    import weight_only_int4_topk_amd as B
+    out = []
+    for n in DENSE_NS:
+        d = synth.make_dense(m, n, k, 4, "fp16", seed=seed, device="cuda")
+        names = ("B", "scales", "zeros")
+        wbytes = sum(d[t].numel() * d[t].element_size() for t in names)
+        L = max(2, min(64, math.ceil(512 * MIB / wbytes) + 1))
+        copies = [d] + [{t: d[t].clone() for t in names} for _ in range(L - 1)]
+        ws_n = B.moe_wna16_dense_gemm_workspace_size(m, n, k, B.QUANT_INT4, torch.float16)
+        ws = torch.empty((max(ws_n, 256),), dtype=torch.uint8, device="cuda")
+        C = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        A = d["A"]
+        fns = [(lambda w=w: B.moe_wna16_dense_gemm(A, w["B"], w["scales"], w["zeros"],
+                                                   workspace=ws, C=C)) for w in copies]
+        t, _, _ = graph_replay(fns, steps, warmup)
+        us = t / steps * 1e6
+        gbps = wbytes / (us * 1e-6) / 1e9
+        # same-hardware reference: the plain fp16 GEMM with the weights stored decoded (torch's
+        # linear, i.e. the vendor BLAS), as the benchmark's fp16 column; weight copies rotated alike
+        w16 = _decode_uint4_fp16(d["B"], d["scales"], d["zeros"])
+        L16 = max(2, min(64, math.ceil(512 * MIB / (w16.numel() * 2)) + 1))
+        w16s = [w16] + [w16.clone() for _ in range(L16 - 1)]
+        fns16 = [(lambda w=w: torch.nn.functional.linear(A, w, out=C)) for w in w16s]
+        t16, _, _ = graph_replay(fns16, steps, warmup)
+        us16 = t16 / steps * 1e6
+        out.append({"m": m, "k": k, "n": n, "us": round(us, 2), "weight_GBps": round(gbps, 1),
+                    "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                    "split_k": ws_n // (m * n * 4) if ws_n else 1, "weight_copies": L,
+                    "fp16_gemm_us": round(us16, 2)})
+        log(f"[bench] dense {out[-1]}")
+        del copies, d, fns, A, w16, w16s, fns16
+        torch.cuda.empty_cache()
+    return out
 
 
 KERNEL_SOURCES = ("gemm.hip", "common.h", "launch.h", "api.cpp")
@@ -283,6 +344,8 @@ def main():
         cpu = cpu_baseline(bench, M, x, lg, args.cpu_tokens)
         log(f"[bench] cpu baseline: {cpu}")
 
+    dense = None if args.no_dense else dense_sweep(args.sweep_steps, max(10, args.warmup // 4))
+
     value = M * args.steps / t_layer
     line = {
         "metric": "fused-MoE w4a16 layer tokens/s + achieved HBM GB/s vs peak, M=1..4096",
@@ -306,6 +369,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "dense_w4a16": dense,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
