@@ -111,10 +111,11 @@ def test_dequant_identity_probe(dt, bits, bm):
 
 
 @pytest.mark.parametrize("dt,bits", [("fp16", 4), ("bf16", 4), ("bf16", 8)])
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 @pytest.mark.parametrize("act,weighted", [(1, False), (0, True), (0, False)])
 def test_grouped_gemm_vs_oracle(dt, bits, bm, act, weighted):
-    # block_m 32 without SiLU runs the 8-wavefront workgroup (N = 512 divides its 256 columns)
+    # block_m 32 without SiLU runs the 8-wavefront workgroup (N = 512 divides its 256 columns), as
+    # do block_m 64 and 128 with bf16 activations or int8 weights (SiLU: 512 gate columns)
     wl = synth.Workload("g", E=6, H=512, I=512, topk=3, Ms=(45,), dtype=dt, bits=bits)
     layer = synth.make_layer(wl, seed=8)
     lay = cuda_layer(layer)

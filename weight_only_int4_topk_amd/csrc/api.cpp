@@ -127,13 +127,22 @@ int pick_ntw(int act, int N, int bm, int64_t est_blocks) {
   return N % 256 == 0 ? 4 : 2;
 }
 
-// Wavefronts per workgroup: 8 for the second GEMM at block_m 32 (2 column tiles) where N divides
-// the wider workgroup.  The 8 wavefronts share one activation tile, so each issues half the
-// activation loads per weight byte of a 4-wavefront workgroup (measured on the fused layer: Mixtral
-// shape at M = 64 -2.2 %, Qwen2 shape at M = 128 -1.3 %); for the first GEMM it measured neutral
-// to slower, and it keeps 4.
-int pick_waves(int act, int N, int bm, int ntw) {
-  if (act || bm != 32 || ntw != 2) return 4;
+// Wavefronts per workgroup.  8 share one activation tile, so each issues half the activation loads
+// per weight byte of a 4-wavefront workgroup:
+//   - the second GEMM at block_m 32 (2 column tiles) where N divides the wider workgroup (measured
+//     on the fused layer: Mixtral shape at M = 64 -2.2 %, Qwen2 shape at M = 128 -1.3 %; for the
+//     first GEMM it measured neutral to slower, and it keeps 4);
+//   - both GEMMs at block_m 64 and 128 when the activations go straight from memory into LDS
+//     (bf16 activations or int8 weights), where the activation loads are two to four times the
+//     weight loads (DeepSeek-V3-shaped prefill layers: -2 to -5 %); with fp16 uint4 weights, whose
+//     activations are staged through registers, it measured 4 % slower and keeps 4.
+int pick_waves(int act, int N, int bm, int ntw, int dtype, int bits) {
+  if (ntw != 2) return 4;
+  if (bm >= 64) {
+    if (dtype != 1 && bits != 8) return 4;
+    return (act ? (N / 2) % 128 : N % 256) == 0 ? 8 : 4;
+  }
+  if (act || bm != 32) return 4;
   return N % 256 == 0 ? 8 : 4;
 }
 
@@ -179,7 +188,6 @@ int64_t estimate_active_blocks(int64_t M, int topk, int E, int bm) {
 }
 
 Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int block_m) {
-  (void)dtype;
   Plan p{};
   const int64_t slots = (int64_t)M * topk;
   p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E, bits);
@@ -189,8 +197,8 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   const int64_t est_blocks = estimate_blocks(slots, E, p.bm);
   p.ntw1 = pick_ntw(1, 2 * I, p.bm, est_blocks);
   p.ntw2 = pick_ntw(0, H, p.bm, est_blocks);
-  p.wv1 = pick_waves(1, 2 * I, p.bm, p.ntw1);
-  p.wv2 = pick_waves(0, H, p.bm, p.ntw2);
+  p.wv1 = pick_waves(1, 2 * I, p.bm, p.ntw1, dtype, bits);
+  p.wv2 = pick_waves(0, H, p.bm, p.ntw2, dtype, bits);
   // The first GEMM (K = H) keeps SiLU in its epilogue unless it has fewer workgroups than compute
   // units (few experts and a narrow I, as in a tensor-parallel share of many small experts): then
   // it is split over K into float32 partials.  Measured: with a few hundred workgroups the extra
@@ -239,7 +247,7 @@ DensePlan make_dense_plan(int M, int N, int K, int bits, int dtype) {
   int ntw = 2;
   if (bm == 16 && N % 256 == 0 && (int64_t)(N / 256) * d.nblk * std::max(1, kb_total / 4) >= 512)
     ntw = 4;
-  const int wv = pick_waves(0, N, bm, ntw);
+  const int wv = pick_waves(0, N, bm, ntw, dtype, bits);
   const int64_t wgs = (int64_t)d.nblk * (N / (ntw * 16 * wv));
   d.split = pick_split(kb_total, wgs, 4, 512);
   d.c = moe::GemmConfig{dtype, bits, bm, 0, d.split > 1 ? 1 : 0, ntw, wv};
@@ -366,7 +374,8 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   p.C = C;
   p.split_k = 1;
   const int ntw = pick_ntw(act, N, block_m, estimate_blocks(num_slots, E, block_m));
-  moe::GemmConfig c{dtype, quant->bits, block_m, act, 0, ntw, pick_waves(act, N, block_m, ntw)};
+  moe::GemmConfig c{dtype, quant->bits, block_m, act, 0, ntw,
+                    pick_waves(act, N, block_m, ntw, dtype, quant->bits)};
   if (int rc = fit_lds(K, 1, c, "gemm")) return rc;
   hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "gemm launch");

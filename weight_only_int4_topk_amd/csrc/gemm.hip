@@ -800,7 +800,9 @@ hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stre
 template <int DT, int BITS, int MT>
 hipError_t launch_mt(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
   if (MT == 1 && c.ntw == 4) return launch_ntw<DT, BITS, MT, (MT == 1 ? 4 : 2), 4>(p, c, stream);
-  if (MT == 2 && c.waves == 8) return launch_ntw<DT, BITS, MT, 2, (MT == 2 ? 8 : 4)>(p, c, stream);
+  if constexpr (MT >= 2) {
+    if (c.waves == 8) return launch_ntw<DT, BITS, MT, 2, 8>(p, c, stream);
+  }
   return launch_ntw<DT, BITS, MT, 2, 4>(p, c, stream);
 }
 
@@ -817,8 +819,11 @@ hipError_t launch_bits(const GemmParams& p, const GemmConfig& c, hipStream_t str
 
 }  // namespace
 
-// wavefronts per workgroup the launch uses (8 only where the kernel is built with 8)
-static int gemm_waves(const GemmConfig& c) { return c.waves == 8 && c.block_m == 32 ? 8 : 4; }
+// wavefronts per workgroup the launch uses (8 only where the kernel is built with 8: block_m >= 32
+// with two column tiles)
+static int gemm_waves(const GemmConfig& c) {
+  return c.waves == 8 && c.block_m >= 32 ? 8 : 4;
+}
 
 size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c) {
   if (c.bits != 4) return 0;
