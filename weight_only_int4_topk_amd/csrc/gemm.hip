@@ -129,10 +129,12 @@ __device__ __forceinline__ u32x4_t decode_u4(uint32_t w, const DecodeK& d, uint3
     b[3] = h2_sub_mul(and_or(w8, mhi, magic), d.zn2h, d.s2);
   } else {
     // bf16, natural k order (k0,k1)(k2,k3)(k4,k5)(k6,k7): every nibble in a byte of its own, one
-    // byte-to-float conversion each, then (q - z) * s exactly in one float32 fma (4-bit times 8-bit
-    // operands) and one rounding to bf16
-    const uint32_t even = w & 0x0F0F0F0Fu;
-    const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;
+    // byte-to-float conversion each (v_cvt_f32_ubyte0..3), then (q - z) * s exactly in one float32
+    // fma (4-bit times 8-bit operands) and one rounding to bf16.  The masks go through
+    // v_bitop3_b32: a plain `&` lets the compiler fold mask and byte select into a 4-bit field
+    // extract per nibble (v_bfe_u32 + v_cvt_f32_ubyte0, two instructions instead of one).
+    const uint32_t even = __builtin_amdgcn_bitop3_b32(w, 0x0F0F0F0Fu, 0u, 0xC0);       // w & m
+    const uint32_t odd = __builtin_amdgcn_bitop3_b32(w >> 4, 0x0F0F0F0Fu, 0u, 0xC0);  // (w >> 4) & m
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float q0 = (float)((even >> (8 * i)) & 0xFFu);
