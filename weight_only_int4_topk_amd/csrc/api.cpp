@@ -199,12 +199,25 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   p.ntw2 = pick_ntw(0, H, p.bm, est_blocks);
   p.wv1 = pick_waves(1, 2 * I, p.bm, p.ntw1, dtype, bits);
   p.wv2 = pick_waves(0, H, p.bm, p.ntw2, dtype, bits);
-  // The first GEMM (K = H) keeps SiLU in its epilogue unless it has fewer workgroups than compute
-  // units (few experts and a narrow I, as in a tensor-parallel share of many small experts): then
-  // it is split over K into float32 partials.  Measured: with a few hundred workgroups the extra
-  // pass costs what the split gains.
-  const int64_t wgs1 = est_blocks * (I / 64);
-  p.split1 = wgs1 < 256 ? pick_split(H / kb, wgs1, 4, 512) : 1;
+  // The first GEMM (K = H) keeps SiLU in its epilogue unless its workgroups cannot fill the chip:
+  // then it is split over K into float32 partials and a second pass applies SiLU(gate) * up.
+  //   - under 256 workgroups (few experts and a narrow I, as in a tensor-parallel share of many
+  //     small experts at M = 1): split to ~512;
+  //   - under one round of resident workgroups (~1024): split towards ~1024, keeping >= 14
+  //     k-blocks per split so the extra pass stays small against the stream (measured: DeepSeek-V3
+  //     TP share M = 16 107 -> 103 us, M = 64 199 -> 190 us, Qwen2 shape M = 1 62 -> 59 us; the
+  //     Mixtral shape at M = 1, 448 workgroups of 32 k-blocks, is 1-4 % slower split in two);
+  //   - otherwise unsplit: with more workgroups than that the extra pass costs what the split
+  //     gains (Mixtral shape at M = 16 and 64: 3-6 % slower split).
+  const int64_t blocks = estimate_active_blocks(M, topk, E, p.bm);
+  const int64_t wgs1 = blocks * (I / (p.ntw1 / 2 * 16 * p.wv1));  // unsplit SiLU workgroups
+  const int64_t wgs1_split = blocks * (I / 64);                   // per split (128 columns of 2I)
+  if (wgs1 < 256)
+    p.split1 = pick_split(H / kb, wgs1_split, 4, 512);
+  else if (wgs1 < 1024)
+    p.split1 = pick_split(H / kb, wgs1_split, 14, 1024);
+  else
+    p.split1 = 1;
   // The second GEMM (K = I) writes float32 partials anyway; split it to about two workgroups per
   // compute unit (more, shorter workgroups pay their start-up more often and write more partials)
   const int64_t wgs2 = estimate_active_blocks(M, topk, E, p.bm) * (H / (p.ntw2 * 16 * p.wv2));
