@@ -252,8 +252,14 @@ def test_fused_empty_batch():
 # ------------------------------------------------------------------------------------------------
 # full-size layers (drawn on the GPU), sampled tokens against the oracle
 # ------------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("name,M", [("mixtral", 64), ("mixtral", 1), ("qwen2", 512), ("dsv3_tp8", 256),
+# Every decode M of the workloads, so each tile plan the library picks at full size runs once:
+# BLOCK_M 16/32/64, the first GEMM unsplit, split to ~512 workgroups (DeepSeek-V3 TP share at M=1)
+# and split towards one round (TP share at M=16 and 64, Qwen2 shape at M=1), 8-wavefront workgroups.
+@pytest.mark.parametrize("name,M", [("mixtral", 64), ("mixtral", 16), ("mixtral", 4), ("mixtral", 1),
+                                    ("qwen2", 512), ("qwen2", 128), ("qwen2", 16), ("qwen2", 1),
+                                    ("dsv3_tp8", 256), ("dsv3_tp8", 64), ("dsv3_tp8", 16),
                                     ("dsv3_tp8", 1), ("dsv3_prefill_int4", 4096),
+                                    ("dsv3_prefill_int4", 1024), ("dsv3_prefill_int8", 4096),
                                     ("dsv3_prefill_int8", 1024)])
 def test_fused_full_size_sampled(name, M):
     wl = W[name]
