@@ -62,6 +62,27 @@ def test_align_exact(M, k, E, bm):
     assert np.array_equal(O.to_numpy(ex), r_ex)
 
 
+@pytest.mark.parametrize("numel,E,bm,foreign", [(64, 256, 16, False), (65, 256, 16, False),
+                                                  (32, 1024, 64, False), (6, 8, 128, False),
+                                                  (64, 64, 32, False), (1, 256, 16, False),
+                                                  (40, 16, 16, True), (64, 3, 16, True)])
+def test_align_small_batches(numel, E, bm, foreign):
+    """Up to 64 slots one wavefront aligns alone (65 takes the workgroup path): stable order,
+    experts repeated many times, ids of other shards (negative or >= E) left out."""
+    rng = np.random.default_rng(numel * 7 + E + bm)
+    ids = rng.integers(0, E, size=numel).astype(np.int32)
+    if E <= 16:
+        ids[: numel // 2] = E - 1                          # one expert takes many slots
+    if foreign:
+        ids[::5] = -1
+        ids[1::7] = E + 3
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), E, bm)
+    r_st, r_ex, r_T = O.align_block_size(ids, E, bm)
+    assert int(npost.item()) == r_T
+    assert np.array_equal(O.to_numpy(st), r_st)
+    assert np.array_equal(O.to_numpy(ex), r_ex)
+
+
 def test_align_skewed_and_foreign_ids():
     """All slots on one expert (many blocks), and ids outside [0, E) (not listed)."""
     ids = np.full((300, 2), 5, np.int32)

@@ -122,4 +122,67 @@ __device__ inline void align_body(const int32_t* __restrict__ ids, int numel, in
 }
 
 
+// The same operation for at most 64 slots by one wavefront (lane s holds slot s): no per-wave count
+// arrays and no workgroup barriers.  Lanes holding the same expert find each other with one ballot
+// per expert-id bit (a match-any): a lane's rank among them is its position in ascending slot
+// order, their number is the group size.  The lowest lane of each group writes the group's padded
+// size into pad[e] (LDS, E ints), one exclusive scan over the experts turns pad into offsets, and
+// every lane places its slot; the group's lowest lane also writes its padding and block expert ids.
+// Output identical to align_body.  ids may live in LDS or global memory.
+__device__ inline void align_one_wave(const int32_t* ids, int numel, int E, int bm, int nbits,
+                                      int32_t* __restrict__ sorted_ids,
+                                      int32_t* __restrict__ expert_ids,
+                                      int32_t* __restrict__ num_post, int64_t capacity, int* pad) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int e = lane; e < E; e += kWave) pad[e] = 0;
+  const int e = lane < numel ? ids[lane] : -1;
+  const bool valid = (unsigned)e < (unsigned)E;
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t m = __ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank = valid ? __popcll(peers & lanemask_lt(lane)) : 0;
+  const int cnt = valid ? __popcll(peers) : 0;
+  const int padded = (cnt + bm - 1) / bm * bm;
+  __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in program order
+  if (valid && rank == 0) pad[e] = padded;
+  __builtin_amdgcn_wave_barrier();
+
+  // exclusive scan of the padded sizes over experts (lane owns a contiguous run of experts)
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = min(E, lane * per);
+  const int e1 = min(E, e0 + per);
+  int local = 0;
+  for (int x = e0; x < e1; ++x) local += pad[x];
+  int inc = local;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  int run = inc - local;
+  for (int x = e0; x < e1; ++x) {
+    const int sz = pad[x];
+    pad[x] = run;
+    run += sz;
+  }
+  const int T = __shfl(inc, kWave - 1, kWave);
+  __builtin_amdgcn_wave_barrier();
+
+  if (valid) {
+    const int off = pad[e];
+    sorted_ids[off + rank] = lane;
+    if (rank == 0) {
+      for (int q = off + cnt; q < off + padded; ++q) sorted_ids[q] = numel;
+      for (int b = off / bm; b < (off + padded) / bm; ++b) expert_ids[b] = e;
+    }
+  }
+  for (int64_t q = T + lane; q < capacity; q += kWave) sorted_ids[q] = numel;
+  const int64_t nblk = (capacity + bm - 1) / bm;
+  for (int64_t b = T / bm + lane; b < nblk; b += kWave) expert_ids[b] = -1;
+  if (lane == 0) num_post[0] = T;
+}
+
 }  // namespace moe

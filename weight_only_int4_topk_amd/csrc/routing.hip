@@ -264,6 +264,25 @@ __global__ void __launch_bounds__(1024) route_align_kernel(
              &s_total);
 }
 
+// Small batches with at most 64 token-slots (M <= 4): one wavefront per token routes it, then the
+// first wavefront aligns all slots alone (align_one_wave), after one barrier of M wavefronts.
+template <int EPL>
+__global__ void __launch_bounds__(256) route_align_small_kernel(
+    const float* __restrict__ logits, int M, int E, int topk, RoutingParams p,
+    float* __restrict__ out_w, int32_t* __restrict__ out_ids, int bm, int nbits,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_post, int64_t capacity) {
+  extern __shared__ int smem[];  // pad[E], then the ids
+  __shared__ float s_score[4][EPL * kWave];
+  int32_t* s_ids = smem + E;
+  const int wid = threadIdx.x / kWave;
+  route_token<EPL>(logits + (size_t)wid * E, E, topk, p, s_score[wid],
+                   out_w + (size_t)wid * topk, out_ids + (size_t)wid * topk, s_ids + wid * topk);
+  __syncthreads();
+  if (wid == 0)
+    align_one_wave(s_ids, M * topk, E, bm, nbits, sorted_ids, expert_ids, num_post, capacity, smem);
+}
+
 template <int EPL>
 hipError_t launch_epl(const float* logits, int M, int E, int topk, const RoutingParams& p,
                       float* w, int32_t* ids, hipStream_t stream) {
@@ -279,6 +298,13 @@ hipError_t launch_ra(const float* logits, int M, int E, int topk, const RoutingP
                      int32_t* num_post, int64_t capacity, hipStream_t stream) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (M <= 4 && M * topk <= kWave) {
+    const size_t lds_small = ((size_t)E + (size_t)M * topk) * sizeof(int);
+    hipLaunchKernelGGL(route_align_small_kernel<EPL>, dim3(1), dim3(M * kWave), lds_small, stream,
+                       logits, M, E, topk, p, w, ids, block_m, nbits, sorted_ids, expert_ids,
+                       num_post, capacity);
+    return hipGetLastError();
+  }
   const size_t lds = ((size_t)(kRouteAlignWaves + 2) * E + (size_t)M * topk) * sizeof(int);
   hipLaunchKernelGGL(route_align_kernel<EPL>, dim3(1), dim3(kRouteAlignWaves * kWave), lds, stream,
                      logits, M, E, topk, p, w, ids, block_m, nbits, sorted_ids, expert_ids,
