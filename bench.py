@@ -46,7 +46,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the timed batch the CPU oracle runs (0: all of them; at the "
+                         "default workload, every activated expert decoded once, ~10-20 s)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense uint4 GEMM sweep (m 16, k 8192, n 128 ... 32768)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -265,7 +267,7 @@ def cpu_baseline(bench, M, x, lg, ntok):
 
     import oracle as O
     torch, wl = bench.torch, bench.wl
-    rows = np.arange(min(ntok, M))
+    rows = np.arange(min(ntok, M) if ntok > 0 else M)
     lg_np = O.to_numpy(lg)[rows]
     ids, _ = O.route(lg_np, wl.topk, wl.score, wl.renormalize, wl.num_groups, wl.topk_groups,
                      wl.scale)
