@@ -37,7 +37,7 @@ __all__ = [
     "GROUP", "unpack_uint4", "dequant_uint4", "dequant_int8", "dequant_bits",
     "exp_f32_spec", "sigmoid_f32_spec", "route_softmax", "route_sigmoid_grouped", "route",
     "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
-    "grouped_gemm", "dense_gemm", "to_numpy",
+    "grouped_gemm", "dense_gemm", "batched_gemm", "to_numpy",
 ]
 
 
@@ -348,3 +348,30 @@ def dense_gemm(A, qweight, scales, zeros=None):
         W = dequant_int8(to_numpy(qweight), to_numpy(scales))
     assert A64.shape[1] == W.shape[1], (A64.shape, W.shape)
     return A64 @ W.T
+
+
+def batched_gemm(A, expert_num_tokens, weight_of, act: int = 0):
+    """The grouped GEMM over activations already batched per expert, as a definition.
+
+    The int8 MoE backend listing hands the experts their activations in the BatchedExperts format
+    (select_int8_moe_backend, make_int8_moe_kernel: sized by a per-rank max_num_tokens); the pages
+    print no layout, and the reading used is the plainest one: A [E, T, K] where rows r <
+    expert_num_tokens[e] of expert e are tokens routed to it (T = max_num_tokens).  For each expert e
+    and valid row r: h = A[e, r] @ W[e]^T (float64), with act == 1 c = SiLU(h[:N/2]) * h[N/2:],
+    else c = h.  Returns {(e, r): row float64} for the valid rows only."""
+    A64 = np.asarray(to_numpy(A), dtype=np.float64)
+    counts = np.asarray(to_numpy(expert_num_tokens)).astype(np.int64)
+    E, T = A64.shape[0], A64.shape[1]
+    out = {}
+    for e in range(E):
+        n = int(min(max(counts[e], 0), T))
+        if n == 0:
+            continue
+        W = weight_of(e)
+        for r in range(n):
+            h = W @ A64[e, r]
+            if act == 1:
+                n2 = W.shape[0] // 2
+                h = silu(h[:n2]) * h[n2:]
+            out[(e, r)] = h
+    return out

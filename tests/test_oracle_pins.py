@@ -407,3 +407,40 @@ def test_dense_gemm_is_the_one_expert_grouped_gemm():
     dense = O.dense_gemm(A, qp, s[0], zp)
     for r in range(M):
         np.testing.assert_allclose(rows[r], dense[r], rtol=1e-13, atol=1e-15)
+
+
+# ---- batched-experts activation format --------------------------------------------------------
+def test_batched_gemm_is_the_grouped_gemm_of_the_same_rows():
+    """Rows of A [E, T, K] below each expert's count, routed as slots to that expert through the
+    align definition, give the same products (SiLU and plain); rows past a count are absent."""
+    rng = np.random.default_rng(21)
+    E, T, K, N = 3, 5, 256, 32
+    counts = np.array([5, 0, 2])
+    q = rng.integers(0, 16, size=(E, N, K))
+    z = rng.integers(0, 16, size=(E, N, K // 128))
+    s = rng.uniform(0.01, 0.1, size=(E, N, K // 128))
+    W = [((q[e].reshape(N, 2, 128) - z[e][..., None]) * s[e][..., None]).reshape(N, K) for e in range(E)]
+    A = rng.standard_normal((E, T, K))
+    # the same rows as slots of a grouped GEMM: slot list in (e, r) order, ids = e
+    pairs = [(e, r) for e in range(E) for r in range(counts[e])]
+    A_rows = np.stack([A[e, r] for e, r in pairs])
+    ids = np.array([e for e, _ in pairs], np.int32)
+    st, ex, Tp = O.align_block_size(ids, E, 16)
+    for act in (0, 1):
+        b = O.batched_gemm(A, counts, lambda e: W[e], act=act)
+        g = O.grouped_gemm(A_rows, 1, lambda e: W[e], st, ex, Tp, 16, len(pairs), act=act)
+        assert sorted(b) == sorted(pairs)
+        for i, pr in enumerate(pairs):
+            np.testing.assert_allclose(b[pr], g[i], rtol=1e-13, atol=1e-15)
+            # and the plain definition, written out
+            h = W[pr[0]] @ A[pr]
+            ref = h if act == 0 else (h[: N // 2] / (1 + np.exp(-h[: N // 2]))) * h[N // 2:]
+            np.testing.assert_allclose(b[pr], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_batched_gemm_counts_are_clamped_to_the_batch():
+    rng = np.random.default_rng(22)
+    A = rng.standard_normal((2, 3, 256))
+    W = [rng.standard_normal((16, 256)) for _ in range(2)]
+    out = O.batched_gemm(A, np.array([7, -1]), lambda e: W[e])
+    assert sorted(out) == [(0, 0), (0, 1), (0, 2)]
