@@ -158,6 +158,25 @@ int moe_wna16_dense_gemm(const void* A, int M, int K, const void* B, const void*
 size_t moe_wna16_dense_gemm_workspace_size(int M, int N, int K, const moe_quant_t* quant,
                                            int dtype);
 
+/* Grouped GEMM over activations already batched per expert: the BatchedExperts activation format
+ * that the int8 MoE backend listing selects for expert-parallel dispatch (select_int8_moe_backend,
+ * make_int8_moe_kernel: sized by a per-rank max_num_tokens).  The pages give no layout; the one used
+ * here is the plainest reading.  No align step: for every expert e and row r < min(
+ * expert_num_tokens[e], max_tokens):
+ *   h = A[e, r, :] . W[e]^T  (float32 accumulation of the decoded weights)
+ *   act 0: C[e, r, 0:N] = h;  act 1: C[e, r, 0:N/2] = SiLU(h[:N/2]) * h[N/2:]; rounded to dtype.
+ *   A     device dtype [E, max_tokens, K]
+ *   expert_num_tokens device int32 [E] (read on the device; negative counts as 0)
+ *   B, scales, zeros: weight storage of E experts with N rows and K columns (zeros NULL for int8)
+ *   C     device dtype [E, max_tokens, N] (act 1: N/2 columns); rows at or past an expert's count
+ *         are not written
+ *   block_m 0 = the smallest of {16, 32, 64} (int8: 128) that holds max_tokens
+ * Limits: 1 <= E <= 1024, K % 256 == 0, N % 128 == 0, the uint4 K limits of moe_wna16_gemm. */
+int moe_wna16_batched_gemm(const void* A, int E, int max_tokens, int K,
+                           const int32_t* expert_num_tokens, const void* B, const void* scales,
+                           const void* zeros, const moe_quant_t* quant, int N, int dtype,
+                           int block_m, int act, void* C, void* stream);
+
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits: the smallest of {16, 32, 64, 128} that holds 1.5x the average number of slots per active
  * expert (min(E, M*topk) experts), so a typical expert's slots share one block and its weights

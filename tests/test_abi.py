@@ -199,6 +199,31 @@ def test_dense_gemm_validation_and_workspace(lib):
     assert dense(M=0) == OK
 
 
+def test_batched_gemm_validation(lib):
+    q4 = _q(4, 128, 1)
+
+    def batched(**kw):
+        a = dict(A=FAKE, E=8, T=16, K=512, cnt=FAKE, Bw=FAKE, S=FAKE, Z=FAKE, q=q4, N=256, dt=0,
+                 bm=0, act=1, C=FAKE)
+        a.update(kw)
+        return lib.moe_wna16_batched_gemm(a["A"], a["E"], a["T"], a["K"], a["cnt"], a["Bw"], a["S"],
+                                          a["Z"], a["q"], a["N"], a["dt"], a["bm"], a["act"],
+                                          a["C"], NULL)
+
+    assert batched(E=0) == INVALID
+    assert batched(E=1025) == UNSUPPORTED
+    assert batched(T=-1) == INVALID
+    assert batched(act=2) == INVALID
+    assert batched(bm=24) == UNSUPPORTED
+    assert batched(K=384) == UNSUPPORTED
+    assert batched(N=200) == UNSUPPORTED
+    assert batched(cnt=NULL) == INVALID
+    assert batched(cnt=ctypes.c_void_p(0x100002)) == INVALID   # counts need 4-byte alignment
+    assert batched(C=ctypes.c_void_p(0x100008)) == INVALID
+    assert batched(Z=NULL) == INVALID
+    assert batched(T=0) == OK                                  # nothing to do, no launch
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(B, "_lib", None)

@@ -56,6 +56,8 @@ _SIGS = {
                               ctypes.c_size_t, _P, _P], _I),
     "moe_wna16_dense_gemm_workspace_size": ([_I, _I, _I, ctypes.POINTER(MoeQuant), _I],
                                             ctypes.c_size_t),
+    "moe_wna16_batched_gemm": ([_P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I,
+                                _I, _I, _P, _P], _I),
     "fused_moe_wna16_workspace_size": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I],
                                        ctypes.c_size_t),
     "fused_moe_wna16": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P, _P,
@@ -189,6 +191,21 @@ def moe_wna16_dense_gemm(A, B, scales, zeros=None, workspace=None, C=None, strea
                                       ctypes.byref(quant), N, _dtype_code(A.dtype),
                                       _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                       _ptr(C), _stream(stream)))
+    return C
+
+
+def moe_wna16_batched_gemm(A, expert_num_tokens, B, scales, zeros=None, act=0, block_m=0, C=None,
+                           stream=None):
+    """C [E, T, N or N/2] from A [E, T, K] batched per expert (rows below expert_num_tokens[e])."""
+    quant = _quant_of(B, zeros)
+    E, T, K = A.shape
+    N = B.shape[1]
+    if C is None:
+        C = torch.empty((E, T, N // 2 if act == 1 else N), dtype=A.dtype, device=A.device)
+    _check(lib().moe_wna16_batched_gemm(_ptr(A), E, T, K, _ptr(expert_num_tokens), _ptr(B),
+                                        _ptr(scales), _ptr(zeros), ctypes.byref(quant), N,
+                                        _dtype_code(A.dtype), block_m, act, _ptr(C),
+                                        _stream(stream)))
     return C
 
 

@@ -447,6 +447,66 @@ int moe_wna16_dense_gemm(const void* A, int M, int K, const void* B, const void*
   return MOE_OK;
 }
 
+int moe_wna16_batched_gemm(const void* A, int E, int max_tokens, int K,
+                           const int32_t* expert_num_tokens, const void* B, const void* scales,
+                           const void* zeros, const moe_quant_t* quant, int N, int dtype,
+                           int block_m, int act, void* C, void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (int rc = check_quant(quant)) return rc;
+  if (E <= 0 || max_tokens < 0 || K <= 0 || N <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "E=%d max_tokens=%d K=%d N=%d", E, max_tokens, K, N);
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 1024", E);
+  if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL)
+    return fail(MOE_ERR_INVALID_ARG, "act = %d", act);
+  if (block_m != 0 && !valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128)", block_m);
+  if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
+  if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
+  const int64_t rows = (int64_t)E * max_tokens;
+  if (rows * K * 2 >= ((int64_t)1 << 31) || rows * N * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)N * (quant->bits == 4 ? K / 2 : K) >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "A, C or one expert's weights exceed 2 GiB");
+  if (int rc = check_weights(B, scales, zeros, quant)) return rc;
+  if (max_tokens == 0) return MOE_OK;
+  if (!A || !C || !expert_num_tokens) return fail(MOE_ERR_INVALID_ARG, "NULL A / C / counts");
+  if (!aligned(A, 16) || !aligned(C, 16) || !aligned(expert_num_tokens, 4))
+    return fail(MOE_ERR_INVALID_ARG, "A and C need 16-byte, counts 4-byte alignment");
+  // rows per block: the smallest of {16, 32, 64} (int8: 128) that holds a full batch, so an expert
+  // with a full batch streams its weights once
+  int bm = block_m;
+  if (bm == 0) {
+    bm = 16;
+    const int top = quant->bits == 4 ? 64 : 128;
+    while (bm < max_tokens && bm < top) bm *= 2;
+  }
+  const int bpe = (max_tokens + bm - 1) / bm;
+  const int64_t nblk = (int64_t)E * bpe;
+  const int ntw = pick_ntw(act, N, bm, nblk);
+  moe::GemmConfig c{dtype, quant->bits, bm, act, 0, ntw,
+                    pick_waves(act, N, bm, ntw, dtype, quant->bits)};
+  if (int rc = fit_lds(K, 1, c, "batched gemm")) return rc;
+  moe::GemmParams p{};
+  p.A = A;
+  p.num_a_rows = (int)rows;
+  p.a_row_div = 1;
+  p.B = (const uint8_t*)B;
+  p.scales = scales;
+  p.zeros = (const uint8_t*)zeros;
+  p.E = E;
+  p.N = N;
+  p.K = K;
+  p.num_blocks = (int)nblk;
+  p.num_slots = (int)rows;
+  p.C = C;
+  p.split_k = 1;
+  p.batched = 1;
+  p.expert_counts = expert_num_tokens;
+  p.max_tokens = max_tokens;
+  p.bpe = bpe;
+  hipError_t e = moe::launch_gemm(p, c, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "batched gemm launch");
+}
+
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
                                       const moe_quant_t* quant, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || !quant) return 0;

@@ -332,11 +332,27 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   bid /= split;
   const int nc = bid % n_chunks;
   const int blk = bid / n_chunks;
-  // dense: rows are slots 0..num_slots-1 in order, one expert, no align arrays
-  if (blk * BM >= (p.dense ? p.num_slots : p.num_post[0])) return;
-  const int e = p.dense ? 0 : p.expert_ids[blk];
+  // Row maps.  Aligned: slots listed by sorted_ids, expert per block from expert_ids.  Dense: rows
+  // are slots 0..num_slots-1 in order, one expert.  Batched: block blk covers rows j*BM.. of expert
+  // blk / bpe (j = blk % bpe), slot = row index e * max_tokens + j*BM + r, valid below the expert's
+  // count (clamped to max_tokens).
+  int e, n_valid = 0, brow0 = 0;
+  if (p.batched) {
+    e = blk / p.bpe;
+    const int j = blk - e * p.bpe;
+    n_valid = min(p.expert_counts[e], p.max_tokens) - j * BM;
+    if (n_valid <= 0) return;
+    brow0 = e * p.max_tokens + j * BM;
+  } else {
+    if (blk * BM >= (p.dense ? p.num_slots : p.num_post[0])) return;
+    e = p.dense ? 0 : p.expert_ids[blk];
+  }
   if ((unsigned)e >= (unsigned)p.E) return;
   auto slot_at = [&](int i) -> int {
+    if (p.batched) {
+      const int r = i - blk * BM;
+      return r < n_valid ? brow0 + r : -1;
+    }
     return p.dense ? (i < p.num_slots ? i : -1) : p.sorted_ids[i];
   };
 

@@ -47,6 +47,12 @@ struct GemmParams {
   int split_k;                // K split count (out_f32 only, else 1)
   int dense;                  // 1: slot r of block b is row b * block_m + r (< num_slots), expert
                               // 0; sorted_ids, expert_ids and num_post are not read
+  int batched;                // 1: A and C hold E blocks of max_tokens rows; block b covers rows
+                              // (b % bpe) * block_m .. of expert b / bpe, valid below
+                              // min(expert_counts[e], max_tokens); align arrays are not read
+  const int32_t* expert_counts;
+  int max_tokens;
+  int bpe;                    // blocks per expert: ceil(max_tokens / block_m)
   uint32_t dec_mask;          // set by launch_gemm: low nibble-pair mask of the decode
   uint32_t dec_mask_hi;       // set by launch_gemm: high nibble-pair mask (fp16 uint4 decode)
   uint32_t dec_magic;         // set by launch_gemm: magic bias in both 16-bit halves
