@@ -10,8 +10,9 @@ that hold several consecutive layer calls.
 
 Also reported: the roofline of the dominant kernel (the w13 grouped GEMM with the SiLU epilogue),
 timed alone with HIP events on the stream it is launched on; an M sweep of the workload; the CPU
-oracle's throughput on a bounded sample of the same batch; and the dense uint4 GEMM at the small-n
-benchmark's shapes (m 16, k 8192, n 128 ... 32768).
+oracle's throughput on a bounded sample of the same batch; the dense uint4 GEMM at the small-n
+benchmark's shapes (m 16, k 8192, n 128 ... 32768); and the grouped GEMM over batched-experts
+activations on an expert-parallel share of 32 DeepSeek-V3-shaped experts.
 """
 from __future__ import annotations
 
@@ -51,6 +52,8 @@ def parse():
                          "default workload, every activated expert decoded once, ~10-20 s)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense uint4 GEMM sweep (m 16, k 8192, n 128 ... 32768)")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batched-experts GEMM sweep (expert-parallel share, 32 experts)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device-to-device copy (known bytes) so that "
                          "profiler traffic counters can be scaled")
@@ -237,6 +240,42 @@ def dense_sweep(steps, warmup, m=16, k=8192, seed=0):
     return out
 
 
+def batched_sweep(steps, warmup, E=32, H=7168, I=2048, Ts=(8, 64), seed=0):
+    """moe_wna16_batched_gemm on an expert-parallel share of the DeepSeek-V3 expert shape (32 local
+    experts of H 7168, I 2048, uint4 g128, bf16), every expert with a full batch of T tokens: the w13
+    GEMM with SiLU and the w2 GEMM, time per call from graph replays over rotated weight copies, and
+    the weight bytes streamed per second."""
+    import torch
+
+    import synth
+    import weight_only_int4_topk_amd as B
+    wl = synth.Workload("ep_share", E=E, H=H, I=I, topk=1, Ms=(1,), dtype="bf16", bits=4)
+    layer = synth.make_layer(wl, seed=seed, device="cuda")
+    wb = {n: sum(layer[n + t].numel() * layer[n + t].element_size() for t in ("", "_scales", "_zeros"))
+          for n in ("w13", "w2")}
+    L = max(2, min(64, math.ceil(512 * MIB / wb["w13"]) + 1))
+    copies = [layer] + [{k: v.clone() for k, v in layer.items()} for _ in range(L - 1)]
+    out = []
+    for T in Ts:
+        cnt = torch.full((E,), T, dtype=torch.int32, device="cuda")
+        x = (torch.randn((E, T, H), device="cuda") * 0.1).to(torch.bfloat16)
+        h = torch.empty((E, T, I), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((E, T, H), dtype=torch.bfloat16, device="cuda")
+        f13 = [(lambda c=c: B.moe_wna16_batched_gemm(x, cnt, c["w13"], c["w13_scales"], c["w13_zeros"],
+                                                     act=1, C=h)) for c in copies]
+        f2 = [(lambda c=c: B.moe_wna16_batched_gemm(h, cnt, c["w2"], c["w2_scales"], c["w2_zeros"],
+                                                    act=0, C=y)) for c in copies]
+        t13 = graph_replay(f13, steps, warmup)[0] / steps * 1e6
+        t2 = graph_replay(f2, steps, warmup)[0] / steps * 1e6
+        out.append({"experts": E, "tokens_per_expert": T, "w13_us": round(t13, 2),
+                    "w13_GBps": round(wb["w13"] / (t13 * 1e-6) / 1e9, 1), "w2_us": round(t2, 2),
+                    "w2_GBps": round(wb["w2"] / (t2 * 1e-6) / 1e9, 1), "weight_copies": L})
+        log(f"[bench] batched {out[-1]}")
+    del copies, layer
+    torch.cuda.empty_cache()
+    return out
+
+
 KERNEL_SOURCES = ("gemm.hip", "common.h", "launch.h", "api.cpp")
 
 
@@ -347,6 +386,7 @@ def main():
         log(f"[bench] cpu baseline: {cpu}")
 
     dense = None if args.no_dense else dense_sweep(args.sweep_steps, max(10, args.warmup // 4))
+    batched = None if args.no_batched else batched_sweep(args.sweep_steps, max(10, args.warmup // 4))
 
     value = M * args.steps / t_layer
     line = {
@@ -372,6 +412,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "dense_w4a16": dense,
+        "batched_experts": batched,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
