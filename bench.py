@@ -143,7 +143,7 @@ class Bench:
         w13_bytes = active * synth.w13_bytes_per_expert(wl)
         L = self.n_copies(act_bytes)
         self.ensure_copies(L)
-        bm = B.moe_pick_block_m(M, wl.E, wl.topk, wl.bits)
+        bm = B.moe_pick_block_m(M, wl.E, wl.topk, wl.bits, wl.torch_dtype)
         quant = B.QUANT_INT4 if wl.bits == 4 else B.QUANT_INT8
         ws = torch.empty((B.fused_moe_wna16_workspace_size(M, wl.H, wl.I, wl.E, wl.topk, quant,
                                                            wl.torch_dtype, 0),),

@@ -48,7 +48,7 @@ _SIGS = {
     "moe_last_error": ([], ctypes.c_char_p),
     "moe_topk_softmax": ([_P, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P], _I),
     "moe_align_capacity": ([_I, _I, _I], _I64),
-    "moe_pick_block_m": ([_I, _I, _I, _I], _I),
+    "moe_pick_block_m": ([_I, _I, _I, _I, _I], _I),
     "moe_align_block_size": ([_P, _I, _I, _I, _P, _P, _P, _I64, _P], _I),
     "moe_wna16_gemm": ([_P, _I, _I, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _I, _I,
                         _P, _P, _P, _I64, _I, _I, _P, _I, _P, _P], _I),
@@ -136,8 +136,9 @@ def moe_topk_softmax(logits, topk, rt: MoeRouting, topk_weights=None, topk_ids=N
     return topk_weights, topk_ids
 
 
-def moe_pick_block_m(M, E, topk, bits=4) -> int:
-    return int(lib().moe_pick_block_m(M, E, topk, bits))
+def moe_pick_block_m(M, E, topk, bits=4, dtype=torch.float16) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().moe_pick_block_m(M, E, topk, bits, code))
 
 
 def moe_align_capacity(numel, E, block_m) -> int:

@@ -102,16 +102,20 @@ struct Plan {
 
 // uint4 stops at 64: the fp16 128-row kernel stages activations through registers and runs at two
 // wavefronts per SIMD (Qwen2-shaped layer at M = 512: GEMMs 798 us at 128 rows, 497 us at 64); in
-// bf16 the two are within a few percent (DeepSeek-V3 expert at M = 4096).  int8 keeps 128.
-int pick_block_m(int M, int topk, int E, int bits) {
+// bf16 the two are within a few percent (DeepSeek-V3 expert at M = 4096).  int8 keeps 128.  fp16
+// uint4 where 64 rows would be picked for up to 128 needed: 32 rows (the fp16 64-row kernel also
+// stages activations through registers; Qwen2 shape at M = 512, ~72 slots per expert: 555 -> 529
+// us per layer; bf16 and int8 measured equal or slower at 32).
+int pick_block_m(int M, int topk, int E, int bits, int dtype) {
   const int64_t slots = (int64_t)M * topk;
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, slots));
   const int64_t avg = (slots + active - 1) / active;
   const int64_t need = avg + avg / 2;
   const int top = bits == 4 ? 64 : 128;
-  for (int bm : {16, 32, 64})
+  for (int bm : {16, 32})
     if (need <= bm) return bm;
-  return top;
+  if (bits == 4 && dtype == MOE_DTYPE_FP16 && need <= 128) return 32;
+  return need <= 64 ? 64 : top;
 }
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -190,7 +194,7 @@ int64_t estimate_active_blocks(int64_t M, int topk, int E, int bm) {
 Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int block_m) {
   Plan p{};
   const int64_t slots = (int64_t)M * topk;
-  p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E, bits);
+  p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E, bits, dtype);
   p.cap = align_capacity(slots, E, p.bm);
   p.nblk = (int)((p.cap + p.bm - 1) / p.bm);
   const int kb = bits == 4 ? 128 : 64;
@@ -274,9 +278,10 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
 
-int moe_pick_block_m(int M, int E, int topk, int bits) {
+int moe_pick_block_m(int M, int E, int topk, int bits, int dtype) {
   if (M <= 0 || E <= 0 || topk <= 0 || (bits != 4 && bits != 8)) return -1;
-  return pick_block_m(M, topk, E, bits);
+  if (dtype != MOE_DTYPE_FP16 && dtype != MOE_DTYPE_BF16) return -1;
+  return pick_block_m(M, topk, E, bits, dtype);
 }
 
 int64_t moe_align_capacity(int numel, int E, int block_m) {
