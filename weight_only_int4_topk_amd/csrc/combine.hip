@@ -80,6 +80,53 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   *(uint2*)(out + (size_t)m * H + c) = make_uint2(lo, hi);
 }
 
+// Few tokens with many partial terms (k * split >= 16, as at M = 1 where the second GEMM is split
+// 5-16 ways): the plain kernel leaves most lanes idle and walks the terms in dependent batches.
+// Here four wavefronts cover 256 columns of one token, wavefront q summing the q-th quarter of the
+// (slot, split) terms (slot-major, each term times its slot's routing weight) in one batch of
+// loads, and the quarters are added in LDS in wavefront order: ((q0 + q1) + q2) + q3.  A fixed
+// order, so the layer stays bitwise deterministic.
+template <int DT>
+__global__ void __launch_bounds__(256) combine_quarters_kernel(const float* __restrict__ partial,
+                                                               int split, size_t split_stride,
+                                                               const float* __restrict__ topk_w,
+                                                               int topk, int H,
+                                                               uint16_t* __restrict__ out) {
+  __shared__ floatx4_t s_q[3][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int q = threadIdx.x / kWave;
+  const int cpb = H / 256;
+  const int m = blockIdx.x / cpb;
+  const int c = (blockIdx.x - m * cpb) * 256 + lane * 4;
+  const int n = topk * split;
+  const int t0 = q * n / 4, t1 = (q + 1) * n / 4;
+  const size_t slot0 = (size_t)m * topk;
+  const float* src = partial + slot0 * H + c;
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int b = t0; b < t1; b += kBatch) {
+    floatx4_t t[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int k = b + i;
+      if (k < t1) {
+        const int j = k / split;
+        t[i] = *(const floatx4_t*)(src + (size_t)j * H + (size_t)(k - j * split) * split_stride);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int k = b + i;
+      if (k < t1) acc += topk_w[slot0 + k / split] * t[i];
+    }
+  }
+  if (q > 0) s_q[q - 1][lane] = acc;
+  __syncthreads();
+  if (q == 0) {
+    acc = ((acc + s_q[0][lane]) + s_q[1][lane]) + s_q[2][lane];
+    store4<DT>(out + (size_t)m * H + c, acc);
+  }
+}
+
 // First GEMM split over K: inter[s, i] = SiLU(g) * u with g = sum_z partial[z, s, i] and
 // u = sum_z partial[z, s, I + i] (z ascending), rounded to dtype; four columns per thread.
 template <int DT>
@@ -147,6 +194,17 @@ hipError_t launch_act_combine(const float* partial, int split, int slots, int I,
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (topk * split >= 16 && H % 256 == 0 && (int64_t)M * (H / 256) <= 1024) {
+    const unsigned grid = (unsigned)(M * (H / 256));
+    const size_t stride = (size_t)M * topk * H;
+    if (dtype == 0)
+      hipLaunchKernelGGL(combine_quarters_kernel<0>, dim3(grid), dim3(256), 0, stream, partial,
+                         split, stride, topk_w, topk, H, (uint16_t*)out);
+    else
+      hipLaunchKernelGGL(combine_quarters_kernel<1>, dim3(grid), dim3(256), 0, stream, partial,
+                         split, stride, topk_w, topk, H, (uint16_t*)out);
+    return hipGetLastError();
+  }
   const size_t total = (size_t)M * (H / 4);
   const unsigned grid = (unsigned)((total + 255) / 256);
   const size_t stride = (size_t)M * topk * H;
