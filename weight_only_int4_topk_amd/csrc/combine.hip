@@ -139,8 +139,31 @@ __global__ void __launch_bounds__(256) act_combine_kernel(const float* __restric
   const int s = (int)(idx / i4);
   const int c = (int)(idx - (size_t)s * i4) * 4;
   const float* src = partial + (size_t)s * 2 * I + c;
-  const floatx4_t g = sum_splits(src, split, split_stride);
-  const floatx4_t u = sum_splits(src + I, split, split_stride);
+  floatx4_t g, u;
+  if (split <= kBatch) {
+    // gate and up partials in one batch of loads (one memory round trip instead of two), summed
+    // in the order of sum_splits (z ascending), so the result is unchanged
+    floatx4_t tg[kBatch], tu[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (q < split) {
+        tg[q] = *(const floatx4_t*)(src + (size_t)q * split_stride);
+        tu[q] = *(const floatx4_t*)(src + I + (size_t)q * split_stride);
+      }
+    }
+    g = tg[0];
+    u = tu[0];
+#pragma unroll
+    for (int q = 1; q < kBatch; ++q) {
+      if (q < split) {
+        g = g + tg[q];
+        u = u + tu[q];
+      }
+    }
+  } else {
+    g = sum_splits(src, split, split_stride);
+    u = sum_splits(src + I, split, split_stride);
+  }
   floatx4_t a;
 #pragma unroll
   for (int q = 0; q < 4; ++q) a[q] = g[q] / (1.0f + __expf(-g[q])) * u[q];
