@@ -37,7 +37,8 @@ __all__ = [
     "GROUP", "unpack_uint4", "dequant_uint4", "dequant_int8", "dequant_bits",
     "exp_f32_spec", "sigmoid_f32_spec", "route_softmax", "route_sigmoid_grouped", "route",
     "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
-    "grouped_gemm", "dense_gemm", "batched_gemm", "to_numpy",
+    "grouped_gemm", "dense_gemm", "batched_gemm", "quant_int8_rows", "w8a8_grouped_gemm",
+    "to_numpy",
 ]
 
 
@@ -375,3 +376,61 @@ def batched_gemm(A, expert_num_tokens, weight_of, act: int = 0):
                 h = silu(h[:n2]) * h[n2:]
             out[(e, r)] = h
     return out
+
+
+def quant_int8_rows(x):
+    """Dynamic symmetric int8 quantisation with one scale per row (per token), as a definition.
+
+    The int8 MoE backend listing pairs int8 weights with activations quantised per token at run time
+    (activation key kInt8DynamicTokenSym; int8_w8a8_moe_quant_config with per_act_token_quant); the
+    pages print no formula, and the reading used is the plain symmetric one, in float32 (the
+    precision the codes are decided in on the GPU): s = max|x_row| / 127 (one correctly rounded
+    division), q = clamp(rint(x / s), -127, 127) with rint = round half to even; a row of zeros has
+    s = 0 and q = 0.  x [R, K] (any float dtype) -> (q int8 [R, K], s float32 [R])."""
+    x32 = np.asarray(to_numpy(x), dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    s = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32)
+    q = np.zeros(x32.shape, np.int8)
+    nz = s > 0
+    if nz.any():
+        r = np.rint(x32[nz] / s[nz][:, None])          # float32 division, then round half to even
+        q[nz] = np.clip(r, -127, 127).astype(np.int8)
+    return q, s
+
+
+def w8a8_grouped_gemm(Aq, a_scales, a_row_div: int, w_of, sorted_token_ids, expert_ids,
+                      num_tokens_post_padded, block_m: int, num_slots: int, topk_weights=None,
+                      act: int = 0):
+    """The grouped GEMM with int8 activations and int8 weights, as a definition.
+
+    For every listed slot s (as in grouped_gemm): row = s // a_row_div, e = the block's expert,
+    h[n] = (sum_k Aq[row, k] * qw[e, n, k]) * a_scales[row] * w_scales[e, n] (the integer sum is exact;
+    float64 afterwards); act == 1: SiLU(h[:N/2]) * h[N/2:]; times topk_weights[s] if given.
+    w_of(e) -> (qw int8 [N, K], w_scales [N]).  Returns {slot: row float64}."""
+    Aq = np.asarray(to_numpy(Aq)).astype(np.int64)
+    sa = np.asarray(to_numpy(a_scales), dtype=np.float64)
+    st = np.asarray(sorted_token_ids)
+    ex = np.asarray(expert_ids)
+    tw = None if topk_weights is None else np.asarray(to_numpy(topk_weights), np.float64).reshape(-1)
+    out = {}
+    cache = {}
+    for p in range(int(num_tokens_post_padded)):
+        s = int(st[p])
+        if s >= num_slots:
+            continue
+        e = int(ex[p // block_m])
+        if e not in cache:
+            qw, ws = w_of(e)
+            cache[e] = (np.asarray(to_numpy(qw)).astype(np.int64),
+                        np.asarray(to_numpy(ws), dtype=np.float64))
+        qw, ws = cache[e]
+        row = s // a_row_div
+        h = (qw @ Aq[row]).astype(np.float64) * sa[row] * ws
+        if act == 1:
+            n2 = qw.shape[0] // 2
+            h = silu(h[:n2]) * h[n2:]
+        if tw is not None:
+            h = h * tw[s]
+        out[s] = h
+    return out
+

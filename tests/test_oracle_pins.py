@@ -444,3 +444,57 @@ def test_batched_gemm_counts_are_clamped_to_the_batch():
     W = [rng.standard_normal((16, 256)) for _ in range(2)]
     out = O.batched_gemm(A, np.array([7, -1]), lambda e: W[e])
     assert sorted(out) == [(0, 0), (0, 1), (0, 2)]
+
+
+# ---- w8a8: per-token int8 activations, per-channel int8 weights ---------------------------------
+def test_quant_int8_rows_error_bound_and_range():
+    """|q * s - x| <= s / 2 for every element (round to nearest), codes in [-127, 127], the row
+    maximum maps to +-127, and a zero row gives zero codes and scale 0."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((9, 512)) * 0.1).astype(np.float32)
+    x[3] = 0.0
+    q, s = O.quant_int8_rows(x)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    assert s[3] == 0 and not q[3].any()
+    for r in range(9):
+        if r == 3:
+            continue
+        err = np.abs(q[r].astype(np.float64) * s[r] - x[r].astype(np.float64))
+        assert (err <= s[r] / 2 * (1 + 1e-6)).all()
+        assert np.abs(q[r]).max() == 127
+
+
+def test_quant_int8_rows_on_grid_is_exact():
+    """Rows that are integer multiples of a power-of-two step, with the extreme at 127 steps,
+    come back as exactly those integers."""
+    rng = np.random.default_rng(32)
+    codes = rng.integers(-127, 128, size=(4, 256))
+    codes[:, 0] = 127
+    step = np.float32(2.0 ** -9)
+    x = (codes * step).astype(np.float32)
+    q, s = O.quant_int8_rows(x)
+    assert np.array_equal(q, codes.astype(np.int8))
+    assert np.all(s == np.float32(127 * step) / np.float32(127))
+
+
+def test_w8a8_grouped_gemm_is_the_scaled_integer_product():
+    """Against the products written out per slot with integer dot products, on a tiny routed
+    batch; a non-square weight so a transposed operand fails."""
+    rng = np.random.default_rng(33)
+    E, N, K, M, k = 3, 24, 256, 5, 2
+    qw = rng.integers(-127, 128, size=(E, N, K)).astype(np.int8)
+    ws = rng.uniform(0.001, 0.01, size=(E, N))
+    x = (rng.standard_normal((M, K)) * 0.1).astype(np.float32)
+    Aq, sa = O.quant_int8_rows(x)
+    ids = np.array([[0, 2], [1, 2], [2, 0], [1, 0], [2, 1]], np.int32)
+    st, ex, T = O.align_block_size(ids, E, 16)
+    for act in (0, 1):
+        got = O.w8a8_grouped_gemm(Aq, sa, k, lambda e: (qw[e], ws[e]), st, ex, T, 16, M * k, act=act)
+        for s in range(M * k):
+            e, row = ids.reshape(-1)[s], s // k
+            h = np.array([float(sum(int(a) * int(b) for a, b in zip(Aq[row], qw[e, n])))
+                          for n in range(N)]) * float(sa[row]) * ws[e]
+            if act:
+                h = h[: N // 2] / (1 + np.exp(-h[: N // 2])) * h[N // 2:]
+            np.testing.assert_allclose(got[s], h, rtol=1e-13, atol=1e-15)
