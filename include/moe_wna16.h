@@ -177,6 +177,35 @@ int moe_wna16_batched_gemm(const void* A, int E, int max_tokens, int K,
                            const void* zeros, const moe_quant_t* quant, int N, int dtype,
                            int block_m, int act, void* C, void* stream);
 
+/* w8a8: the int8 MoE backend listing pairs int8 weights with one symmetric scale per output
+ * channel (kInt8StaticChannelSym) with activations quantised per token at run time
+ * (kInt8DynamicTokenSym; int8_w8a8_moe_quant_config with per_act_token_quant).  The pages print no
+ * formula; the one used is the plain symmetric quantisation, decided in float32.
+ *
+ * moe_quant_int8_rows: for each row of x (device dtype [rows, K]):
+ *   scales[row] = max_k |x[row, k]| / 127 (one correctly rounded float32 division),
+ *   q[row, k] = clamp(rint(x[row, k] / scales[row]), -127, 127), rint = round half to even;
+ *   a row of zeros gets scale 0 and codes 0.
+ *   q device int8 [rows, K]; scales device float [rows].  Limits: K % 256 == 0. */
+int moe_quant_int8_rows(const void* x, int rows, int K, int dtype, int8_t* q, float* scales,
+                        void* stream);
+
+/* moe_w8a8_gemm: the grouped GEMM of moe_wna16_gemm with int8 activations, on the integer matrix
+ * cores.  For every listed slot s (row = s / a_row_div, e = the block's expert):
+ *   h[n] = (sum_k A[row, k] * B[e, n, k]) * a_scales[row] * w_scales[e, n]  (exact integer sum)
+ *   act 0: C[s, 0:N] = h;  act 1: C[s, 0:N/2] = SiLU(h[:N/2]) * h[N/2:]; times topk_weights[s] if
+ *   not NULL; rounded to dtype.
+ *   A        device int8 [num_a_rows, K], a_scales device float [num_a_rows] (moe_quant_int8_rows)
+ *   B        device int8 [E, N, K], w_scales device dtype [E, N] (the int8 weight storage above)
+ *   sorted_token_ids / expert_ids / num_tokens_post_padded: moe_align_block_size with block_m
+ * Rows of C whose slot is not listed are not written.
+ * Limits: block_m in {16, 32, 64}, K % 256 == 0, N % 128 == 0. */
+int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_row_div,
+                  const int8_t* B, const void* w_scales, int E, int N, int K, int dtype,
+                  const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                  const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
+                  int num_slots, const float* topk_weights, int act, void* C, void* stream);
+
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits and activations of `dtype`: the smallest of {16, 32, 64, 128} that holds 1.5x the average
  * number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots share one

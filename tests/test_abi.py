@@ -231,6 +231,32 @@ def test_batched_gemm_validation(lib):
     assert batched(T=0) == OK                                  # nothing to do, no launch
 
 
+def test_w8a8_validation(lib):
+    assert lib.moe_quant_int8_rows(FAKE, 4, 300, 0, FAKE, FAKE, NULL) == UNSUPPORTED  # K % 256
+    assert lib.moe_quant_int8_rows(FAKE, 4, 256, 2, FAKE, FAKE, NULL) == UNSUPPORTED  # dtype
+    assert lib.moe_quant_int8_rows(FAKE, -1, 256, 0, FAKE, FAKE, NULL) == INVALID
+    assert lib.moe_quant_int8_rows(FAKE, 4, 256, 0, NULL, FAKE, NULL) == INVALID
+    assert lib.moe_quant_int8_rows(FAKE, 0, 256, 0, NULL, NULL, NULL) == OK         # no rows
+
+    def w8(**kw):
+        a = dict(A=FAKE, sa=FAKE, rows=32, div=2, Bw=FAKE, ws=FAKE, E=8, N=1024, K=256, dt=0,
+                 st=FAKE, ex=FAKE, npost=FAKE, cap=152, bm=16, slots=32, tw=NULL, act=1, C=FAKE)
+        a.update(kw)
+        return lib.moe_w8a8_gemm(a["A"], a["sa"], a["rows"], a["div"], a["Bw"], a["ws"], a["E"],
+                                 a["N"], a["K"], a["dt"], a["st"], a["ex"], a["npost"], a["cap"],
+                                 a["bm"], a["slots"], a["tw"], a["act"], a["C"], NULL)
+
+    assert w8(bm=128) == UNSUPPORTED
+    assert w8(K=320) == UNSUPPORTED
+    assert w8(N=1000) == UNSUPPORTED
+    assert w8(act=3) == INVALID
+    assert w8(rows=15) == INVALID                               # 15 rows * 2 < 32 slots
+    assert w8(sa=NULL) == INVALID
+    assert w8(A=ctypes.c_void_p(0x100008)) == INVALID
+    assert w8(dt=5) == UNSUPPORTED
+    assert w8(slots=0) == OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(B, "_lib", None)

@@ -56,6 +56,9 @@ _SIGS = {
                               ctypes.c_size_t, _P, _P], _I),
     "moe_wna16_dense_gemm_workspace_size": ([_I, _I, _I, ctypes.POINTER(MoeQuant), _I],
                                             ctypes.c_size_t),
+    "moe_quant_int8_rows": ([_P, _I, _I, _I, _P, _P, _P], _I),
+    "moe_w8a8_gemm": ([_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I64, _I, _I, _P, _I,
+                       _P, _P], _I),
     "moe_wna16_batched_gemm": ([_P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I,
                                 _I, _I, _P, _P], _I),
     "fused_moe_wna16_workspace_size": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I],
@@ -207,6 +210,33 @@ def moe_wna16_batched_gemm(A, expert_num_tokens, B, scales, zeros=None, act=0, b
                                         _ptr(scales), _ptr(zeros), ctypes.byref(quant), N,
                                         _dtype_code(A.dtype), block_m, act, _ptr(C),
                                         _stream(stream)))
+    return C
+
+
+def moe_quant_int8_rows(x, q=None, scales=None, stream=None):
+    """(q int8 [R, K], scales float [R]) = per-row symmetric int8 of x [R, K] (fp16/bf16)."""
+    R, K = x.shape
+    if q is None:
+        q = torch.empty((R, K), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R,), dtype=torch.float32, device=x.device)
+    _check(lib().moe_quant_int8_rows(_ptr(x), R, K, _dtype_code(x.dtype), _ptr(q), _ptr(scales),
+                                     _stream(stream)))
+    return q, scales
+
+
+def moe_w8a8_gemm(Aq, a_scales, a_row_div, B, w_scales, sorted_ids, expert_ids, num_post, block_m,
+                  num_slots, dtype, topk_weights=None, act=0, C=None, stream=None):
+    """Grouped GEMM of int8 activations (per-row scales) with int8 weights (per-channel scales)."""
+    E, N, K = B.shape
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    if C is None:
+        C = torch.empty((num_slots, N // 2 if act == 1 else N),
+                        dtype=torch.float16 if code == 0 else torch.bfloat16, device=Aq.device)
+    _check(lib().moe_w8a8_gemm(_ptr(Aq), _ptr(a_scales), Aq.shape[0], a_row_div, _ptr(B),
+                               _ptr(w_scales), E, N, K, code, _ptr(sorted_ids), _ptr(expert_ids),
+                               _ptr(num_post), sorted_ids.numel(), block_m, num_slots,
+                               _ptr(topk_weights), act, _ptr(C), _stream(stream)))
     return C
 
 

@@ -512,6 +512,72 @@ int moe_wna16_batched_gemm(const void* A, int E, int max_tokens, int K,
   return e == hipSuccess ? MOE_OK : hip_fail(e, "batched gemm launch");
 }
 
+int moe_quant_int8_rows(const void* x, int rows, int K, int dtype, int8_t* q, float* scales,
+                        void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (rows < 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "rows=%d K=%d", rows, K);
+  if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
+  if ((int64_t)rows * K * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "x exceeds 2 GiB");
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL x / q / scales");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x and q need 16-byte, scales 4-byte alignment");
+  hipError_t e = moe::launch_quant_rows(x, rows, K, dtype, q, scales, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "quant launch");
+}
+
+int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_row_div,
+                  const int8_t* B, const void* w_scales, int E, int N, int K, int dtype,
+                  const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                  const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
+                  int num_slots, const float* topk_weights, int act, void* C, void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (E <= 0 || N <= 0 || K <= 0 || num_a_rows < 0 || a_row_div <= 0 || num_slots < 0 ||
+      capacity < 0)
+    return fail(MOE_ERR_INVALID_ARG, "E=%d N=%d K=%d rows=%d a_row_div=%d slots=%d", E, N, K,
+                num_a_rows, a_row_div, num_slots);
+  if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL)
+    return fail(MOE_ERR_INVALID_ARG, "act = %d", act);
+  if (block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64)", block_m);
+  if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
+  if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
+  if ((int64_t)num_a_rows * K >= ((int64_t)1 << 31) || (int64_t)N * K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "A or one expert's weights exceed 2 GiB");
+  if ((int64_t)num_a_rows * a_row_div < num_slots)
+    return fail(MOE_ERR_INVALID_ARG, "A has %d rows, slots need %lld", num_a_rows,
+                (long long)((num_slots + a_row_div - 1) / a_row_div));
+  if (!A || !a_scales || !B || !w_scales || !C || !sorted_token_ids || !expert_ids ||
+      !num_tokens_post_padded)
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(a_scales, 4) ||
+      !aligned(w_scales, 2))
+    return fail(MOE_ERR_INVALID_ARG, "A, B and C need 16-byte alignment");
+  if (topk_weights && !aligned(topk_weights, 4))
+    return fail(MOE_ERR_INVALID_ARG, "topk_weights must be 4-byte aligned");
+  if (num_slots == 0 || capacity == 0) return MOE_OK;
+  moe::W8A8Params p{};
+  p.A = A;
+  p.a_scales = a_scales;
+  p.num_a_rows = num_a_rows;
+  p.a_row_div = a_row_div;
+  p.B = B;
+  p.w_scales = w_scales;
+  p.E = E;
+  p.N = N;
+  p.K = K;
+  p.sorted_ids = sorted_token_ids;
+  p.expert_ids = expert_ids;
+  p.num_post = num_tokens_post_padded;
+  p.num_blocks = (int)(capacity / block_m);
+  p.num_slots = num_slots;
+  p.topk_w = topk_weights;
+  p.C = C;
+  hipError_t e = moe::launch_w8a8_gemm(p, block_m, act, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "w8a8 gemm launch");
+}
+
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
                                       const moe_quant_t* quant, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || !quant) return 0;

@@ -80,6 +80,28 @@ hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t str
 // out[r, c] = sum_z partial[z, r, c] (z ascending) over rows x cols, rounded to dtype.
 hipError_t launch_split_reduce(const float* partial, int split, int rows, int cols, int dtype,
                                void* out, hipStream_t stream);
+// w8a8: int8 activations (one float32 scale per row) x int8 weights (one dtype scale per column)
+struct W8A8Params {
+  const int8_t* A;            // [num_a_rows, K]
+  const float* a_scales;      // [num_a_rows]
+  int num_a_rows;
+  int a_row_div;
+  const int8_t* B;            // [E, N, K]
+  const void* w_scales;       // dtype [E, N]
+  int E, N, K;
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* num_post;
+  int num_blocks;
+  int num_slots;
+  const float* topk_w;        // nullable
+  void* C;                    // dtype [num_slots, N] (act: N/2)
+};
+hipError_t launch_quant_rows(const void* x, int rows, int K, int dtype, int8_t* q, float* scales,
+                             hipStream_t stream);
+hipError_t launch_w8a8_gemm(const W8A8Params& p, int block_m, int act, int dtype,
+                            hipStream_t stream);
+
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);
 // inter[s, i] = SiLU(sum_z partial[z, s, i]) * sum_z partial[z, s, I + i] (first GEMM split over K)
