@@ -11,8 +11,9 @@ that hold several consecutive layer calls.
 Also reported: the roofline of the dominant kernel (the w13 grouped GEMM with the SiLU epilogue),
 timed alone with HIP events on the stream it is launched on; an M sweep of the workload; the CPU
 oracle's throughput on a bounded sample of the same batch; the dense uint4 GEMM at the small-n
-benchmark's shapes (m 16, k 8192, n 128 ... 32768); and the grouped GEMM over batched-experts
-activations on an expert-parallel share of 32 DeepSeek-V3-shaped experts.
+benchmark's shapes (m 16, k 8192, n 128 ... 32768); the grouped GEMM over batched-experts
+activations on an expert-parallel share of 32 DeepSeek-V3-shaped experts; and w8a8 (per-token
+int8 activations) against w8a16 on the DeepSeek-V3 int8 experts.
 """
 from __future__ import annotations
 
@@ -54,6 +55,8 @@ def parse():
                     help="skip the dense uint4 GEMM sweep (m 16, k 8192, n 128 ... 32768)")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched-experts GEMM sweep (expert-parallel share, 32 experts)")
+    ap.add_argument("--no-w8a8", action="store_true",
+                    help="skip the w8a8 vs w8a16 first-GEMM comparison (DeepSeek-V3 int8 experts)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device-to-device copy (known bytes) so that "
                          "profiler traffic counters can be scaled")
@@ -276,6 +279,50 @@ def batched_sweep(steps, warmup, E=32, H=7168, I=2048, Ts=(8, 64), seed=0):
     return out
 
 
+def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
+    """w8a8 against w8a16 on the DeepSeek-V3 full-expert layer with int8 weights (256 experts,
+    H 7168, I 2048, top-8 grouped sigmoid routing, bf16): the per-token activation quantiser, the
+    first grouped GEMM with SiLU on int8 activations (integer matrix cores), and the same GEMM on
+    bf16 activations, on the same weights and routing; time per call from graph replays over two
+    weight copies, and tera-operations per second against the dense peaks (int8 5.0 POP/s, bf16
+    2.5 PFLOP/s)."""
+    import torch
+
+    import synth
+    import weight_only_int4_topk_amd as B
+    wl = synth.WORKLOADS["dsv3_prefill_int8"]
+    layer = synth.make_layer(wl, seed=seed, device="cuda")
+    copies = [layer, {k: (v.clone() if v is not None else None) for k, v in layer.items()}]
+    rt = B.routing(wl.score, wl.renormalize, wl.num_groups, wl.topk_groups, wl.scale)
+    out = []
+    for M in Ms:
+        x = synth.make_x(wl, M, seed=seed, device="cuda")
+        lg = synth.make_logits(wl, M, seed=seed, device="cuda")
+        tw, ti = B.moe_topk_softmax(lg, wl.topk, rt)
+        bm = 64
+        st, ex, npost = B.moe_align_block_size(ti, wl.E, bm)
+        q, sa = B.moe_quant_int8_rows(x)
+        ns = M * wl.topk
+        h = torch.empty((ns, wl.I), dtype=wl.torch_dtype, device="cuda")
+        t_q = graph_replay([lambda: B.moe_quant_int8_rows(x, q, sa)], steps, warmup)[0] / steps
+        f8 = [(lambda c=c: B.moe_w8a8_gemm(q, sa, wl.topk, c["w13"], c["w13_scales"], st, ex, npost,
+                                           bm, ns, wl.torch_dtype, act=1, C=h)) for c in copies]
+        f16 = [(lambda c=c: B.moe_wna16_gemm(x, wl.topk, c["w13"], c["w13_scales"], None, st, ex,
+                                             npost, bm, ns, act=1, C=h)) for c in copies]
+        t8 = graph_replay(f8, steps, warmup)[0] / steps
+        t16 = graph_replay(f16, steps, warmup)[0] / steps
+        ops = 4.0 * wl.H * wl.I * ns
+        out.append({"M": M, "block_m": bm, "quant_us": round(t_q * 1e6, 2),
+                    "w8a8_w13_us": round(t8 * 1e6, 2), "w8a8_TOPs": round(ops / t8 / 1e12, 1),
+                    "w8a8_int8_mfma_frac": round(ops / t8 / 1e12 / 5000.0, 4),
+                    "w8a16_w13_us": round(t16 * 1e6, 2), "w8a16_TFLOPs": round(ops / t16 / 1e12, 1),
+                    "w8a16_bf16_mfma_frac": round(ops / t16 / 1e12 / MFMA_PEAK_TFLOPS, 4)})
+        log(f"[bench] w8a8 {out[-1]}")
+    del copies, layer
+    torch.cuda.empty_cache()
+    return out
+
+
 KERNEL_SOURCES = ("gemm.hip", "common.h", "launch.h", "api.cpp")
 
 
@@ -387,6 +434,8 @@ def main():
 
     dense = None if args.no_dense else dense_sweep(args.sweep_steps, max(10, args.warmup // 4))
     batched = None if args.no_batched else batched_sweep(args.sweep_steps, max(10, args.warmup // 4))
+    w8a8 = None if args.no_w8a8 else w8a8_sweep(max(20, args.sweep_steps // 4),
+                                                 max(5, args.warmup // 8))
 
     value = M * args.steps / t_layer
     line = {
@@ -413,6 +462,7 @@ def main():
         "sweep": sweep,
         "dense_w4a16": dense,
         "batched_experts": batched,
+        "w8a8": w8a8,
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(line), flush=True)
