@@ -38,7 +38,7 @@ __all__ = [
     "exp_f32_spec", "sigmoid_f32_spec", "route_softmax", "route_sigmoid_grouped", "route",
     "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
     "grouped_gemm", "dense_gemm", "batched_gemm", "quant_int8_rows", "w8a8_grouped_gemm",
-    "to_numpy",
+    "round_to_dtype", "moe_layer_w8a8_rows", "to_numpy",
 ]
 
 
@@ -434,3 +434,43 @@ def w8a8_grouped_gemm(Aq, a_scales, a_row_div: int, w_of, sorted_token_ids, expe
         out[s] = h
     return out
 
+
+def round_to_dtype(x64, dtype: str) -> np.ndarray:
+    """Values rounded to fp16 or bf16 (through float32, round to nearest even), as float64."""
+    x32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    if dtype == "fp16":
+        return x32.astype(np.float16).astype(np.float64)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def moe_layer_w8a8_rows(x, topk_ids, topk_weights, layer: dict, dtype: str, rows=None):
+    """The layer with int8 experts and per-token int8 activations, as a definition.
+
+    For token m and its j-th expert e: (xq, xs) = quant_int8_rows(x[m]);
+    h = (W13q[e] @ xq) * xs * W13s[e]; a = SiLU(h[:I]) * h[I:] rounded to the activation dtype (the
+    rows the two GEMMs exchange); (aq, as) = quant_int8_rows(a); y = (W2q[e] @ aq) * as * W2s[e];
+    out[m] = sum_j w[m, j] * y_j (j ascending).  Integer sums exact, float64 elsewhere.
+    layer: w13 int8 [E, 2I, H], w13_scales [E, 2I], w2 int8 [E, H, I], w2_scales [E, H]."""
+    xs_all = np.asarray(to_numpy(x), dtype=np.float32)
+    ids = np.asarray(to_numpy(topk_ids), dtype=np.int64)
+    wts = np.asarray(to_numpy(topk_weights), dtype=np.float64)
+    rows = np.arange(ids.shape[0]) if rows is None else np.asarray(rows)
+    L = {k: np.asarray(to_numpy(v)) for k, v in layer.items() if v is not None}
+    H = xs_all.shape[1]
+    out = np.zeros((len(rows), H), np.float64)
+    for i, m in enumerate(rows):
+        xq, xsc = quant_int8_rows(xs_all[m:m + 1])
+        for j in range(ids.shape[1]):
+            e = int(ids[m, j])
+            w13q = L["w13"][e].astype(np.int64)
+            I = w13q.shape[0] // 2
+            h = (w13q @ xq[0].astype(np.int64)).astype(np.float64) * float(xsc[0]) * \
+                L["w13_scales"][e].astype(np.float64)
+            a = round_to_dtype(silu(h[:I]) * h[I:], dtype)
+            aq, asc = quant_int8_rows(a.astype(np.float32)[None, :])
+            y = (L["w2"][e].astype(np.int64) @ aq[0].astype(np.int64)).astype(np.float64) * \
+                float(asc[0]) * L["w2_scales"][e].astype(np.float64)
+            out[i] += wts[m, j] * y
+    return out

@@ -498,3 +498,27 @@ def test_w8a8_grouped_gemm_is_the_scaled_integer_product():
             if act:
                 h = h[: N // 2] / (1 + np.exp(-h[: N // 2])) * h[N // 2:]
             np.testing.assert_allclose(got[s], h, rtol=1e-13, atol=1e-15)
+
+
+def test_w8a8_layer_is_the_grouped_pipeline():
+    """The per-token layer definition equals the grouped form: GEMM1 with SiLU over align output,
+    rows rounded to the activation dtype and quantised per slot, GEMM2, then the weighted sum in
+    slot order; and it stays within int8 quantisation error of the float layer on the same weights."""
+    wl = synth.Workload("l8", E=4, H=256, I=256, topk=2, Ms=(6,), dtype="bf16", bits=8)
+    layer = synth.make_layer(wl, seed=12)
+    x = synth.make_x(wl, 6, seed=12)
+    ids, w = O.route(O.to_numpy(synth.make_logits(wl, 6, seed=12)), 2)
+    L = {k: O.to_numpy(v) for k, v in layer.items() if v is not None}
+    ref = O.moe_layer_w8a8_rows(x, ids, w, L, "bf16")
+    xq, xs = O.quant_int8_rows(x)
+    st, ex, T = O.align_block_size(ids, wl.E, 16)
+    ns = 12
+    g1 = O.w8a8_grouped_gemm(xq, xs, 2, lambda e: (L["w13"][e], L["w13_scales"][e]), st, ex, T, 16,
+                             ns, act=1)
+    inter = np.stack([O.round_to_dtype(g1[s], "bf16") for s in range(ns)]).astype(np.float32)
+    iq, isc = O.quant_int8_rows(inter)
+    g2 = O.w8a8_grouped_gemm(iq, isc, 1, lambda e: (L["w2"][e], L["w2_scales"][e]), st, ex, T, 16, ns)
+    grouped = np.stack([w[m, 0] * g2[2 * m] + w[m, 1] * g2[2 * m + 1] for m in range(6)])
+    np.testing.assert_allclose(ref, grouped, rtol=1e-12, atol=1e-15)
+    flt = O.moe_layer(x, ids, w, O.ExpertSource(layer, 8))
+    assert np.linalg.norm(ref - flt) / np.linalg.norm(flt) < 2e-2
