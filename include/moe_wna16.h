@@ -206,6 +206,22 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
                   const int32_t* num_tokens_post_padded, int64_t capacity, int block_m,
                   int num_slots, const float* topk_weights, int act, void* C, void* stream);
 
+/* The whole layer with w8a8 experts: routing and align as in fused_moe_wna16, x quantised per
+ * token (moe_quant_int8_rows), w8a8 GEMM1 with SiLU(gate) * up into dtype rows, those rows
+ * quantised per slot, w8a8 GEMM2 into float32 rows, top-k weighted combine in float32 (fixed order).
+ *   w13 device int8 [E, 2I, H], w13_scales device dtype [E, 2I]; w2 int8 [E, H, I], w2_scales [E, H]
+ *   workspace: at least fused_moe_w8a8_workspace_size(...) bytes, 256-byte aligned
+ *   block_m 0 = the library's choice (as moe_pick_block_m for int8 weights, at most 64)
+ * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, block_m in {0, 16, 32, 64}. */
+int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+                   const moe_routing_t* routing, const int8_t* w13, const void* w13_scales,
+                   const int8_t* w2, const void* w2_scales, int dtype, int block_m,
+                   void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
+                   int32_t* topk_ids_out, void* stream);
+
+/* Workspace bytes fused_moe_w8a8 needs (0 for invalid sizes). */
+size_t fused_moe_w8a8_workspace_size(int M, int H, int I, int E, int topk, int dtype, int block_m);
+
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits and activations of `dtype`: the smallest of {16, 32, 64, 128} that holds 1.5x the average
  * number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots share one

@@ -1,0 +1,74 @@
+"""The fused w8a8 layer (int8 experts, per-token int8 activations) on the GPU vs the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_only_int4_topk_amd as B
+from helpers import assert_layer_close, cuda_layer, oracle_route, routing_of
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "softmax_fp16": synth.Workload("a", E=8, H=512, I=512, topk=2, Ms=(33,), dtype="fp16", bits=8),
+    "softmax_bf16": synth.Workload("b", E=8, H=768, I=256, topk=2, Ms=(70,), dtype="bf16", bits=8),
+    "sigmoid_groups_bf16": synth.Workload("c", E=64, H=512, I=256, topk=8, Ms=(20,), score="sigmoid",
+                                          num_groups=8, topk_groups=4, scale=2.5, dtype="bf16",
+                                          bits=8),
+    "single_token": synth.Workload("d", E=16, H=1024, I=512, topk=4, Ms=(1,), bits=8),
+}
+
+
+def _run(wl, M, seed, device="cpu", block_m=0):
+    layer = synth.make_layer(wl, seed=seed, device=device)
+    x = synth.make_x(wl, M, seed=seed, device=device)
+    lg = synth.make_logits(wl, M, seed=seed, device=device)
+    lay = cuda_layer(layer) if device == "cpu" else layer
+    ti = torch.empty((M, wl.topk), dtype=torch.int32, device="cuda")
+    tw = torch.empty((M, wl.topk), dtype=torch.float32, device="cuda")
+    out = B.fused_moe_w8a8(x.cuda(), lg.cuda(), wl.topk, routing_of(wl), lay["w13"],
+                           lay["w13_scales"], lay["w2"], lay["w2_scales"], block_m=block_m,
+                           topk_weights=tw, topk_ids=ti)
+    torch.cuda.synchronize()
+    ids, w = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids)
+    return out, x, ids, w, lay
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_fused_w8a8_vs_oracle(name):
+    wl = SMALL[name]
+    M = wl.Ms[0]
+    out, x, ids, w, lay = _run(wl, M, seed=5)
+    print(f"fused w8a8 {name} M={M}", flush=True)
+    ref = O.moe_layer_w8a8_rows(x, ids, w, {k: v.cpu() for k, v in lay.items() if v is not None},
+                                wl.dtype)
+    assert_layer_close(out, ref, f"w8a8 {name}")
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_fused_w8a8_block_sizes_deterministic(bm):
+    wl = SMALL["softmax_fp16"]
+    out1, x, ids, w, lay = _run(wl, 33, seed=6, block_m=bm)
+    out2, *_ = _run(wl, 33, seed=6, block_m=bm)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    ref = O.moe_layer_w8a8_rows(x, ids, w, {k: v.cpu() for k, v in lay.items() if v is not None},
+                                wl.dtype)
+    assert_layer_close(out1, ref, f"w8a8 bm={bm}")
+
+
+def test_fused_w8a8_mixtral_shape_sampled():
+    """Mixtral-shaped int8 experts at M = 16 on the GPU; three tokens checked against the oracle
+    (their experts copied to the host)."""
+    wl = synth.WORKLOADS["mixtral"].with_(bits=8)
+    M = 16
+    out, x, ids, w, lay = _run(wl, M, seed=0, device="cuda")
+    rows = [0, 7, 15]
+    experts = sorted(set(ids[rows].reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
+    remap = {e: i for i, e in enumerate(experts)}
+    ids_sub = np.vectorize(lambda e: remap.get(int(e), 0))(ids)
+    ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows)
+    assert_layer_close(O.to_numpy(out)[rows], ref, "w8a8 mixtral")

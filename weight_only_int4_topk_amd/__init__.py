@@ -59,6 +59,9 @@ _SIGS = {
     "moe_quant_int8_rows": ([_P, _I, _I, _I, _P, _P, _P], _I),
     "moe_w8a8_gemm": ([_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I64, _I, _I, _P, _I,
                        _P, _P], _I),
+    "fused_moe_w8a8": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P, _P, _I,
+                        _I, _P, ctypes.c_size_t, _P, _P, _P, _P], _I),
+    "fused_moe_w8a8_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], ctypes.c_size_t),
     "moe_wna16_batched_gemm": ([_P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I,
                                 _I, _I, _P, _P], _I),
     "fused_moe_wna16_workspace_size": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I],
@@ -238,6 +241,26 @@ def moe_w8a8_gemm(Aq, a_scales, a_row_div, B, w_scales, sorted_ids, expert_ids, 
                                _ptr(num_post), sorted_ids.numel(), block_m, num_slots,
                                _ptr(topk_weights), act, _ptr(C), _stream(stream)))
     return C
+
+
+def fused_moe_w8a8(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w2, w2_scales,
+                   block_m=0, workspace=None, out=None, topk_weights=None, topk_ids=None,
+                   stream=None):
+    """The whole layer with int8 experts and per-token int8 activations; returns out [M, H]."""
+    M, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    code = _dtype_code(x.dtype)
+    need = int(lib().fused_moe_w8a8_workspace_size(M, H, I, E, topk, code, block_m))
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=x.dtype, device=x.device)
+    _check(lib().fused_moe_w8a8(_ptr(x), _ptr(router_logits), M, H, I, E, topk, ctypes.byref(rt),
+                                _ptr(w13), _ptr(w13_scales), _ptr(w2), _ptr(w2_scales), code,
+                                block_m, _ptr(workspace), workspace.numel(), _ptr(out),
+                                _ptr(topk_weights), _ptr(topk_ids), _stream(stream)))
+    return out
 
 
 def fused_moe_wna16_workspace_size(M, H, I, E, topk, quant: MoeQuant, dtype, block_m=0) -> int:

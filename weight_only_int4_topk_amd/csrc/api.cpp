@@ -578,6 +578,140 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
   return e == hipSuccess ? MOE_OK : hip_fail(e, "w8a8 gemm launch");
 }
 
+// ------------------------------------------------------------------------------------------------
+// the fused w8a8 layer
+// ------------------------------------------------------------------------------------------------
+namespace {
+struct PlanW8 {
+  int bm;
+  int64_t cap;
+  size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_xq, off_xs, off_inter, off_iq, off_is,
+      off_y, total;
+};
+PlanW8 make_plan_w8(int M, int H, int I, int E, int topk, int dtype, int block_m) {
+  PlanW8 p{};
+  const int64_t slots = (int64_t)M * topk;
+  p.bm = block_m > 0 ? block_m : std::min(64, pick_block_m(M, topk, E, 8, dtype));
+  p.cap = align_capacity(slots, E, p.bm);
+  const int64_t nblk = (p.cap + p.bm - 1) / p.bm;
+  size_t off = 0;
+  p.off_w = off;      off += up256((size_t)slots * 4);
+  p.off_ids = off;    off += up256((size_t)slots * 4);
+  p.off_sorted = off; off += up256((size_t)p.cap * 4);
+  p.off_eids = off;   off += up256((size_t)nblk * 4);
+  p.off_npost = off;  off += 256;
+  p.off_xq = off;     off += up256((size_t)M * H);
+  p.off_xs = off;     off += up256((size_t)M * 4);
+  p.off_inter = off;  off += up256((size_t)slots * I * 2);
+  p.off_iq = off;     off += up256((size_t)slots * I);
+  p.off_is = off;     off += up256((size_t)slots * 4);
+  p.off_y = off;      off += up256((size_t)slots * H * 4);
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+size_t fused_moe_w8a8_workspace_size(int M, int H, int I, int E, int topk, int dtype, int block_m) {
+  if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;
+  if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64) return 0;
+  return make_plan_w8(M, H, I, E, topk, dtype, block_m).total;
+}
+
+int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+                   const moe_routing_t* routing, const int8_t* w13, const void* w13_scales,
+                   const int8_t* w2, const void* w2_scales, int dtype, int block_m,
+                   void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
+                   int32_t* topk_ids_out, void* stream) {
+  if (int rc = check_dtype(dtype)) return rc;
+  if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d H=%d I=%d", M, H, I);
+  if (int rc = check_routing(routing, E, topk)) return rc;
+  if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64)", block_m);
+  if (H % 256 || I % 256)
+    return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
+  if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");
+  if ((int64_t)M * topk * H * 4 >= ((int64_t)1 << 31) || (int64_t)2 * I * H >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "intermediate rows or one expert's weights exceed 2 GiB");
+  if (M == 0) return MOE_OK;
+  if (!x || !router_logits || !out || !workspace || !w13 || !w13_scales || !w2 || !w2_scales)
+    return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+      !aligned(router_logits, 4) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(w13_scales, 2) || !aligned(w2_scales, 2))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned pointer argument");
+  if ((topk_weights_out && !aligned(topk_weights_out, 4)) ||
+      (topk_ids_out && !aligned(topk_ids_out, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "routing outputs must be 4-byte aligned");
+  const PlanW8 pl = make_plan_w8(M, H, I, E, topk, dtype, block_m);
+  if (workspace_bytes < pl.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.total);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* tw = topk_weights_out ? topk_weights_out : (float*)(ws + pl.off_w);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(ws + pl.off_ids);
+  int32_t* sorted = (int32_t*)(ws + pl.off_sorted);
+  int32_t* eids = (int32_t*)(ws + pl.off_eids);
+  int32_t* npost = (int32_t*)(ws + pl.off_npost);
+  int8_t* xq = (int8_t*)(ws + pl.off_xq);
+  float* xs = (float*)(ws + pl.off_xs);
+  void* inter = ws + pl.off_inter;
+  int8_t* iq = (int8_t*)(ws + pl.off_iq);
+  float* is = (float*)(ws + pl.off_is);
+  float* y = (float*)(ws + pl.off_y);
+  const int slots = M * topk;
+
+  const moe::RoutingParams rp{routing->score, routing->renormalize, routing->num_groups,
+                              routing->topk_groups, routing->scale};
+  hipError_t e;
+  if (moe::route_align_fits(M, E)) {
+    e = moe::launch_route_align(router_logits, M, E, topk, rp, tw, ids, pl.bm, sorted, eids, npost,
+                                pl.cap, st);
+    if (e != hipSuccess) return hip_fail(e, "routing + align launch");
+  } else {
+    e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
+    if (e != hipSuccess) return hip_fail(e, "routing launch");
+    e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
+    if (e != hipSuccess) return hip_fail(e, "align launch");
+  }
+  e = moe::launch_quant_rows(x, M, H, dtype, xq, xs, st);
+  if (e != hipSuccess) return hip_fail(e, "quant launch");
+  moe::W8A8Params g1{};
+  g1.A = xq;
+  g1.a_scales = xs;
+  g1.num_a_rows = M;
+  g1.a_row_div = topk;
+  g1.B = w13;
+  g1.w_scales = w13_scales;
+  g1.E = E;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.sorted_ids = sorted;
+  g1.expert_ids = eids;
+  g1.num_post = npost;
+  g1.num_blocks = (int)(pl.cap / pl.bm);
+  g1.num_slots = slots;
+  g1.C = inter;
+  e = moe::launch_w8a8_gemm(g1, pl.bm, 1, dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "w8a8 gemm1 launch");
+  e = moe::launch_quant_rows(inter, slots, I, dtype, iq, is, st);
+  if (e != hipSuccess) return hip_fail(e, "quant launch");
+  moe::W8A8Params g2 = g1;
+  g2.A = iq;
+  g2.a_scales = is;
+  g2.num_a_rows = slots;
+  g2.a_row_div = 1;
+  g2.B = w2;
+  g2.w_scales = w2_scales;
+  g2.N = H;
+  g2.K = I;
+  g2.C = y;
+  e = moe::launch_w8a8_gemm(g2, pl.bm, 0, dtype, st, 1);
+  if (e != hipSuccess) return hip_fail(e, "w8a8 gemm2 launch");
+  e = moe::launch_combine(y, 1, tw, M, topk, H, dtype, out, st);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
                                       const moe_quant_t* quant, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || !quant) return 0;

@@ -99,8 +99,9 @@ struct W8A8Params {
 };
 hipError_t launch_quant_rows(const void* x, int rows, int K, int dtype, int8_t* q, float* scales,
                              hipStream_t stream);
+// out_f32 (act 0 only): C is float [num_slots, N] (the fused layer's second GEMM, combined later)
 hipError_t launch_w8a8_gemm(const W8A8Params& p, int block_m, int act, int dtype,
-                            hipStream_t stream);
+                            hipStream_t stream, int out_f32 = 0);
 
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);

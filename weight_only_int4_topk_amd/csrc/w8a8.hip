@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
   if (lane == 0) scales[row] = s;
 }
 
-template <int DT, int MT, int ACT>
+template <int DT, int MT, int ACT, int OUTF32>
 __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8A8Params p) {
   constexpr int NTW = 2;                     // column tiles of 16 per wavefront
   constexpr int BM = 16 * MT;
@@ -203,6 +203,9 @@ __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8A8Params p) {
           const float u = (float)acc[m][t + NOUT][i] * sa * bits_to_float<DT>(wsc[N / 2 + cc]);
           ((uint16_t*)p.C)[(size_t)slot * (N / 2) + cc] =
               float_to_bits<DT>(g / (1.0f + __expf(-g)) * u * wscale);
+        } else if constexpr (OUTF32) {
+          const float v = (float)acc[m][t][i] * sa * bits_to_float<DT>(wsc[cc]);
+          ((float*)p.C)[(size_t)slot * N + cc] = v * wscale;
         } else {
           const float v = (float)acc[m][t][i] * sa * bits_to_float<DT>(wsc[cc]);
           ((uint16_t*)p.C)[(size_t)slot * N + cc] = float_to_bits<DT>(v * wscale);
@@ -213,25 +216,28 @@ __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8A8Params p) {
 }
 
 template <int DT, int MT>
-hipError_t launch_w8a8_mt(const W8A8Params& p, int act, hipStream_t stream) {
+hipError_t launch_w8a8_mt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
   const int n_out = act ? p.N / 2 : p.N;
   const int wg_cols = act ? 64 : 128;
   const long long grid = (long long)(n_out / wg_cols) * p.num_blocks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (act)
-    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 1, 0>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+  else if (out_f32)
+    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0, 0>), dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_w8a8_dt(const W8A8Params& p, int block_m, int act, hipStream_t stream) {
+hipError_t launch_w8a8_dt(const W8A8Params& p, int block_m, int act, int out_f32,
+                          hipStream_t stream) {
   switch (block_m) {
-    case 16: return launch_w8a8_mt<DT, 1>(p, act, stream);
-    case 32: return launch_w8a8_mt<DT, 2>(p, act, stream);
-    case 64: return launch_w8a8_mt<DT, 4>(p, act, stream);
+    case 16: return launch_w8a8_mt<DT, 1>(p, act, out_f32, stream);
+    case 32: return launch_w8a8_mt<DT, 2>(p, act, out_f32, stream);
+    case 64: return launch_w8a8_mt<DT, 4>(p, act, out_f32, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -252,9 +258,9 @@ hipError_t launch_quant_rows(const void* x, int rows, int K, int dtype, int8_t* 
 }
 
 hipError_t launch_w8a8_gemm(const W8A8Params& p, int block_m, int act, int dtype,
-                            hipStream_t stream) {
-  return dtype == 0 ? launch_w8a8_dt<0>(p, block_m, act, stream)
-                    : launch_w8a8_dt<1>(p, block_m, act, stream);
+                            hipStream_t stream, int out_f32) {
+  return dtype == 0 ? launch_w8a8_dt<0>(p, block_m, act, out_f32, stream)
+                    : launch_w8a8_dt<1>(p, block_m, act, out_f32, stream);
 }
 
 }  // namespace moe
