@@ -311,12 +311,27 @@ def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
                                              npost, bm, ns, act=1, C=h)) for c in copies]
         t8 = graph_replay(f8, steps, warmup)[0] / steps
         t16 = graph_replay(f16, steps, warmup)[0] / steps
+        # the whole layer both ways, same weights, routing computed inside
+        o = torch.empty((M, wl.H), dtype=wl.torch_dtype, device="cuda")
+        ws8 = torch.empty((B.lib().fused_moe_w8a8_workspace_size(M, wl.H, wl.I, wl.E, wl.topk, 1, 0),),
+                          dtype=torch.uint8, device="cuda")
+        ws16 = torch.empty((B.fused_moe_wna16_workspace_size(M, wl.H, wl.I, wl.E, wl.topk,
+                                                             B.QUANT_INT8, wl.torch_dtype),),
+                           dtype=torch.uint8, device="cuda")
+        l8 = [(lambda c=c: B.fused_moe_w8a8(x, lg, wl.topk, rt, c["w13"], c["w13_scales"], c["w2"],
+                                            c["w2_scales"], workspace=ws8, out=o)) for c in copies]
+        l16 = [(lambda c=c: B.fused_moe_wna16(x, lg, wl.topk, rt, c["w13"], c["w13_scales"], None,
+                                              c["w2"], c["w2_scales"], None, workspace=ws16, out=o))
+               for c in copies]
+        tl8 = graph_replay(l8, steps, warmup)[0] / steps
+        tl16 = graph_replay(l16, steps, warmup)[0] / steps
         ops = 4.0 * wl.H * wl.I * ns
         out.append({"M": M, "block_m": bm, "quant_us": round(t_q * 1e6, 2),
                     "w8a8_w13_us": round(t8 * 1e6, 2), "w8a8_TOPs": round(ops / t8 / 1e12, 1),
                     "w8a8_int8_mfma_frac": round(ops / t8 / 1e12 / 5000.0, 4),
                     "w8a16_w13_us": round(t16 * 1e6, 2), "w8a16_TFLOPs": round(ops / t16 / 1e12, 1),
-                    "w8a16_bf16_mfma_frac": round(ops / t16 / 1e12 / MFMA_PEAK_TFLOPS, 4)})
+                    "w8a16_bf16_mfma_frac": round(ops / t16 / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                    "w8a8_layer_us": round(tl8 * 1e6, 1), "w8a16_layer_us": round(tl16 * 1e6, 1)})
         log(f"[bench] w8a8 {out[-1]}")
     del copies, layer
     torch.cuda.empty_cache()
