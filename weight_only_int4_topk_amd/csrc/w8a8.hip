@@ -57,9 +57,9 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(const uint16_t* __restr
   if (lane == 0) scales[row] = s;
 }
 
-template <int DT, int MT, int ACT, int OUTF32>
+template <int DT, int MT, int ACT, int OUTF32, int NTW>
 __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8A8Params p) {
-  constexpr int NTW = 2;                     // column tiles of 16 per wavefront
+  // NTW column tiles of 16 per wavefront: each activation fragment read from LDS feeds NTW MFMAs
   constexpr int BM = 16 * MT;
   constexpr int KC = 256;                    // k per activation chunk: 4 k-blocks of 64
   constexpr int KBC = KC / 64;
@@ -215,20 +215,33 @@ __global__ void __launch_bounds__(256) w8a8_gemm_kernel(W8A8Params p) {
   }
 }
 
-template <int DT, int MT>
-hipError_t launch_w8a8_mt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
+template <int DT, int MT, int NTW>
+hipError_t launch_w8a8_ntw(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
   const int n_out = act ? p.N / 2 : p.N;
-  const int wg_cols = act ? 64 : 128;
+  const int wg_cols = 4 * (act ? NTW / 2 : NTW) * 16;
   const long long grid = (long long)(n_out / wg_cols) * p.num_blocks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (act)
-    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 1, 0>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 1, 0, NTW>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
   else if (out_f32)
-    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0, 1, NTW>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0, 0>), dim3((unsigned)grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((w8a8_gemm_kernel<DT, MT, 0, 0, NTW>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
+}
+
+// The SiLU GEMM takes four column tiles per wavefront where its gate columns divide the wider
+// workgroup (each activation fragment then feeds four MFMAs instead of two: DeepSeek-V3 int8
+// experts at M = 4096 3012 -> 2852 us); the plain GEMM keeps two (with four, H = 7168 gives half as
+// many workgroups and the M = 1024 layer measured 4 % slower).
+template <int DT, int MT>
+hipError_t launch_w8a8_mt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
+  if (act && (p.N / 2) % 128 == 0) return launch_w8a8_ntw<DT, MT, 4>(p, act, out_f32, stream);
+  return launch_w8a8_ntw<DT, MT, 2>(p, act, out_f32, stream);
 }
 
 template <int DT>
