@@ -38,7 +38,7 @@ __all__ = [
     "exp_f32_spec", "sigmoid_f32_spec", "route_softmax", "route_sigmoid_grouped", "route",
     "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
     "grouped_gemm", "dense_gemm", "batched_gemm", "quant_int8_rows", "w8a8_grouped_gemm",
-    "round_to_dtype", "moe_layer_w8a8_rows", "to_numpy",
+    "round_to_dtype", "moe_layer_w8a8_rows", "dequant_uint4_gidx", "to_numpy",
 ]
 
 
@@ -474,3 +474,20 @@ def moe_layer_w8a8_rows(x, topk_ids, topk_weights, layer: dict, dtype: str, rows
                 float(asc[0]) * L["w2_scales"][e].astype(np.float64)
             out[i] += wts[m, j] * y
     return out
+
+
+def dequant_uint4_gidx(qweight, scales, zeros, g_idx) -> np.ndarray:
+    """Exact decoded weights of one expert whose input columns carry a group index (GPTQ act-order).
+
+    The GEMM of "[Kernel] optimize performance of gptq marlin kernel when n is small" takes a
+    g_idx and a sort_indices argument (its benchmark passes them empty); the reading used: input
+    column k belongs to quantisation group g_idx[k] (128 columns per group, in any order), so
+    w[n, k] = (q[n, k] - z[n, g_idx[k]]) * s[n, g_idx[k]] in float64, columns in their original order.
+    qweight uint8 [N, K/2] (original column order), scales [N, K/128], zeros uint8 [N, K/256]."""
+    q = unpack_uint4(to_numpy(qweight)).astype(np.float64)
+    z = unpack_uint4(to_numpy(zeros)).astype(np.float64)
+    s = np.asarray(to_numpy(scales), dtype=np.float64)
+    g = np.asarray(to_numpy(g_idx)).astype(np.int64)
+    assert q.shape[1] == g.shape[0] and g.min() >= 0 and g.max() < s.shape[1]
+    return (q - z[:, g]) * s[:, g]
+

@@ -522,3 +522,35 @@ def test_w8a8_layer_is_the_grouped_pipeline():
     np.testing.assert_allclose(ref, grouped, rtol=1e-12, atol=1e-15)
     flt = O.moe_layer(x, ids, w, O.ExpertSource(layer, 8))
     assert np.linalg.norm(ref - flt) / np.linalg.norm(flt) < 2e-2
+
+
+# ---- GPTQ act-order: input columns carry their group index ------------------------------------
+def test_dequant_gidx_in_column_order_is_plain_decoding():
+    """With g_idx[k] = k // 128 the group-indexed decoding is the plain one."""
+    rng = np.random.default_rng(41)
+    N, K = 8, 512
+    q = rng.integers(0, 16, size=(N, K))
+    z = rng.integers(0, 16, size=(N, K // 128))
+    s = rng.uniform(0.01, 0.1, size=(N, K // 128))
+    got = O.dequant_uint4_gidx(_pack_nibbles(q), s, _pack_nibbles(z), np.arange(K) // 128)
+    np.testing.assert_array_equal(got, O.dequant_uint4(_pack_nibbles(q), s, _pack_nibbles(z)))
+
+
+def test_dequant_gidx_sorted_columns_give_the_grouped_storage():
+    """Columns permuted so that every group is contiguous (the sorted storage the layer reads) decode
+    to the same weights: w_gidx[:, perm] equals the plain decoding of the permuted codes, with
+    perm = stable argsort(g_idx) and w written out per element."""
+    rng = np.random.default_rng(42)
+    N, K = 6, 768
+    perm_true = rng.permutation(K)
+    g_idx = np.empty(K, np.int64)
+    g_idx[perm_true] = np.arange(K) // 128                 # group g = columns perm_true[128g:...]
+    q = rng.integers(0, 16, size=(N, K))
+    z = rng.integers(0, 16, size=(N, K // 128))
+    s = rng.uniform(0.01, 0.1, size=(N, K // 128))
+    w = O.dequant_uint4_gidx(_pack_nibbles(q), s, _pack_nibbles(z), g_idx)
+    for n, k in [(0, 0), (5, 767), (3, 400)]:
+        assert w[n, k] == (q[n, k] - z[n, g_idx[k]]) * s[n, g_idx[k]]
+    perm = np.argsort(g_idx, kind="stable")
+    sorted_w = O.dequant_uint4(_pack_nibbles(q[:, perm]), s, _pack_nibbles(z))
+    np.testing.assert_array_equal(w[:, perm], sorted_w)
