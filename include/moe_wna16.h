@@ -222,6 +222,29 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
 /* Workspace bytes fused_moe_w8a8 needs (0 for invalid sizes). */
 size_t fused_moe_w8a8_workspace_size(int M, int H, int I, int E, int topk, int dtype, int block_m);
 
+/* The whole layer with GPTQ act-order uint4 experts: the group of an input column is given per
+ * column (g_idx) rather than by its position.  The GEMM of "[Kernel] optimize performance of gptq
+ * marlin kernel when n is small" takes g_idx and sort_indices for this (its benchmark passes them
+ * empty); here the experts arrive in the sorted storage: for expert e, w13_perm[e] (int32 [H]) lists
+ * the original input columns in group order (group g = w13_perm[e][128g : 128g+128], i.e. a stable
+ * argsort of g_idx), and w13 / w13_scales / w13_zeros are the uint4 storage above of the weights
+ * with their columns in that order; likewise w2_perm [E, I] for w2.  The layer gathers each slot's
+ * activation row through its expert's permutation before each GEMM, and is otherwise
+ * fused_moe_wna16 (the same result as decoding w[n, k] = (q - z[g_idx[k]]) * s[g_idx[k]] in the
+ * original column order).  Permutation entries outside [0, H) (or [0, I)) read as zero.
+ *   workspace: at least fused_moe_wna16_act_order_workspace_size(...) bytes. */
+int fused_moe_wna16_act_order(const void* x, const float* router_logits, int M, int H, int I,
+                              int E, int topk, const moe_routing_t* routing, const void* w13,
+                              const void* w13_scales, const void* w13_zeros,
+                              const int32_t* w13_perm, const void* w2, const void* w2_scales,
+                              const void* w2_zeros, const int32_t* w2_perm, int dtype,
+                              int block_m, void* workspace, size_t workspace_bytes, void* out,
+                              float* topk_weights_out, int32_t* topk_ids_out, void* stream);
+
+/* Workspace bytes fused_moe_wna16_act_order needs (0 for invalid sizes). */
+size_t fused_moe_wna16_act_order_workspace_size(int M, int H, int I, int E, int topk, int dtype,
+                                                int block_m);
+
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits and activations of `dtype`: the smallest of {16, 32, 64, 128} that holds 1.5x the average
  * number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots share one

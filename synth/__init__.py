@@ -84,7 +84,8 @@ WORKLOADS = {
 # ----------------------------------------------------------------------------------------------
 # seeded streams
 # ----------------------------------------------------------------------------------------------
-_TAGS = {"w13": 1, "w2": 2, "x": 3, "logits": 4, "bias": 5, "dense_w": 6, "dense_x": 7}
+_TAGS = {"w13": 1, "w2": 2, "x": 3, "logits": 4, "bias": 5, "dense_w": 6, "dense_x": 7,
+         "perm13": 8, "perm2": 9}
 
 
 def stream_seed(seed: int, tag: str, idx: int = 0) -> int:
@@ -243,3 +244,30 @@ def make_dense(M: int, N: int, K: int, bits: int = 4, dtype: str = "fp16", seed:
         qw, sc = encode_int8_channel(w, dt)
         zp = None
     return {"A": A, "B": qw, "scales": sc, "zeros": zp}
+
+
+# ----------------------------------------------------------------------------------------------
+# act-order layers: every expert's input columns grouped by a seeded random permutation
+# ----------------------------------------------------------------------------------------------
+def make_layer_act_order(wl: Workload, seed: int = 0, device="cpu") -> dict:
+    """uint4 g128 experts whose quantisation groups are sets of 128 input columns in any order (GPTQ
+    act-order), in the sorted storage the layer reads: for expert e, perm[e] lists the original
+    input columns in group order (group g = perm[e][128g : 128g + 128]), and the codes, scales and
+    zero points are those of the drawn weights with their columns taken in that order.
+    Adds w13_perm int32 [E, H] and w2_perm int32 [E, I] to the usual tensors."""
+    assert wl.bits == 4
+    dt = wl.torch_dtype
+    out = {k: [] for k in ("w13", "w13_scales", "w13_zeros", "w2", "w2_scales", "w2_zeros",
+                           "w13_perm", "w2_perm")}
+    for e in range(wl.E):
+        w13, w2 = expert_weights_fp32(wl, e, seed, device)
+        for name, w, tag in (("w13", w13, "perm13"), ("w2", w2, "perm2")):
+            g = _gen(seed, tag, e, device)
+            perm = torch.randperm(w.shape[1], generator=g, device=device)
+            q, s, z = encode_uint4_g128(w[:, perm], dt)
+            out[name].append(q)
+            out[name + "_scales"].append(s)
+            out[name + "_zeros"].append(z)
+            out[name + "_perm"].append(perm.to(torch.int32))
+    return {k: torch.stack(v).contiguous() for k, v in out.items()}
+

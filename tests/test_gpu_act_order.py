@@ -1,0 +1,93 @@
+"""The fused layer with GPTQ act-order uint4 experts on the GPU vs the CPU oracle.
+
+The library reads the sorted storage (columns in group order plus each expert's permutation); the
+oracle reads the GPTQ form (codes in the original column order plus the group index of every
+column), rebuilt here from the seeded layer, and decodes with oracle.dequant_uint4_gidx."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_only_int4_topk_amd as B
+from helpers import assert_layer_close, oracle_route, routing_of
+
+pytestmark = pytest.mark.gpu
+
+
+class GidxSource:
+    """float64 weights of each expert in the original column order, from the GPTQ form."""
+
+    def __init__(self, layer, experts):
+        self.layer = {k: O.to_numpy(v) for k, v in layer.items()}
+        self.index = {int(e): i for i, e in enumerate(experts)}
+
+    def _deq(self, name, e):
+        i = self.index[int(e)]
+        q_sorted = O.unpack_uint4(self.layer[name][i])
+        perm = self.layer[name + "_perm"][i].astype(np.int64)
+        q = np.empty_like(q_sorted)
+        q[:, perm] = q_sorted                                 # column perm[j] holds sorted column j
+        g_idx = np.empty(perm.shape[0], np.int64)
+        g_idx[perm] = np.arange(perm.shape[0]) // 128
+        packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+        return O.dequant_uint4_gidx(packed, self.layer[name + "_scales"][i],
+                                    self.layer[name + "_zeros"][i], g_idx)
+
+    def w13(self, e):
+        return self._deq("w13", e)
+
+    def w2(self, e):
+        return self._deq("w2", e)
+
+
+SMALL = {
+    "softmax_fp16": synth.Workload("a", E=8, H=512, I=512, topk=2, Ms=(33,)),
+    "softmax_bf16": synth.Workload("b", E=16, H=768, I=512, topk=4, Ms=(50,), dtype="bf16"),
+    "sigmoid_groups": synth.Workload("c", E=64, H=512, I=256, topk=8, Ms=(20,), score="sigmoid",
+                                     num_groups=8, topk_groups=4, scale=2.5),
+    "single_token": synth.Workload("d", E=8, H=1792, I=768, topk=2, Ms=(1,)),
+}
+
+
+def _run(wl, M, seed, device="cpu", rows=None):
+    layer = synth.make_layer_act_order(wl, seed=seed, device=device)
+    x = synth.make_x(wl, M, seed=seed, device=device)
+    lg = synth.make_logits(wl, M, seed=seed, device=device)
+    lay = {k: v.cuda() for k, v in layer.items()}
+    ti = torch.empty((M, wl.topk), dtype=torch.int32, device="cuda")
+    tw = torch.empty((M, wl.topk), dtype=torch.float32, device="cuda")
+    out = B.fused_moe_wna16_act_order(x.cuda(), lg.cuda(), wl.topk, routing_of(wl), lay["w13"],
+                                      lay["w13_scales"], lay["w13_zeros"], lay["w13_perm"],
+                                      lay["w2"], lay["w2_scales"], lay["w2_zeros"], lay["w2_perm"],
+                                      topk_weights=tw, topk_ids=ti)
+    torch.cuda.synchronize()
+    ids, w = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids)
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    experts = sorted(set(ids[rows].reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device=lay["w13"].device)
+    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items()}
+    ref, _ = O.moe_layer_rows(x.cpu(), ids, w, GidxSource(sub, experts), rows)
+    return out, ref, rows
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_act_order_layer_vs_oracle(name):
+    wl = SMALL[name]
+    out, ref, rows = _run(wl, wl.Ms[0], seed=3)
+    print(f"act-order {name}", flush=True)
+    assert_layer_close(O.to_numpy(out)[rows], ref, f"act-order {name}")
+
+
+def test_act_order_deterministic():
+    wl = SMALL["softmax_fp16"]
+    a, _, _ = _run(wl, 33, seed=4)
+    b, _, _ = _run(wl, 33, seed=4)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_act_order_mixtral_shape_sampled():
+    wl = synth.WORKLOADS["mixtral"]
+    out, ref, rows = _run(wl, 16, seed=0, device="cuda", rows=[0, 9, 15])
+    assert_layer_close(O.to_numpy(out)[rows], ref, "act-order mixtral")

@@ -62,6 +62,10 @@ _SIGS = {
     "fused_moe_w8a8": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P, _P, _I,
                         _I, _P, ctypes.c_size_t, _P, _P, _P, _P], _I),
     "fused_moe_w8a8_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], ctypes.c_size_t),
+    "fused_moe_wna16_act_order": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P,
+                                   _P, _P, _P, _P, _P, _P, _I, _I, _P, ctypes.c_size_t, _P, _P,
+                                   _P, _P], _I),
+    "fused_moe_wna16_act_order_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], ctypes.c_size_t),
     "moe_wna16_batched_gemm": ([_P, _I, _I, _I, _P, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I,
                                 _I, _I, _P, _P], _I),
     "fused_moe_wna16_workspace_size": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I],
@@ -260,6 +264,28 @@ def fused_moe_w8a8(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w2, 
                                 _ptr(w13), _ptr(w13_scales), _ptr(w2), _ptr(w2_scales), code,
                                 block_m, _ptr(workspace), workspace.numel(), _ptr(out),
                                 _ptr(topk_weights), _ptr(topk_ids), _stream(stream)))
+    return out
+
+
+def fused_moe_wna16_act_order(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w13_zeros,
+                              w13_perm, w2, w2_scales, w2_zeros, w2_perm, block_m=0,
+                              workspace=None, out=None, topk_weights=None, topk_ids=None,
+                              stream=None):
+    """The layer with act-order uint4 experts in sorted storage plus per-expert permutations."""
+    M, H = x.shape
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    code = _dtype_code(x.dtype)
+    need = int(lib().fused_moe_wna16_act_order_workspace_size(M, H, I, E, topk, code, block_m))
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=x.dtype, device=x.device)
+    _check(lib().fused_moe_wna16_act_order(
+        _ptr(x), _ptr(router_logits), M, H, I, E, topk, ctypes.byref(rt), _ptr(w13),
+        _ptr(w13_scales), _ptr(w13_zeros), _ptr(w13_perm), _ptr(w2), _ptr(w2_scales),
+        _ptr(w2_zeros), _ptr(w2_perm), code, block_m, _ptr(workspace), workspace.numel(),
+        _ptr(out), _ptr(topk_weights), _ptr(topk_ids), _stream(stream)))
     return out
 
 

@@ -719,12 +719,24 @@ size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
   return make_plan(M, H, I, E, topk, quant->bits, dtype, block_m).total;
 }
 
-int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
-                    const moe_routing_t* routing, const void* w13, const void* w13_scales,
-                    const void* w13_zeros, const void* w2, const void* w2_scales,
-                    const void* w2_zeros, const moe_quant_t* quant, int dtype, int block_m,
-                    void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
-                    int32_t* topk_ids_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Extra workspace of the act-order layer: each slot's activation row gathered through its expert's
+// input-column permutation, for both GEMMs.
+size_t act_order_bytes(int M, int H, int I, int topk) {
+  return up256((size_t)M * topk * H * 2) + up256((size_t)M * topk * I * 2);
+}
+
+// The fused layer; w13_perm / w2_perm non-NULL: act-order experts (the activation rows are
+// gathered per slot through the expert's permutation before each GEMM).
+int fused_impl(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+               const moe_routing_t* routing, const void* w13, const void* w13_scales,
+               const void* w13_zeros, const void* w2, const void* w2_scales, const void* w2_zeros,
+               const moe_quant_t* quant, int dtype, int block_m, void* workspace,
+               size_t workspace_bytes, void* out, float* topk_weights_out, int32_t* topk_ids_out,
+               const int32_t* w13_perm, const int32_t* w2_perm, void* stream) {
   if (int rc = check_dtype(dtype)) return rc;
   if (int rc = check_quant(quant)) return rc;
   if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d H=%d I=%d", M, H, I);
@@ -748,8 +760,10 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
       (topk_ids_out && !aligned(topk_ids_out, 4)))
     return fail(MOE_ERR_INVALID_ARG, "routing outputs must be 4-byte aligned");
   const Plan pl = make_plan(M, H, I, E, topk, quant->bits, dtype, block_m);
-  if (workspace_bytes < pl.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, pl.total);
+  const bool act_order = w13_perm != nullptr;
+  const size_t need = pl.total + (act_order ? act_order_bytes(M, H, I, topk) : 0);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   const bool split1 = pl.split1 > 1;
   // split: plain columns (gate rows, then up rows) into float32 partials, 2 column tiles per
   // wavefront so the workgroup count matches the estimate the split was chosen for
@@ -784,10 +798,18 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
     if (e != hipSuccess) return hip_fail(e, "align launch");
   }
 
+  // act-order: slot s reads x[s / topk] through its expert's permutation of the H input columns
+  void* xa = act_order ? (void*)(ws + pl.total) : nullptr;
+  void* ia = act_order ? (void*)(ws + pl.total + up256((size_t)M * topk * H * 2)) : nullptr;
+  if (act_order) {
+    e = moe::launch_gather_cols(x, topk, ids, E, w13_perm, H, slots, dtype, xa, st);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+  }
+
   moe::GemmParams g1{};
-  g1.A = x;
-  g1.num_a_rows = M;
-  g1.a_row_div = topk;
+  g1.A = act_order ? xa : x;
+  g1.num_a_rows = act_order ? slots : M;
+  g1.a_row_div = act_order ? 1 : topk;
   g1.B = (const uint8_t*)w13;
   g1.scales = w13_scales;
   g1.zeros = (const uint8_t*)w13_zeros;
@@ -809,8 +831,13 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
     if (e != hipSuccess) return hip_fail(e, "gemm1 combine launch");
   }
 
+  if (act_order) {
+    e = moe::launch_gather_cols(inter, 1, ids, E, w2_perm, I, slots, dtype, ia, st);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+  }
+
   moe::GemmParams g2 = g1;
-  g2.A = inter;
+  g2.A = act_order ? ia : inter;
   g2.num_a_rows = slots;
   g2.a_row_div = 1;
   g2.B = (const uint8_t*)w2;
@@ -826,6 +853,44 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   e = moe::launch_combine(part, pl.split2, tw, M, topk, H, dtype, out, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+                    const moe_routing_t* routing, const void* w13, const void* w13_scales,
+                    const void* w13_zeros, const void* w2, const void* w2_scales,
+                    const void* w2_zeros, const moe_quant_t* quant, int dtype, int block_m,
+                    void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
+                    int32_t* topk_ids_out, void* stream) {
+  return fused_impl(x, router_logits, M, H, I, E, topk, routing, w13, w13_scales, w13_zeros, w2,
+                    w2_scales, w2_zeros, quant, dtype, block_m, workspace, workspace_bytes, out,
+                    topk_weights_out, topk_ids_out, nullptr, nullptr, stream);
+}
+
+size_t fused_moe_wna16_act_order_workspace_size(int M, int H, int I, int E, int topk,
+                                                int dtype, int block_m) {
+  const moe_quant_t q{4, 128, 1};
+  const size_t base = fused_moe_wna16_workspace_size(M, H, I, E, topk, &q, dtype, block_m);
+  return base ? base + act_order_bytes(M, H, I, topk) : 0;
+}
+
+int fused_moe_wna16_act_order(const void* x, const float* router_logits, int M, int H, int I,
+                              int E, int topk, const moe_routing_t* routing, const void* w13,
+                              const void* w13_scales, const void* w13_zeros,
+                              const int32_t* w13_perm, const void* w2, const void* w2_scales,
+                              const void* w2_zeros, const int32_t* w2_perm, int dtype,
+                              int block_m, void* workspace, size_t workspace_bytes, void* out,
+                              float* topk_weights_out, int32_t* topk_ids_out, void* stream) {
+  if (!w13_perm || !w2_perm) return fail(MOE_ERR_INVALID_ARG, "NULL permutation");
+  if (!aligned(w13_perm, 4) || !aligned(w2_perm, 4))
+    return fail(MOE_ERR_INVALID_ARG, "permutations must be 4-byte aligned");
+  const moe_quant_t q{4, 128, 1};
+  return fused_impl(x, router_logits, M, H, I, E, topk, routing, w13, w13_scales, w13_zeros, w2,
+                    w2_scales, w2_zeros, &q, dtype, block_m, workspace, workspace_bytes, out,
+                    topk_weights_out, topk_ids_out, w13_perm, w2_perm, stream);
 }
 
 }  // extern "C"

@@ -182,7 +182,47 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* __restri
   store4<DT>(out + idx * 4, sum_splits(partial + idx * 4, split, split_stride));
 }
 
+// Act-order experts: slot s's activation row through its expert's input-column permutation,
+// out[s, j] = in[s / div, perm[ids[s], j]]; eight columns (one 16-byte store) per thread.  Entries
+// that would index outside the row or the permutation table give zero instead.
+__global__ void __launch_bounds__(256) gather_cols_kernel(const uint16_t* __restrict__ in, int div,
+                                                          const int32_t* __restrict__ ids, int E,
+                                                          const int32_t* __restrict__ perm, int K,
+                                                          int slots, uint16_t* __restrict__ out) {
+  const int k8 = K / 8;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)slots * k8) return;
+  const int s = (int)(idx / k8);
+  const int j0 = (int)(idx - (size_t)s * k8) * 8;
+  const int e = ids[s];
+  const uint16_t* row = in + (size_t)(s / div) * K;
+  uint32_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pj = (unsigned)e < (unsigned)E ? perm[(size_t)e * K + j0 + 2 * i + h] : -1;
+      const uint32_t val = (unsigned)pj < (unsigned)K ? row[pj] : 0u;
+      pair |= val << (16 * h);
+    }
+    v[i] = pair;
+  }
+  *(u32x4_t*)(out + (size_t)s * K + j0) = u32x4_t{v[0], v[1], v[2], v[3]};
+}
+
 }  // namespace
+
+hipError_t launch_gather_cols(const void* in, int div, const int32_t* ids, int E,
+                              const int32_t* perm, int K, int slots, int dtype, void* out,
+                              hipStream_t stream) {
+  (void)dtype;  // 2-byte elements either way
+  const size_t total = (size_t)slots * (K / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_cols_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, (const uint16_t*)in, div, ids, E, perm, K, slots, (uint16_t*)out);
+  return hipGetLastError();
+}
 
 hipError_t launch_split_reduce(const float* partial, int split, int rows, int cols, int dtype,
                                void* out, hipStream_t stream) {

@@ -103,6 +103,11 @@ hipError_t launch_quant_rows(const void* x, int rows, int K, int dtype, int8_t* 
 hipError_t launch_w8a8_gemm(const W8A8Params& p, int block_m, int act, int dtype,
                             hipStream_t stream, int out_f32 = 0);
 
+// out[s, j] = in[s / div, perm[ids[s], j]] for slots s < slots, columns j < K (dtype elements); a
+// permutation entry outside [0, K) or an expert id outside [0, E) gives zero.
+hipError_t launch_gather_cols(const void* in, int div, const int32_t* ids, int E,
+                              const int32_t* perm, int K, int slots, int dtype, void* out,
+                              hipStream_t stream);
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);
 // inter[s, i] = SiLU(sum_z partial[z, s, i]) * sum_z partial[z, s, I + i] (first GEMM split over K)
