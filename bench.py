@@ -12,8 +12,9 @@ Also reported: the roofline of the dominant kernel (the w13 grouped GEMM with th
 timed alone with HIP events on the stream it is launched on; an M sweep of the workload; the CPU
 oracle's throughput on a bounded sample of the same batch; the dense uint4 GEMM at the small-n
 benchmark's shapes (m 16, k 8192, n 128 ... 32768); the grouped GEMM over batched-experts
-activations on an expert-parallel share of 32 DeepSeek-V3-shaped experts; and w8a8 (per-token
-int8 activations) against w8a16 on the DeepSeek-V3 int8 experts.
+activations on an expert-parallel share of 32 DeepSeek-V3-shaped experts; w8a8 (per-token int8
+activations) against w8a16 on the DeepSeek-V3 int8 experts; and the layer with GPTQ act-order
+experts beside the plain layer.
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ def parse():
                     help="skip the batched-experts GEMM sweep (expert-parallel share, 32 experts)")
     ap.add_argument("--no-w8a8", action="store_true",
                     help="skip the w8a8 vs w8a16 first-GEMM comparison (DeepSeek-V3 int8 experts)")
+    ap.add_argument("--no-act-order", action="store_true",
+                    help="skip the act-order layer sweep (same workload, permuted experts)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device-to-device copy (known bytes) so that "
                          "profiler traffic counters can be scaled")
@@ -338,6 +341,32 @@ def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
     return out
 
 
+def act_order_sweep(bench, Ms, steps, warmup):
+    """The same layer as GPTQ act-order experts (fused_moe_wna16_act_order: the activation rows
+    gathered per slot through each expert's input-column permutation before each GEMM) beside the
+    plain fused layer, on the bench's own weight copies with a seeded permutation per expert."""
+    torch, synth, B, wl = bench.torch, bench.synth, bench.B, bench.wl
+    g = torch.Generator(device="cuda").manual_seed(bench.seed)
+    p13 = torch.stack([torch.randperm(wl.H, generator=g, device="cuda") for _ in range(wl.E)]).to(torch.int32)
+    p2 = torch.stack([torch.randperm(wl.I, generator=g, device="cuda") for _ in range(wl.E)]).to(torch.int32)
+    out = []
+    for M in Ms:
+        x = synth.make_x(wl, M, seed=bench.seed, device="cuda")
+        lg = synth.make_logits(wl, M, seed=bench.seed, device="cuda")
+        o = torch.empty((M, wl.H), dtype=wl.torch_dtype, device="cuda")
+        ws = torch.empty((B.lib().fused_moe_wna16_act_order_workspace_size(
+            M, wl.H, wl.I, wl.E, wl.topk, 0 if wl.dtype == "fp16" else 1, 0),), dtype=torch.uint8,
+            device="cuda")
+        L = len(bench.copies)
+        fa = [(lambda c=c: B.fused_moe_wna16_act_order(
+            x, lg, wl.topk, bench.rt, c["w13"], c["w13_scales"], c["w13_zeros"], p13, c["w2"],
+            c["w2_scales"], c["w2_zeros"], p2, workspace=ws, out=o)) for c in bench.copies[:L]]
+        t = graph_replay(fa, steps, warmup)[0] / steps
+        out.append({"M": M, "act_order_us_per_layer": round(t * 1e6, 2)})
+        log(f"[bench] act-order {out[-1]}")
+    return out
+
+
 KERNEL_SOURCES = ("gemm.hip", "common.h", "launch.h", "api.cpp")
 
 
@@ -447,6 +476,13 @@ def main():
         cpu = cpu_baseline(bench, M, x, lg, args.cpu_tokens)
         log(f"[bench] cpu baseline: {cpu}")
 
+    act_order = None
+    if not args.no_act_order and wl.bits == 4:
+        act_order = act_order_sweep(bench, [m for m in wl.Ms if m <= 64] or [M], args.sweep_steps,
+                                    max(10, args.warmup // 4))
+        for r in act_order:
+            plain = next((s["us_per_layer"] for s in sweep if s["M"] == r["M"]), None)
+            r["plain_us_per_layer"] = plain
     dense = None if args.no_dense else dense_sweep(args.sweep_steps, max(10, args.warmup // 4))
     batched = None if args.no_batched else batched_sweep(args.sweep_steps, max(10, args.warmup // 4))
     w8a8 = None if args.no_w8a8 else w8a8_sweep(max(20, args.sweep_steps // 4),
@@ -475,6 +511,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "act_order": act_order,
         "dense_w4a16": dense,
         "batched_experts": batched,
         "w8a8": w8a8,
