@@ -292,3 +292,33 @@ def test_fused_full_size_sampled(name, M):
     r_st, r_ex, r_T = O.align_block_size(ids, wl.E, bm)
     assert int(npost.item()) == r_T and np.array_equal(O.to_numpy(st), r_st)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("bm", [16, 32])
+def test_grouped_gemm_longest_k(bm):
+    """K = 35,840, the longest K the 16- and 32-row kernels accept (their scales and zero points for
+    the whole K range staged in LDS beside the activation tiles, at the 160 KiB limit)."""
+    wl = synth.Workload("lk", E=2, H=35840, I=256, topk=1, Ms=(20,), dtype="fp16", bits=4)
+    layer = synth.make_layer(wl, seed=13)
+    lay = cuda_layer(layer)
+    M = 20
+    x = synth.make_x(wl, M, seed=13)
+    ids = (np.arange(M) % 2).astype(np.int32)[:, None]
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), wl.E, bm)
+    C = B.moe_wna16_gemm(x.cuda(), 1, lay["w13"], lay["w13_scales"], lay["w13_zeros"], st, ex,
+                         npost, bm, M, act=1)
+    torch.cuda.synchronize()
+    src = O.ExpertSource(layer, 4)
+    ref = O.grouped_gemm(x, 1, src.w13, *O.align_block_size(ids, wl.E, bm), bm, M, act=1)
+    assert_layer_close(C, np.stack([ref[s] for s in range(M)]), f"K=35840 bm={bm}")
+
+
+def test_fused_zero_activations_give_zero():
+    """x = 0: every product is exactly zero, so the layer output is exactly zero (also after the
+    SiLU, whose value at 0 is 0, and the float32 combine)."""
+    wl = W["tiny"]
+    layer = cuda_layer(synth.make_layer(wl, seed=2))
+    x = torch.zeros((16, wl.H), dtype=torch.float16, device="cuda")
+    lg = synth.make_logits(wl, 16, seed=2).cuda()
+    out, _, _ = run_fused(wl, x, lg, layer)
+    assert (out.float() == 0).all()
