@@ -302,7 +302,7 @@ def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
         x = synth.make_x(wl, M, seed=seed, device="cuda")
         lg = synth.make_logits(wl, M, seed=seed, device="cuda")
         tw, ti = B.moe_topk_softmax(lg, wl.topk, rt)
-        bm = 64
+        bm = B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype)   # the layers' choice
         st, ex, npost = B.moe_align_block_size(ti, wl.E, bm)
         q, sa = B.moe_quant_int8_rows(x)
         ns = M * wl.topk

@@ -199,7 +199,7 @@ int moe_quant_int8_rows(const void* x, int rows, int K, int dtype, int8_t* q, fl
  *   B        device int8 [E, N, K], w_scales device dtype [E, N] (the int8 weight storage above)
  *   sorted_token_ids / expert_ids / num_tokens_post_padded: moe_align_block_size with block_m
  * Rows of C whose slot is not listed are not written.
- * Limits: block_m in {16, 32, 64}, K % 256 == 0, N % 128 == 0. */
+ * Limits: block_m in {16, 32, 64, 128}, K % 256 == 0, N % 128 == 0. */
 int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_row_div,
                   const int8_t* B, const void* w_scales, int E, int N, int K, int dtype,
                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
@@ -211,8 +211,8 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
  * quantised per slot, w8a8 GEMM2 into float32 rows, top-k weighted combine in float32 (fixed order).
  *   w13 device int8 [E, 2I, H], w13_scales device dtype [E, 2I]; w2 int8 [E, H, I], w2_scales [E, H]
  *   workspace: at least fused_moe_w8a8_workspace_size(...) bytes, 256-byte aligned
- *   block_m 0 = the library's choice (as moe_pick_block_m for int8 weights, at most 64)
- * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, block_m in {0, 16, 32, 64}. */
+ *   block_m 0 = the library's choice (as moe_pick_block_m for int8 weights)
+ * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, block_m in {0, 16, 32, 64, 128}. */
 int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
                    const moe_routing_t* routing, const int8_t* w13, const void* w13_scales,
                    const int8_t* w2, const void* w2_scales, int dtype, int block_m,

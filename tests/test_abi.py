@@ -246,7 +246,7 @@ def test_w8a8_validation(lib):
                                  a["N"], a["K"], a["dt"], a["st"], a["ex"], a["npost"], a["cap"],
                                  a["bm"], a["slots"], a["tw"], a["act"], a["C"], NULL)
 
-    assert w8(bm=128) == UNSUPPORTED
+    assert w8(bm=24) == UNSUPPORTED
     assert w8(K=320) == UNSUPPORTED
     assert w8(N=1000) == UNSUPPORTED
     assert w8(act=3) == INVALID

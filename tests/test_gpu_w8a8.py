@@ -33,7 +33,7 @@ def test_quant_int8_rows_exact(dt, rows, K):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-@pytest.mark.parametrize("bm", [16, 64])
+@pytest.mark.parametrize("bm", [16, 64, 128])
 def test_w8a8_layout_probe_bit_exact(dt, bm):
     """Activation codes one-hot at column k with scale 1, routed to one expert: row k of the output
     is column k of that expert's int8 weights times their channel scales, which must equal the
@@ -58,7 +58,7 @@ def test_w8a8_layout_probe_bit_exact(dt, bm):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 @pytest.mark.parametrize("act,weighted", [(1, False), (0, True)])
 def test_w8a8_gemm_vs_oracle(dt, bm, act, weighted):
     wl = synth.Workload("g8", E=6, H=768, I=512, topk=3, Ms=(45,), dtype=dt, bits=8)

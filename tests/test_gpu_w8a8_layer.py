@@ -47,7 +47,7 @@ def test_fused_w8a8_vs_oracle(name):
     assert_layer_close(out, ref, f"w8a8 {name}")
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_fused_w8a8_block_sizes_deterministic(bm):
     wl = SMALL["softmax_fp16"]
     out1, x, ids, w, lay = _run(wl, 33, seed=6, block_m=bm)

@@ -539,8 +539,8 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
                 num_a_rows, a_row_div, num_slots);
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL)
     return fail(MOE_ERR_INVALID_ARG, "act = %d", act);
-  if (block_m != 16 && block_m != 32 && block_m != 64)
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64)", block_m);
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
   if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
   if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
   if ((int64_t)num_a_rows * K >= ((int64_t)1 << 31) || (int64_t)N * K >= ((int64_t)1 << 31))
@@ -591,7 +591,7 @@ struct PlanW8 {
 PlanW8 make_plan_w8(int M, int H, int I, int E, int topk, int dtype, int block_m) {
   PlanW8 p{};
   const int64_t slots = (int64_t)M * topk;
-  p.bm = block_m > 0 ? block_m : std::min(64, pick_block_m(M, topk, E, 8, dtype));
+  p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E, 8, dtype);
   p.cap = align_capacity(slots, E, p.bm);
   const int64_t nblk = (p.cap + p.bm - 1) / p.bm;
   size_t off = 0;
@@ -613,7 +613,7 @@ PlanW8 make_plan_w8(int M, int H, int I, int E, int topk, int dtype, int block_m
 
 size_t fused_moe_w8a8_workspace_size(int M, int H, int I, int E, int topk, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;
-  if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64) return 0;
+  if (block_m != 0 && !valid_block_m(block_m)) return 0;
   return make_plan_w8(M, H, I, E, topk, dtype, block_m).total;
 }
 
@@ -625,8 +625,8 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
   if (int rc = check_dtype(dtype)) return rc;
   if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d H=%d I=%d", M, H, I);
   if (int rc = check_routing(routing, E, topk)) return rc;
-  if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64)
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64)", block_m);
+  if (block_m != 0 && !valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128)", block_m);
   if (H % 256 || I % 256)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");

@@ -240,7 +240,9 @@ hipError_t launch_w8a8_ntw(const W8A8Params& p, int act, int out_f32, hipStream_
 // many workgroups and the M = 1024 layer measured 4 % slower).
 template <int DT, int MT>
 hipError_t launch_w8a8_mt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
-  if (act && (p.N / 2) % 128 == 0) return launch_w8a8_ntw<DT, MT, 4>(p, act, out_f32, stream);
+  if constexpr (MT <= 4) {  // 128 rows: eight row tiles already reuse each fragment, registers bound
+    if (act && (p.N / 2) % 128 == 0) return launch_w8a8_ntw<DT, MT, 4>(p, act, out_f32, stream);
+  }
   return launch_w8a8_ntw<DT, MT, 2>(p, act, out_f32, stream);
 }
 
@@ -251,6 +253,7 @@ hipError_t launch_w8a8_dt(const W8A8Params& p, int block_m, int act, int out_f32
     case 16: return launch_w8a8_mt<DT, 1>(p, act, out_f32, stream);
     case 32: return launch_w8a8_mt<DT, 2>(p, act, out_f32, stream);
     case 64: return launch_w8a8_mt<DT, 4>(p, act, out_f32, stream);
+    case 128: return launch_w8a8_mt<DT, 8>(p, act, out_f32, stream);
     default: return hipErrorInvalidValue;
   }
 }
