@@ -102,6 +102,8 @@ int64_t moe_align_capacity(int numel, int E, int block_m);
  *   expert_ids device int32 [ceil(capacity / block_m)] (out): expert of each block, -1 past T.
  *   num_tokens_post_padded device int32 [1] (out): T, the padded total (stays on the device).
  * Ids outside [0, E) are not listed (a slot of another shard).  The result is deterministic.
+ * numel = 0 writes T = 0 (and sentinels / -1 over any capacity given); with capacity 0 the
+ * sorted_token_ids and expert_ids pointers may be NULL.
  * Limits: 1 <= E <= 1024, block_m in {16, 32, 64, 128}, numel <= 2^24,
  * capacity >= moe_align_capacity(numel, E, block_m) (else MOE_ERR_CAPACITY). */
 int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
@@ -121,7 +123,8 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
  *   B, scales, zeros: weight storage of E experts with N rows and K columns (zeros NULL for int8)
  *   sorted_token_ids/expert_ids/num_tokens_post_padded: output of moe_align_block_size
  *     with the same block_m; capacity = length of sorted_token_ids.
- * Rows of C whose slot is not listed are not written.
+ * Rows of C whose slot is not listed are not written.  num_slots = 0 returns MOE_OK at once
+ * (no pointer is checked or touched).
  * Limits: K % 256 == 0, N % 128 == 0, block_m in
  * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots.  uint4 at block_m 16 and 32: a
  * workgroup stages the scales and zero points of its whole K range in LDS beside its activation
@@ -198,7 +201,7 @@ int moe_quant_int8_rows(const void* x, int rows, int K, int dtype, int8_t* q, fl
  *   A        device int8 [num_a_rows, K], a_scales device float [num_a_rows] (moe_quant_int8_rows)
  *   B        device int8 [E, N, K], w_scales device dtype [E, N] (the int8 weight storage above)
  *   sorted_token_ids / expert_ids / num_tokens_post_padded: moe_align_block_size with block_m
- * Rows of C whose slot is not listed are not written.
+ * Rows of C whose slot is not listed are not written.  num_slots = 0 returns MOE_OK at once.
  * Limits: block_m in {16, 32, 64, 128}, K % 256 == 0, N % 128 == 0. */
 int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_row_div,
                   const int8_t* B, const void* w_scales, int E, int N, int K, int dtype,

@@ -134,6 +134,7 @@ def test_gemm_validation(lib):
     assert _gemm(lib, A=ctypes.c_void_p(0x100008)) == INVALID  # A not 16-byte aligned
     assert _gemm(lib, Bw=NULL) == INVALID
     assert _gemm(lib, slots=0) == OK                           # nothing to do, no launch
+    assert _gemm(lib, slots=0, rows=0, A=NULL, C=NULL, st=NULL, ex=NULL, npost=NULL) == OK
     # uint4 scales of the whole K range must fit in LDS beside the activation tiles
     assert _gemm(lib, K=36096 + 256, bm=16) == UNSUPPORTED
     assert b"LDS" in lib.moe_last_error()
@@ -247,6 +248,7 @@ def test_w8a8_validation(lib):
                                  a["bm"], a["slots"], a["tw"], a["act"], a["C"], NULL)
 
     assert w8(bm=24) == UNSUPPORTED
+    assert w8(slots=0, rows=0, A=NULL, sa=NULL, C=NULL, st=NULL, ex=NULL, npost=NULL) == OK
     assert w8(K=320) == UNSUPPORTED
     assert w8(N=1000) == UNSUPPORTED
     assert w8(act=3) == INVALID

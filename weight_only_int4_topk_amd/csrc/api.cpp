@@ -313,7 +313,9 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
   if (!valid_block_m(block_m))
     return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
   if (numel > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "numel = %d > 2^24", numel);
-  if ((numel > 0 && !topk_ids) || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
+  // an empty batch still gets its padded total (0) written; its id buffers may then be empty
+  if ((numel > 0 && !topk_ids) || (capacity > 0 && (!sorted_token_ids || !expert_ids)) ||
+      !num_tokens_post_padded)
     return fail(MOE_ERR_INVALID_ARG, "NULL align buffer");
   if (!aligned(topk_ids, 4) || !aligned(sorted_token_ids, 4) || !aligned(expert_ids, 4) ||
       !aligned(num_tokens_post_padded, 4))
@@ -363,6 +365,7 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
   if ((int64_t)num_a_rows * a_row_div < num_slots)
     return fail(MOE_ERR_INVALID_ARG, "A has %d rows, slots need %lld", num_a_rows,
                 (long long)((num_slots + a_row_div - 1) / a_row_div));
+  if (num_slots == 0) return MOE_OK;  // nothing to read or write
   if (int rc = check_weights(B, scales, zeros, quant)) return rc;
   if (!A || !C || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
     return fail(MOE_ERR_INVALID_ARG, "NULL A / C / align buffer");
@@ -548,6 +551,7 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
   if ((int64_t)num_a_rows * a_row_div < num_slots)
     return fail(MOE_ERR_INVALID_ARG, "A has %d rows, slots need %lld", num_a_rows,
                 (long long)((num_slots + a_row_div - 1) / a_row_div));
+  if (num_slots == 0) return MOE_OK;  // nothing to read or write
   if (!A || !a_scales || !B || !w_scales || !C || !sorted_token_ids || !expert_ids ||
       !num_tokens_post_padded)
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
