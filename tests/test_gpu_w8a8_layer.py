@@ -72,3 +72,23 @@ def test_fused_w8a8_mixtral_shape_sampled():
     ids_sub = np.vectorize(lambda e: remap.get(int(e), 0))(ids)
     ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows)
     assert_layer_close(O.to_numpy(out)[rows], ref, "w8a8 mixtral")
+
+
+@pytest.mark.parametrize("M", [1024, 4096])
+def test_fused_w8a8_dsv3_full_size_sampled(M):
+    """DeepSeek-V3-shaped int8 experts (256 x H 7168 x I 2048, bf16, grouped sigmoid top-8) at the
+    batch sizes the bench times, with the library's block size (64 rows at 1024 tokens, 128 at
+    4096); every token's routing exact, three tokens' outputs against the oracle."""
+    wl = synth.WORKLOADS["dsv3_prefill_int8"]
+    assert B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype) == (64 if M == 1024 else 128)
+    out, x, ids, w, lay = _run(wl, M, seed=0, device="cuda")
+    print(f"fused w8a8 dsv3 full size M={M}", flush=True)
+    rows = [0, M // 2 + 3, M - 1]
+    experts = sorted(set(ids[rows].reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
+    del lay
+    remap = {e: i for i, e in enumerate(experts)}
+    ids_sub = np.vectorize(lambda e: remap.get(int(e), 0))(ids)
+    ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows)
+    assert_layer_close(O.to_numpy(out)[rows], ref, f"w8a8 dsv3 M={M}")
