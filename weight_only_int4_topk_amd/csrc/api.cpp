@@ -121,10 +121,10 @@ int pick_block_m(int M, int topk, int E, int bits, int dtype) {
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Column tiles of 16 per wavefront for a grouped GEMM with N weight rows.  Four tiles halve the
-// activation traffic per weight byte; they need block_m 16 (at 32 the kernel's registers leave room
-// for two wavefronts per SIMD against three with 2 tiles, and three stream faster), N divisible by
-// the wider workgroup, and (for the SiLU epilogue, whose grid is narrower) enough workgroups to
-// fill the chip.
+// activation traffic per weight byte; they need block_m 16 (at 32 the 4-tile kernel takes 211
+// registers, two wavefronts per SIMD, against 128 and four with 2 tiles, and more wavefronts stream
+// faster), N divisible by the wider workgroup, and (for the SiLU epilogue, whose grid is narrower)
+// enough workgroups to fill the chip.
 int pick_ntw(int act, int N, int bm, int64_t est_blocks) {
   if (bm > 16) return 2;
   if (act) return ((N / 2) % 128 == 0 && est_blocks * ((N / 2) / 128) >= 1024) ? 4 : 2;
