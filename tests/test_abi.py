@@ -264,3 +264,69 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_binding_rejects_mis_shaped_tensors():
+    """The binding checks every tensor against the sizes it passes to the library (which trusts
+    them) before any pointer is taken: CPU tensors of the wrong shape or dtype raise here."""
+    import torch
+    import weight_only_int4_topk_amd as B
+
+    def raises(fn, what):
+        with pytest.raises(B.MoeError, match=what):
+            fn()
+
+    E, H, I, M, k = 8, 256, 256, 4, 2
+    lg = torch.zeros(M, E)
+    raises(lambda: B.moe_topk_softmax(lg, k, B.routing(), topk_ids=torch.zeros(M, 3, dtype=torch.int32)),
+           "topk_ids has shape")
+    raises(lambda: B.moe_topk_softmax(lg.double(), k, B.routing()), "logits has dtype")
+    raises(lambda: B.moe_align_block_size(torch.zeros(8, dtype=torch.int64), E, 16),
+           "topk_ids has dtype")
+    x = torch.zeros(M, H, dtype=torch.float16)
+    w13 = torch.zeros(E, 2 * I, H // 2, dtype=torch.uint8)
+    s13 = torch.zeros(E, 2 * I, H // 128, dtype=torch.float16)
+    z13 = torch.zeros(E, 2 * I, H // 256, dtype=torch.uint8)
+    w2 = torch.zeros(E, H, I // 2, dtype=torch.uint8)
+    s2 = torch.zeros(E, H, I // 128, dtype=torch.float16)
+    z2 = torch.zeros(E, H, I // 256, dtype=torch.uint8)
+    args = (x, lg, k, B.routing(), w13, s13, z13, w2, s2, z2)
+    raises(lambda: B.fused_moe_wna16(*args, out=torch.zeros(M, H - 8, dtype=torch.float16)),
+           "out has shape")
+    raises(lambda: B.fused_moe_wna16(*args, out=torch.zeros(M, H, dtype=torch.bfloat16)),
+           "out has dtype")
+    raises(lambda: B.fused_moe_wna16(*args, topk_ids=torch.zeros(M, k, dtype=torch.int64)),
+           "topk_ids has dtype")
+    raises(lambda: B.fused_moe_wna16(x, lg, k, B.routing(), w13, s13.bfloat16(), z13, w2, s2, z2),
+           "w13 scales has dtype")
+    raises(lambda: B.fused_moe_wna16(x, lg, k, B.routing(), w13, s13, z13, w2, s2[:, :, :1], z2),
+           "w2 scales has shape")
+    raises(lambda: B.fused_moe_wna16(x, lg[:, :4], k, B.routing(), w13, s13, z13, w2, s2, z2),
+           "router_logits has shape")
+    st = torch.zeros(152, dtype=torch.int32)
+    ex = torch.zeros(10, dtype=torch.int32)
+    npost = torch.zeros(1, dtype=torch.int32)
+    raises(lambda: B.moe_wna16_gemm(x, k, w13, s13, z13, st, ex, npost, 16, M * k, act=1,
+                                    C=torch.zeros(M * k, 2 * I, dtype=torch.float16)), "C has shape")
+    raises(lambda: B.moe_wna16_gemm(x, k, w13, s13, z13, st, ex[:5], npost, 16, M * k, act=1),
+           "expert_ids holds")
+    raises(lambda: B.moe_wna16_gemm(x, k, w13, s13, z13, st, ex, npost, 16, M * k, act=1,
+                                    topk_weights=torch.zeros(M * k - 1)), "topk_weights holds")
+    raises(lambda: B.moe_wna16_dense_gemm(x, w13[0], s13[0], z13[0],
+                                          C=torch.zeros(M, 2 * I + 16, dtype=torch.float16)),
+           "C has shape")
+    raises(lambda: B.moe_quant_int8_rows(x, q=torch.zeros(M, H, dtype=torch.uint8)), "q has dtype")
+    w8 = torch.zeros(E, 2 * I, H, dtype=torch.int8)
+    raises(lambda: B.moe_w8a8_gemm(torch.zeros(M, H, dtype=torch.int8), torch.zeros(M), k, w8,
+                                   torch.zeros(E, 2 * I, dtype=torch.float16), st, ex, npost, 16,
+                                   M * k, torch.bfloat16, act=1), "B scales has dtype")
+    raises(lambda: B.fused_moe_w8a8(x, lg, k, B.routing(), w8, torch.zeros(E, 2 * I, dtype=torch.float16),
+                                    torch.zeros(E, H, I + 256, dtype=torch.int8),
+                                    torch.zeros(E, H, dtype=torch.float16)), "w2 has shape")
+    raises(lambda: B.fused_moe_wna16_act_order(x, lg, k, B.routing(), w13, s13, z13,
+                                               torch.zeros(E, H, dtype=torch.int64), w2, s2, z2,
+                                               torch.zeros(E, I, dtype=torch.int32)),
+           "w13_perm has dtype")
+    raises(lambda: B.moe_wna16_batched_gemm(torch.zeros(E, 16, H, dtype=torch.float16),
+                                            torch.zeros(E - 1, dtype=torch.int32), w13, s13, z13, act=1),
+           "expert_num_tokens has shape")

@@ -13,9 +13,11 @@ import os
 import torch
 
 __all__ = [
-    "MoeError", "lib", "QUANT_INT4", "QUANT_INT8", "routing", "moe_topk_softmax",
-    "moe_align_capacity", "moe_align_block_size", "moe_pick_block_m", "moe_wna16_gemm",
-    "fused_moe_wna16_workspace_size", "fused_moe_wna16", "LIB_PATH",
+    "MoeError", "MoeQuant", "MoeRouting", "lib", "LIB_PATH", "QUANT_INT4", "QUANT_INT8", "routing",
+    "moe_topk_softmax", "moe_align_capacity", "moe_align_block_size", "moe_pick_block_m",
+    "moe_wna16_gemm", "moe_wna16_dense_gemm", "moe_wna16_dense_gemm_workspace_size",
+    "moe_wna16_batched_gemm", "moe_quant_int8_rows", "moe_w8a8_gemm", "fused_moe_w8a8",
+    "fused_moe_wna16_act_order", "fused_moe_wna16_workspace_size", "fused_moe_wna16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wna16.so")
@@ -130,6 +132,41 @@ def _quant_of(B: torch.Tensor, zeros) -> MoeQuant:
     raise MoeError(-2, f"weights of dtype {B.dtype} with zeros={'set' if zeros is not None else 'None'}")
 
 
+# The library takes plain pointers and trusts the sizes passed beside them, so every tensor is
+# checked here against the shape those sizes imply before its pointer is handed over.
+def _want(t, shape, dtype, name):
+    """Raise unless t (when given) has exactly this shape and dtype."""
+    if t is None:
+        return
+    shape = tuple(int(s) for s in shape)
+    if tuple(t.shape) != shape:
+        raise MoeError(-1, f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if dtype is not None and t.dtype != dtype:
+        raise MoeError(-1, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _want_len(t, n, dtype, name):
+    """Raise unless t (when given) holds at least n elements of this dtype."""
+    if t is None:
+        return
+    if t.numel() < n:
+        raise MoeError(-1, f"{name} holds {t.numel()} elements, needs {n}")
+    if t.dtype != dtype:
+        raise MoeError(-1, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _want_weights(name, B, scales, zeros, lead, N, K, act_dtype):
+    """Weight storage of the header's layouts; lead = (E,) for experts, () for one matrix."""
+    lead = tuple(lead)
+    if B.dtype == torch.uint8:
+        _want(B, lead + (N, K // 2), torch.uint8, name)
+        _want(scales, lead + (N, K // 128), act_dtype, name + " scales")
+        _want(zeros, lead + (N, K // 256), torch.uint8, name + " zeros")
+    else:
+        _want(B, lead + (N, K), torch.int8, name)
+        _want(scales, lead + (N,), act_dtype, name + " scales")
+
+
 def routing(score="softmax", renormalize=True, num_groups=1, topk_groups=1, scale=1.0) -> MoeRouting:
     return MoeRouting(0 if score == "softmax" else 1, int(bool(renormalize)), num_groups,
                       topk_groups, float(scale))
@@ -137,6 +174,9 @@ def routing(score="softmax", renormalize=True, num_groups=1, topk_groups=1, scal
 
 def moe_topk_softmax(logits, topk, rt: MoeRouting, topk_weights=None, topk_ids=None, stream=None):
     M, E = logits.shape
+    _want(logits, (M, E), torch.float32, "logits")
+    _want(topk_weights, (M, topk), torch.float32, "topk_weights")
+    _want(topk_ids, (M, topk), torch.int32, "topk_ids")
     if topk_weights is None:
         topk_weights = torch.empty((M, topk), dtype=torch.float32, device=logits.device)
     if topk_ids is None:
@@ -157,6 +197,7 @@ def moe_align_capacity(numel, E, block_m) -> int:
 
 def moe_align_block_size(topk_ids, E, block_m, capacity=None, stream=None):
     numel = topk_ids.numel()
+    _want_len(topk_ids, numel, torch.int32, "topk_ids")
     cap = moe_align_capacity(numel, E, block_m) if capacity is None else capacity
     dev = topk_ids.device
     sorted_ids = torch.empty((cap,), dtype=torch.int32, device=dev)
@@ -173,6 +214,15 @@ def moe_wna16_gemm(A, a_row_div, B, scales, zeros, sorted_ids, expert_ids, num_p
     E, N = B.shape[0], B.shape[1]
     K = B.shape[2] * (2 if quant.bits == 4 else 1)
     n_out = N // 2 if act == 1 else N
+    _want(A, (A.shape[0], K), A.dtype, "A")
+    _dtype_code(A.dtype)
+    _want_weights("B", B, scales, zeros, (E,), N, K, A.dtype)
+    _want_len(sorted_ids, sorted_ids.numel(), torch.int32, "sorted_ids")
+    _want_len(expert_ids, -(-sorted_ids.numel() // block_m) if block_m > 0 else 0, torch.int32,
+              "expert_ids")
+    _want_len(num_post, 1, torch.int32, "num_post")
+    _want_len(topk_weights, num_slots, torch.float32, "topk_weights")
+    _want(C, (num_slots, n_out), A.dtype, "C")
     if C is None:
         C = torch.empty((num_slots, n_out), dtype=A.dtype, device=A.device)
     _check(lib().moe_wna16_gemm(_ptr(A), A.shape[0], a_row_div, _ptr(B), _ptr(scales), _ptr(zeros),
@@ -193,6 +243,8 @@ def moe_wna16_dense_gemm(A, B, scales, zeros=None, workspace=None, C=None, strea
     quant = _quant_of(B, zeros)
     M, K = A.shape
     N = B.shape[0]
+    _want_weights("B", B, scales, zeros, (), N, K, A.dtype)
+    _want(C, (M, N), A.dtype, "C")
     need = moe_wna16_dense_gemm_workspace_size(M, N, K, quant, A.dtype)
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=A.device)
@@ -211,6 +263,9 @@ def moe_wna16_batched_gemm(A, expert_num_tokens, B, scales, zeros=None, act=0, b
     quant = _quant_of(B, zeros)
     E, T, K = A.shape
     N = B.shape[1]
+    _want_weights("B", B, scales, zeros, (E,), N, K, A.dtype)
+    _want(expert_num_tokens, (E,), torch.int32, "expert_num_tokens")
+    _want(C, (E, T, N // 2 if act == 1 else N), A.dtype, "C")
     if C is None:
         C = torch.empty((E, T, N // 2 if act == 1 else N), dtype=A.dtype, device=A.device)
     _check(lib().moe_wna16_batched_gemm(_ptr(A), E, T, K, _ptr(expert_num_tokens), _ptr(B),
@@ -223,6 +278,8 @@ def moe_wna16_batched_gemm(A, expert_num_tokens, B, scales, zeros=None, act=0, b
 def moe_quant_int8_rows(x, q=None, scales=None, stream=None):
     """(q int8 [R, K], scales float [R]) = per-row symmetric int8 of x [R, K] (fp16/bf16)."""
     R, K = x.shape
+    _want(q, (R, K), torch.int8, "q")
+    _want(scales, (R,), torch.float32, "scales")
     if q is None:
         q = torch.empty((R, K), dtype=torch.int8, device=x.device)
     if scales is None:
@@ -237,6 +294,16 @@ def moe_w8a8_gemm(Aq, a_scales, a_row_div, B, w_scales, sorted_ids, expert_ids, 
     """Grouped GEMM of int8 activations (per-row scales) with int8 weights (per-channel scales)."""
     E, N, K = B.shape
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    odt = torch.float16 if code == 0 else torch.bfloat16
+    _want(Aq, (Aq.shape[0], K), torch.int8, "Aq")
+    _want(a_scales, (Aq.shape[0],), torch.float32, "a_scales")
+    _want_weights("B", B, w_scales, None, (E,), N, K, odt)
+    _want_len(expert_ids, -(-sorted_ids.numel() // block_m) if block_m > 0 else 0, torch.int32,
+              "expert_ids")
+    _want_len(sorted_ids, sorted_ids.numel(), torch.int32, "sorted_ids")
+    _want_len(num_post, 1, torch.int32, "num_post")
+    _want_len(topk_weights, num_slots, torch.float32, "topk_weights")
+    _want(C, (num_slots, N // 2 if act == 1 else N), odt, "C")
     if C is None:
         C = torch.empty((num_slots, N // 2 if act == 1 else N),
                         dtype=torch.float16 if code == 0 else torch.bfloat16, device=Aq.device)
@@ -247,6 +314,15 @@ def moe_w8a8_gemm(Aq, a_scales, a_row_div, B, w_scales, sorted_ids, expert_ids, 
     return C
 
 
+def _want_layer_io(x, router_logits, E, topk, out, topk_weights, topk_ids):
+    M, H = x.shape
+    _dtype_code(x.dtype)
+    _want(router_logits, (M, E), torch.float32, "router_logits")
+    _want(out, (M, H), x.dtype, "out")
+    _want(topk_weights, (M, topk), torch.float32, "topk_weights")
+    _want(topk_ids, (M, topk), torch.int32, "topk_ids")
+
+
 def fused_moe_w8a8(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w2, w2_scales,
                    block_m=0, workspace=None, out=None, topk_weights=None, topk_ids=None,
                    stream=None):
@@ -255,6 +331,9 @@ def fused_moe_w8a8(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w2, 
     E, I2, _ = w13.shape
     I = I2 // 2
     code = _dtype_code(x.dtype)
+    _want_layer_io(x, router_logits, E, topk, out, topk_weights, topk_ids)
+    _want_weights("w13", w13, w13_scales, None, (E,), 2 * I, H, x.dtype)
+    _want_weights("w2", w2, w2_scales, None, (E,), H, I, x.dtype)
     need = int(lib().fused_moe_w8a8_workspace_size(M, H, I, E, topk, code, block_m))
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
@@ -276,6 +355,11 @@ def fused_moe_wna16_act_order(x, router_logits, topk, rt: MoeRouting, w13, w13_s
     E = w13.shape[0]
     I = w13.shape[1] // 2
     code = _dtype_code(x.dtype)
+    _want_layer_io(x, router_logits, E, topk, out, topk_weights, topk_ids)
+    _want_weights("w13", w13, w13_scales, w13_zeros, (E,), 2 * I, H, x.dtype)
+    _want_weights("w2", w2, w2_scales, w2_zeros, (E,), H, I, x.dtype)
+    _want(w13_perm, (E, H), torch.int32, "w13_perm")
+    _want(w2_perm, (E, I), torch.int32, "w2_perm")
     need = int(lib().fused_moe_wna16_act_order_workspace_size(M, H, I, E, topk, code, block_m))
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
@@ -303,6 +387,9 @@ def fused_moe_wna16(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w13
     M, H = x.shape
     E = w13.shape[0]
     I = w13.shape[1] // 2
+    _want_layer_io(x, router_logits, E, topk, out, topk_weights, topk_ids)
+    _want_weights("w13", w13, w13_scales, w13_zeros, (E,), 2 * I, H, x.dtype)
+    _want_weights("w2", w2, w2_scales, w2_zeros, (E,), H, I, x.dtype)
     need = fused_moe_wna16_workspace_size(M, H, I, E, topk, quant, x.dtype, block_m)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
