@@ -164,6 +164,10 @@ def test_fused_validation_and_workspace(lib):
 
     assert fused(wsb=ws - 1) == WORKSPACE
     assert b"workspace" in lib.moe_last_error()
+    # DeepSeek-V3 prefill shape: 65535 tokens keep the intermediate under 2 GiB, 65536 do not
+    big = dict(H=7168, I=2048, E=256, k=8, bm=0, wsb=1 << 62)
+    assert fused(M=65536, **big) == UNSUPPORTED
+    assert b"2 GiB" in lib.moe_last_error()
     assert fused(H=320) == UNSUPPORTED
     assert fused(I=200) == UNSUPPORTED
     assert fused(bm=8) == UNSUPPORTED
