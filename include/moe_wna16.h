@@ -215,7 +215,8 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
  *   w13 device int8 [E, 2I, H], w13_scales device dtype [E, 2I]; w2 int8 [E, H, I], w2_scales [E, H]
  *   workspace: at least fused_moe_w8a8_workspace_size(...) bytes, 256-byte aligned
  *   block_m 0 = the library's choice (as moe_pick_block_m for int8 weights)
- * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, block_m in {0, 16, 32, 64, 128}. */
+ * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, block_m in {0, 16, 32, 64, 128},
+ * M * topk <= 2^24, and below 2^31 (32-bit offsets): M * H, M * topk * I and 2I * H. */
 int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
                    const moe_routing_t* routing, const int8_t* w13, const void* w13_scales,
                    const int8_t* w2, const void* w2_scales, int dtype, int block_m,
@@ -274,7 +275,9 @@ size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, cons
  *   block_m       0 = library's choice, else one of {16, 32, 64, 128}
  * Launches: routing, align, GEMM1 (+SiLU*up), GEMM2 (split over K into float32 partials),
  * combine.  Deterministic: identical inputs give bitwise identical outputs.
- * Limits: those of the calls above with N = 2I and N = H; H % 256 == 0, I % 256 == 0. */
+ * Limits: those of the calls above with N = 2I and N = H; H % 256 == 0, I % 256 == 0,
+ * M * topk <= 2^24, and below 2^31 bytes (32-bit offsets): x (M * H * 2), the intermediate rows
+ * (M * topk * I * 2) and one expert's w13. */
 int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
                     const moe_routing_t* routing, const void* w13, const void* w13_scales,
                     const void* w13_zeros, const void* w2, const void* w2_scales,

@@ -262,6 +262,17 @@ def test_w8a8_validation(lib):
     assert w8(dt=5) == UNSUPPORTED
     assert w8(slots=0) == OK
 
+    def fused8(M, wsb, H=7168, I=2048, E=256, k=8):
+        return lib.fused_moe_w8a8(FAKE, FAKE, M, H, I, E, k, _rt(), FAKE, FAKE, FAKE, FAKE, 1, 0,
+                                  FAKE, wsb, FAKE, NULL, NULL, NULL)
+
+    # DeepSeek-V3 int8 shape: the second GEMM's int8 activations (M * topk * I bytes) bound the
+    # batch at 131071 tokens; the float32 rows after it are addressed with 64 bits.  (A one-byte
+    # workspace stops the accepted call at its workspace check, before any launch.)
+    assert fused8(131072, 1 << 62) == UNSUPPORTED
+    assert b"2 GiB" in lib.moe_last_error()
+    assert fused8(131071, 1) == WORKSPACE
+
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))

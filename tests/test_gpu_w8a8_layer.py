@@ -92,3 +92,34 @@ def test_fused_w8a8_dsv3_full_size_sampled(M):
     ids_sub = np.vectorize(lambda e: remap.get(int(e), 0))(ids)
     ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows)
     assert_layer_close(O.to_numpy(out)[rows], ref, f"w8a8 dsv3 M={M}")
+
+
+def test_fused_w8a8_largest_batch_sampled():
+    """The largest batch the w8a8 layer accepts at the DeepSeek-V3 int8 shape: M = 131071 keeps the
+    second GEMM's int8 activations (M * topk * I bytes) under 2 GiB, one token more is refused.
+    Its float32 rows then take 30 GB and the combine reads them past 2^34 bytes.  First, middle and
+    last token against the oracle, their routing exact."""
+    wl = synth.WORKLOADS["dsv3_prefill_int8"]
+    M = 131071
+    assert M * wl.topk * wl.I < 2**31 <= (M + 1) * wl.topk * wl.I
+    lay = synth.make_layer(wl, seed=0, device="cuda")
+    x = synth.make_x(wl, M, seed=0, device="cuda")
+    lg = synth.make_logits(wl, M, seed=0, device="cuda")
+    ti = torch.empty((M, wl.topk), dtype=torch.int32, device="cuda")
+    tw = torch.empty((M, wl.topk), dtype=torch.float32, device="cuda")
+    print(f"fused w8a8 largest batch M={M}", flush=True)
+    out = B.fused_moe_w8a8(x, lg, wl.topk, routing_of(wl), lay["w13"], lay["w13_scales"],
+                           lay["w2"], lay["w2_scales"], topk_weights=tw, topk_ids=ti)
+    torch.cuda.synchronize()
+    rows = [0, M // 2, M - 1]
+    ids, w = oracle_route(wl, lg[rows])                   # routing is per token
+    assert np.array_equal(O.to_numpy(ti)[rows], ids)
+    experts = sorted(set(ids.reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
+    del lay
+    remap = {e: i for i, e in enumerate(experts)}
+    ids_sub = np.vectorize(lambda e: remap[int(e)])(ids)
+    ref = O.moe_layer_w8a8_rows(x[rows].cpu(), ids_sub, w, sub, wl.dtype)
+    assert_layer_close(O.to_numpy(out)[rows], ref, f"w8a8 dsv3 M={M}")
+    assert torch.isfinite(out[-4096:].float()).all()

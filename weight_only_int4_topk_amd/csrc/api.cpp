@@ -634,8 +634,11 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
   if (H % 256 || I % 256)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");
-  if ((int64_t)M * topk * H * 4 >= ((int64_t)1 << 31) || (int64_t)2 * I * H >= ((int64_t)1 << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "intermediate rows or one expert's weights exceed 2 GiB");
+  // 32-bit buffer offsets: the int8 activations of either GEMM, one expert's weights (the float32
+  // rows of the second GEMM and the combine use 64-bit addresses)
+  if ((int64_t)M * H >= ((int64_t)1 << 31) || (int64_t)M * topk * I >= ((int64_t)1 << 31) ||
+      (int64_t)2 * I * H >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "int8 activations or one expert's weights exceed 2 GiB");
   if (M == 0) return MOE_OK;
   if (!x || !router_logits || !out || !workspace || !w13 || !w13_scales || !w2 || !w2_scales)
     return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
