@@ -174,7 +174,8 @@ size_t moe_wna16_dense_gemm_workspace_size(int M, int N, int K, const moe_quant_
  *   C     device dtype [E, max_tokens, N] (act 1: N/2 columns); rows at or past an expert's count
  *         are not written
  *   block_m 0 = the smallest of {16, 32, 64} (int8: 128) that holds max_tokens
- * Limits: 1 <= E <= 1024, K % 256 == 0, N % 128 == 0, the uint4 K limits of moe_wna16_gemm. */
+ * Limits: 1 <= E <= 1024, K % 256 == 0, N % 128 == 0, the uint4 K limits of moe_wna16_gemm,
+ * below 2^31 bytes (32-bit offsets): A (E * max_tokens * K * 2) and one expert's weights. */
 int moe_wna16_batched_gemm(const void* A, int E, int max_tokens, int K,
                            const int32_t* expert_num_tokens, const void* B, const void* scales,
                            const void* zeros, const moe_quant_t* quant, int N, int dtype,

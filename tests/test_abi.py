@@ -234,6 +234,12 @@ def test_batched_gemm_validation(lib):
     assert batched(C=ctypes.c_void_p(0x100008)) == INVALID
     assert batched(Z=NULL) == INVALID
     assert batched(T=0) == OK                                  # nothing to do, no launch
+    # A (rows * K * 2 bytes) is bounded at 2 GiB, C (rows * N * 2) is not: 64 experts x 4096
+    # tokens, K 2048, N 7168 (C 3.8 GB) passes the size checks and stops at C's alignment
+    big = dict(E=64, T=4096, K=2048, N=7168, act=0)
+    assert batched(C=ctypes.c_void_p(0x100008), **big) == INVALID
+    assert b"alignment" in lib.moe_last_error()
+    assert batched(C=ctypes.c_void_p(0x100008), **{**big, "T": 8192}) == UNSUPPORTED  # A: 2 GiB
 
 
 def test_w8a8_validation(lib):

@@ -74,3 +74,27 @@ def test_batched_expert_parallel_share_sampled():
         keys = sorted(ref)
         assert_layer_close(torch.stack([C[e, r].cpu() for _, r in keys]),
                            np.stack([ref[k] for k in keys]), f"expert {e}")
+
+
+def test_batched_output_past_4_gib():
+    """The output is addressed with 64 bits: 80 experts x 4096 tokens through a DeepSeek-V3 w2
+    (K 2048 -> N 7168, uint4, bf16) give a 4.7 GB C (A stays at 1.3 GB, under its 2 GiB bound); the
+    last 8 rows of the first and the last expert, the latter past 2^32 bytes, against the oracle."""
+    E, T, K, N = 80, 4096, 2048, 7168
+    assert E * T * N * 2 > 2**32 and E * T * K * 2 < 2**31
+    wl = synth.Workload("ep_big", E=E, H=N, I=K, topk=1, Ms=(1,), dtype="bf16", bits=4)
+    layer = synth.make_layer(wl, seed=7, device="cuda")
+    A = (torch.randn((E, T, K), generator=torch.Generator(device="cuda").manual_seed(8),
+                     device="cuda") * 0.1).to(torch.bfloat16)
+    counts = torch.full((E,), T, dtype=torch.int32, device="cuda")
+    print("batched gemm with a 4.7 GB output", flush=True)
+    C = B.moe_wna16_batched_gemm(A, counts, layer["w2"], layer["w2_scales"], layer["w2_zeros"],
+                                 act=0)
+    torch.cuda.synchronize()
+    for e in (0, E - 1):
+        sub = {k: (v[e:e + 1].cpu() if v is not None else None) for k, v in layer.items()}
+        src = O.ExpertSource(sub, 4)
+        ref = O.batched_gemm(A[e:e + 1, T - 8:].cpu(), np.array([8]), src.w2, act=0)
+        keys = sorted(ref)
+        assert_layer_close(torch.stack([C[e, T - 8 + r].cpu() for _, r in keys]),
+                           np.stack([ref[k] for k in keys]), f"expert {e}")

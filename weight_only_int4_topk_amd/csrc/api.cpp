@@ -471,9 +471,10 @@ int moe_wna16_batched_gemm(const void* A, int E, int max_tokens, int K,
   if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
   if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
   const int64_t rows = (int64_t)E * max_tokens;
-  if (rows * K * 2 >= ((int64_t)1 << 31) || rows * N * 2 >= ((int64_t)1 << 31) ||
+  // 32-bit buffer offsets: A and one expert's weights (C is written with 64-bit addresses)
+  if (rows * K * 2 >= ((int64_t)1 << 31) ||
       (int64_t)N * (quant->bits == 4 ? K / 2 : K) >= ((int64_t)1 << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "A, C or one expert's weights exceed 2 GiB");
+    return fail(MOE_ERR_UNSUPPORTED, "A or one expert's weights exceed 2 GiB");
   if (int rc = check_weights(B, scales, zeros, quant)) return rc;
   if (max_tokens == 0) return MOE_OK;
   if (!A || !C || !expert_num_tokens) return fail(MOE_ERR_INVALID_ARG, "NULL A / C / counts");
