@@ -237,7 +237,9 @@ size_t fused_moe_w8a8_workspace_size(int M, int H, int I, int E, int topk, int d
  * activation row through its expert's permutation before each GEMM, and is otherwise
  * fused_moe_wna16 (the same result as decoding w[n, k] = (q - z[g_idx[k]]) * s[g_idx[k]] in the
  * original column order).  Permutation entries outside [0, H) (or [0, I)) read as zero.
- *   workspace: at least fused_moe_wna16_act_order_workspace_size(...) bytes. */
+ *   workspace: at least fused_moe_wna16_act_order_workspace_size(...) bytes.
+ * Limits: those of fused_moe_wna16 for uint4 weights, and the gathered rows of the first GEMM
+ * below 2^31 bytes (M * topk * H * 2, 32-bit offsets). */
 int fused_moe_wna16_act_order(const void* x, const float* router_logits, int M, int H, int I,
                               int E, int topk, const moe_routing_t* routing, const void* w13,
                               const void* w13_scales, const void* w13_zeros,

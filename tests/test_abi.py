@@ -280,6 +280,21 @@ def test_w8a8_validation(lib):
     assert fused8(131071, 1) == WORKSPACE
 
 
+def test_act_order_size_limits(lib):
+    """The act-order layer's first GEMM reads the gathered rows [M * topk, H] with 32-bit offsets:
+    at the DeepSeek-V3 shape 18724 tokens fit (stopped here by a one-byte workspace, before any
+    launch) and 18725 are refused."""
+    def ao(M, wsb):
+        return lib.fused_moe_wna16_act_order(FAKE, FAKE, M, 7168, 2048, 256, 8, _rt(), FAKE, FAKE,
+                                             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, wsb,
+                                             FAKE, NULL, NULL, NULL)
+
+    assert 18724 * 8 * 7168 * 2 < 2**31 <= 18725 * 8 * 7168 * 2
+    assert ao(18725, 1 << 62) == UNSUPPORTED
+    assert b"gathered" in lib.moe_last_error()
+    assert ao(18724, 1) == WORKSPACE
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(B, "_lib", None)

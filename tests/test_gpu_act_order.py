@@ -91,3 +91,34 @@ def test_act_order_mixtral_shape_sampled():
     wl = synth.WORKLOADS["mixtral"]
     out, ref, rows = _run(wl, 16, seed=0, device="cuda", rows=[0, 9, 15])
     assert_layer_close(O.to_numpy(out)[rows], ref, "act-order mixtral")
+
+
+def test_act_order_largest_batch_sampled():
+    """The largest batch the act-order layer accepts at the DeepSeek-V3 prefill shape: M = 18724
+    keeps the first GEMM's gathered rows (M * topk * H * 2 bytes) under 2 GiB, one token more is
+    refused.  The last token, whose gathered rows end just below 2^31 bytes, against the oracle,
+    its routing exact."""
+    wl = synth.WORKLOADS["dsv3_prefill_int4"]
+    M = 18724
+    assert M * wl.topk * wl.H * 2 < 2**31 <= (M + 1) * wl.topk * wl.H * 2
+    lay = synth.make_layer_act_order(wl, seed=0, device="cuda")
+    x = synth.make_x(wl, M, seed=0, device="cuda")
+    lg = synth.make_logits(wl, M, seed=0, device="cuda")
+    ti = torch.empty((M, wl.topk), dtype=torch.int32, device="cuda")
+    tw = torch.empty((M, wl.topk), dtype=torch.float32, device="cuda")
+    print(f"act-order largest batch M={M}", flush=True)
+    out = B.fused_moe_wna16_act_order(x, lg, wl.topk, routing_of(wl), lay["w13"],
+                                      lay["w13_scales"], lay["w13_zeros"], lay["w13_perm"],
+                                      lay["w2"], lay["w2_scales"], lay["w2_zeros"], lay["w2_perm"],
+                                      topk_weights=tw, topk_ids=ti)
+    torch.cuda.synchronize()
+    rows = [M - 1]
+    ids, w = oracle_route(wl, lg[rows])                   # routing is per token
+    assert np.array_equal(O.to_numpy(ti)[rows], ids)
+    experts = sorted(set(ids.reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items()}
+    del lay
+    ref, _ = O.moe_layer_rows(x[rows].cpu(), ids, w, GidxSource(sub, experts),
+                              np.arange(len(rows)))
+    assert_layer_close(O.to_numpy(out)[rows], ref, f"act-order dsv3 M={M}")

@@ -757,6 +757,9 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   if ((int64_t)M * topk * I * 2 >= ((int64_t)1 << 31) || (int64_t)M * H * 2 >= ((int64_t)1 << 31) ||
       (int64_t)2 * I * (quant->bits == 4 ? H / 2 : H) >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "activations or one expert's weights exceed 2 GiB");
+  // act-order: the first GEMM reads the gathered rows [M * topk, H] instead of x
+  if (w13_perm && (int64_t)M * topk * H * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "gathered activation rows (M * topk * H) exceed 2 GiB");
   if (M == 0) return MOE_OK;
   if (int rc = check_weights(w13, w13_scales, w13_zeros, quant)) return rc;
   if (int rc = check_weights(w2, w2_scales, w2_zeros, quant)) return rc;
