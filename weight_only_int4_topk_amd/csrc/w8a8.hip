@@ -236,11 +236,13 @@ hipError_t launch_w8a8_ntw(const W8A8Params& p, int act, int out_f32, hipStream_
 
 // The SiLU GEMM takes four column tiles per wavefront where its gate columns divide the wider
 // workgroup (each activation fragment then feeds four MFMAs instead of two: DeepSeek-V3 int8
-// experts at M = 4096 3012 -> 2852 us); the plain GEMM keeps two (with four, H = 7168 gives half as
-// many workgroups and the M = 1024 layer measured 4 % slower).
+// experts with 64-row blocks at M = 4096, 3012 -> 2852 us; at M = 1024, where the weight stream
+// bounds it, the two are equal); the plain GEMM keeps two (with four, H = 7168 gives half as many
+// workgroups and the M = 1024 layer measured 4 % slower).  128-row blocks keep two: eight row
+// tiles already reuse each fragment, and registers are the limit.
 template <int DT, int MT>
 hipError_t launch_w8a8_mt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
-  if constexpr (MT <= 4) {  // 128 rows: eight row tiles already reuse each fragment, registers bound
+  if constexpr (MT <= 4) {
     if (act && (p.N / 2) % 128 == 0) return launch_w8a8_ntw<DT, MT, 4>(p, act, out_f32, stream);
   }
   return launch_w8a8_ntw<DT, MT, 2>(p, act, out_f32, stream);
