@@ -427,7 +427,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the layer is run on one GPU's share and multi-GPU runs are not part of this build",
+              "the layer is measured on one GPU's share of the experts; runs across several GPUs are not implemented",
               file=sys.stderr)
         sys.exit(2)
     import synth
