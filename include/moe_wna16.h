@@ -21,7 +21,13 @@
  *     nothing was enqueued (except MOE_ERR_HIP, a launch failure); moe_last_error() then returns a
  *     message for the calling thread.
  *   - dtype: 0 = fp16, 1 = bf16.  Activations, outputs and weight scales share it.
- *   - Rows are contiguous (row-major) and every device pointer must be 16-byte aligned.
+ *   - Rows are contiguous (row-major).  Alignment: activations, weights and outputs 16 bytes;
+ *     uint4 scales 4 bytes; int8 scales and uint4 zero points 2 bytes; int32 and float arrays
+ *     4 bytes; workspaces 256 bytes.  A misaligned pointer returns MOE_ERR_INVALID_ARG.
+ *   - fp16 with uint4 weights: activations below 2^-10 in magnitude may lose up to 4 low bits of
+ *     precision inside the GEMMs, and at block_m 64 / 128 group scales above 273 overflow (decoded
+ *     weights beyond about 4000); neither occurs for quantised model weights and activations of
+ *     ordinary scale, and bf16 has neither limit.
  *
  * Weight storage (row-major, expert-major; N = output features, K = input features):
  *   int4 (quant {4, 128, 1}): B uint8 [E, N, K/2], byte j of a row holds k = 2j in bits 0-3 and
@@ -203,7 +209,8 @@ int moe_quant_int8_rows(const void* x, int rows, int K, int dtype, int8_t* q, fl
  *   B        device int8 [E, N, K], w_scales device dtype [E, N] (the int8 weight storage above)
  *   sorted_token_ids / expert_ids / num_tokens_post_padded: moe_align_block_size with block_m
  * Rows of C whose slot is not listed are not written.  num_slots = 0 returns MOE_OK at once.
- * Limits: block_m in {16, 32, 64, 128}, K % 256 == 0, N % 128 == 0. */
+ * Limits: block_m in {16, 32, 64, 128}, K % 256 == 0, N % 128 == 0, K <= 131072 (the int32 sums
+ * of code products stay below 2^31). */
 int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_row_div,
                   const int8_t* B, const void* w_scales, int E, int N, int K, int dtype,
                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
@@ -216,8 +223,9 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
  *   w13 device int8 [E, 2I, H], w13_scales device dtype [E, 2I]; w2 int8 [E, H, I], w2_scales [E, H]
  *   workspace: at least fused_moe_w8a8_workspace_size(...) bytes, 256-byte aligned
  *   block_m 0 = the library's choice (as moe_pick_block_m for int8 weights)
- * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, block_m in {0, 16, 32, 64, 128},
- * M * topk <= 2^24, and below 2^31 (32-bit offsets): M * H, M * topk * I and 2I * H. */
+ * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, H and I <= 131072 (int32 sums), block_m
+ * in {0, 16, 32, 64, 128}, M * topk <= 2^24, and below 2^31 (32-bit offsets): M * H,
+ * M * topk * I and 2I * H. */
 int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
                    const moe_routing_t* routing, const int8_t* w13, const void* w13_scales,
                    const int8_t* w2, const void* w2_scales, int dtype, int block_m,

@@ -125,6 +125,11 @@ def test_gemm_validation(lib):
     assert _gemm(lib, q=_q(8, 0, 0)) == INVALID                # zeros given with has_zero = 0
     assert _gemm(lib, Z=NULL) == INVALID                       # zeros missing with has_zero = 1
     assert _gemm(lib, Z=ctypes.c_void_p(0x100001)) == INVALID  # zeros not 2-byte aligned
+    assert _gemm(lib, S=ctypes.c_void_p(0x100002)) == INVALID  # uint4 scales: 4-byte loads
+    assert b"4-byte" in lib.moe_last_error()
+    # int8 scales are read 2 bytes at a time
+    assert _gemm(lib, q=_q(8, 0, 0), Z=NULL, S=ctypes.c_void_p(0x100002), slots=0) == OK
+    assert _gemm(lib, q=_q(8, 0, 0), Z=NULL, S=ctypes.c_void_p(0x100001)) == INVALID
     assert _gemm(lib, dt=2) == UNSUPPORTED
     assert _gemm(lib, K=300) == UNSUPPORTED
     assert _gemm(lib, N=1000) == UNSUPPORTED
@@ -267,6 +272,9 @@ def test_w8a8_validation(lib):
     assert w8(A=ctypes.c_void_p(0x100008)) == INVALID
     assert w8(dt=5) == UNSUPPORTED
     assert w8(slots=0) == OK
+    # int32 sums of code products: K up to 131072 (127^2 * K < 2^31), one more k-block refused
+    assert w8(K=131072 + 256, rows=8, slots=16, cap=8 * 2 + 8 * 15) == UNSUPPORTED
+    assert b"int32" in lib.moe_last_error()
 
     def fused8(M, wsb, H=7168, I=2048, E=256, k=8):
         return lib.fused_moe_w8a8(FAKE, FAKE, M, H, I, E, k, _rt(), FAKE, FAKE, FAKE, FAKE, 1, 0,
@@ -275,6 +283,8 @@ def test_w8a8_validation(lib):
     # DeepSeek-V3 int8 shape: the second GEMM's int8 activations (M * topk * I bytes) bound the
     # batch at 131071 tokens; the float32 rows after it are addressed with 64 bits.  (A one-byte
     # workspace stops the accepted call at its workspace check, before any launch.)
+    assert fused8(4, 1 << 62, H=131072 + 256, I=256) == UNSUPPORTED
+    assert b"int32" in lib.moe_last_error()
     assert fused8(131072, 1 << 62) == UNSUPPORTED
     assert b"2 GiB" in lib.moe_last_error()
     assert fused8(131071, 1) == WORKSPACE

@@ -102,6 +102,38 @@ def test_dequant_bits_matches_torch_rounding():
                           .view(torch.int16).numpy().view(np.uint16))
 
 
+def _torch_round(x64, dt):
+    t = torch.tensor(np.asarray(x64, np.float64)).float()       # float64 -> float32, RNE
+    return t.to(torch.float16 if dt == "fp16" else torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_round_to_dtype_matches_torch_rounding(dt):
+    """round_to_dtype (the rows the w8a8 layer's two GEMMs exchange) rounds float64 through float32
+    to fp16 / bf16 to nearest even; check it against torch's conversions over signed values from
+    fp16 subnormals to past the fp16 range, and on exact ties, where truncation or round-half-up
+    would differ."""
+    rng = np.random.default_rng(17)
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(np.log(1e-8), np.log(1e5), 20000))
+    np.testing.assert_array_equal(O.round_to_dtype(v, dt), _torch_round(v, dt))
+    if dt == "bf16":
+        # float32 bit patterns: the low half exactly 0x8000 is a tie (upper half 0x3F80 even,
+        # 0x3F81 odd), and one unit above a tie rounds up
+        u = np.array([0x3F808000, 0x3F818000, 0x3F808001, 0xBF818000, 0x3F807FFF], np.uint32)
+        want = np.array([0x3F800000, 0x3F820000, 0x3F810000, 0xBF820000, 0x3F800000], np.uint32)
+        x = u.view(np.float32).astype(np.float64)
+    else:
+        # 1 + 2^-11 is halfway between 1 and 1 + 2^-10 (to even: 1); 1 + 3 * 2^-11 goes up to
+        # 1 + 2^-9; 65520 is halfway between 65504 and the next binade (to even: inf); 2^-25 is
+        # halfway between 0 and the smallest subnormal 2^-24 (to even: 0)
+        x = np.array([1 + 2.0**-11, 1 + 3 * 2.0**-11, 65520.0, -(1 + 2.0**-11), 2.0**-25,
+                      3 * 2.0**-25])
+        want = np.array([1.0, 1 + 2.0**-9, np.inf, -1.0, 0.0, 2.0**-23]).astype(np.float32)
+    np.testing.assert_array_equal(O.round_to_dtype(x, dt), want.view(np.float32).astype(np.float64)
+                                  if dt == "bf16" else want.astype(np.float64))
+    np.testing.assert_array_equal(O.round_to_dtype(x, dt), _torch_round(x, dt))
+
+
 # ------------------------------------------------------------------------------------------------
 # routing
 # ------------------------------------------------------------------------------------------------

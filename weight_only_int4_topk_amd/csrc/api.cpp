@@ -83,6 +83,10 @@ int check_routing(const moe_routing_t* r, int E, int topk) {
   return MOE_OK;
 }
 
+// Longest K of the int8 x int8 GEMMs: their int32 sums of products of codes in [-127, 127]
+// stay below 2^31 (127^2 * 131072 = 2,114,060,288).
+constexpr int kW8A8MaxK = 131072;
+
 int64_t align_capacity(int64_t numel, int E, int bm) {
   return numel + std::min<int64_t>(E, numel) * (bm - 1);
 }
@@ -337,7 +341,11 @@ static int check_weights(const void* B, const void* scales, const void* zeros,
   if (!q->has_zero && zeros)
     return fail(MOE_ERR_INVALID_ARG, "zeros given but has_zero = 0 (both or neither)");
   if (!aligned(B, 16)) return fail(MOE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
-  if (!aligned(scales, 2)) return fail(MOE_ERR_INVALID_ARG, "scales must be 2-byte aligned");
+  // uint4 scales are read two k-blocks at a time (4-byte loads at even k-blocks; a row of K/128
+  // scales is a multiple of 4 bytes since K % 256 == 0); int8 scales and zero points in 2 bytes
+  const size_t salign = q->bits == 4 ? 4 : 2;
+  if (!aligned(scales, salign))
+    return fail(MOE_ERR_INVALID_ARG, "scales must be %zu-byte aligned", salign);
   if (zeros && !aligned(zeros, 2)) return fail(MOE_ERR_INVALID_ARG, "zeros must be 2-byte aligned");
   return MOE_OK;
 }
@@ -549,6 +557,8 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
   if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
   if ((int64_t)num_a_rows * K >= ((int64_t)1 << 31) || (int64_t)N * K >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "A or one expert's weights exceed 2 GiB");
+  // int32 accumulation of products of codes in [-127, 127]: 127^2 * K stays below 2^31
+  if (K > kW8A8MaxK) return fail(MOE_ERR_UNSUPPORTED, "K = %d > %d (int32 sums)", K, kW8A8MaxK);
   if ((int64_t)num_a_rows * a_row_div < num_slots)
     return fail(MOE_ERR_INVALID_ARG, "A has %d rows, slots need %lld", num_a_rows,
                 (long long)((num_slots + a_row_div - 1) / a_row_div));
@@ -634,6 +644,8 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
     return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128)", block_m);
   if (H % 256 || I % 256)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
+  if (H > kW8A8MaxK || I > kW8A8MaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "H = %d or I = %d > %d (int32 sums)", H, I, kW8A8MaxK);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");
   // 32-bit buffer offsets: the int8 activations of either GEMM, one expert's weights (the float32
   // rows of the second GEMM and the combine use 64-bit addresses)

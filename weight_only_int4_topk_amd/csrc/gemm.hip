@@ -27,16 +27,22 @@
 // fp16 uint4: a nibble in bits 0..3 of a 16-bit half under the exponent of 1024 reads as 1024 + q,
 // and one in bits 4..7 reads as 1024 + 16 q; both are exact.  So the pairs (k0,k4) and (k2,k6) are
 // masked out of w and w >> 8 in place, and the pairs (k1,k5) and (k3,k7) in place with the high
-// nibble mask, scaled by 16.  The activations at those k offsets are stored in LDS divided by 16
-// (exact for normal fp16 values), so every product a * w is unchanged: one shift and four
-// and-or per 8 weights instead of three shifts.  bf16 has too few mantissa bits for 1024 + 16 q
-// under any exponent, so its biased codes keep the three shifts, and its exact decode converts
-// each nibble from a byte of its own in natural k order (no activation permutation then).
+// nibble mask, scaled by 16.  The activations at those k offsets are stored in LDS divided by 16,
+// so every product a * w is unchanged: one shift and four and-or per 8 weights instead of three
+// shifts.  bf16 has too few mantissa bits for 1024 + 16 q under any exponent, so its biased codes
+// keep the three shifts, and its exact decode converts each nibble from a byte of its own in
+// natural k order (no activation permutation then).
 //
-// Decoding is exact: the MFMA sees the correctly rounded dtype value of (q - z) * s (fp16: the
-// subtraction of two exact half-precision integers 1024+q and 1024+z, then one rounded multiply,
-// or 16 times that value against an activation divided by 16; bf16: an exact float32 fma of q
-// against s and -z*s, then one rounding to bf16).
+// What the matrix cores see.  block_m 16 and 32: q - z exactly (magic-biased codes whose bias and
+// zero point are removed by a second MFMA or by an exact half-precision subtraction), the group
+// scale applied in float32 to each k-block's partial sum.  block_m 64 and 128: the correctly
+// rounded dtype value of (q - z) * s (fp16: the exact difference of the half-precision integers
+// 1024+q and 1024+z, then one rounded multiply; bf16: an exact float32 fma of q against s and
+// -z*s, then one rounding).  Two limits of the fp16 uint4 paths, both from the factor 16:
+//   - an activation divided by 16 is exact for |a| >= 2^-10; below that a / 16 is subnormal and
+//     loses up to 4 low bits (a relative error up to 2^-7 on such tiny activations);
+//   - the block_m >= 64 decode forms 16 (q - z) s in fp16, which overflows to inf for a group
+//     scale above 65504 / 240 (about 273, decoded weights beyond about 4000 in magnitude).
 #include "common.h"
 #include "launch.h"
 
