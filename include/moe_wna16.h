@@ -296,6 +296,27 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
                     void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
                     int32_t* topk_ids_out, void* stream);
 
+/* Bytes of the static device scratch that fused_moe_wna16_noalloc uses as its workspace. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* fused_moe_wna16 for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, result and determinism as
+ * fused_moe_wna16, without the workspace: the library keeps MOE_NOALLOC_SCRATCH_BYTES (64 MiB) of
+ * device memory in a static array, one per GPU it runs on, held until the process ends, and calls
+ * no allocator.  That covers every decode batch (M <= 64) of the Mixtral-, Qwen2- and DeepSeek-V3-
+ * shaped layers and batches up to about 128-256 tokens; a batch whose
+ * fused_moe_wna16_workspace_size exceeds it returns MOE_ERR_WORKSPACE before anything is enqueued.
+ * The stream must belong to the current device.  All calls on one GPU share that GPU's scratch:
+ * calls that overlap in time on one GPU (different streams or threads) race on it and must be
+ * serialised by the caller; calls in order on one stream are safe (each writes every scratch
+ * element it reads). */
+int fused_moe_wna16_noalloc(const void* x, const float* router_logits, int M, int H, int I, int E,
+                            int topk, const moe_routing_t* routing, const void* w13,
+                            const void* w13_scales, const void* w13_zeros, const void* w2,
+                            const void* w2_scales, const void* w2_zeros, const moe_quant_t* quant,
+                            int dtype, int block_m, void* out, float* topk_weights_out,
+                            int32_t* topk_ids_out, void* stream);
+
 /* Message for the last non-zero status returned on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

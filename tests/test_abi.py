@@ -376,3 +376,18 @@ def test_binding_rejects_mis_shaped_tensors():
     raises(lambda: B.moe_wna16_batched_gemm(torch.zeros(E, 16, H, dtype=torch.float16),
                                             torch.zeros(E - 1, dtype=torch.int32), w13, s13, z13, act=1),
            "expert_num_tokens has shape")
+
+
+def test_noalloc_scratch_limit(lib):
+    """fused_moe_wna16_noalloc refuses, before any device call, a batch whose workspace exceeds its
+    64 MiB static scratch (the Mixtral shape at 4096 tokens needs about 1.1 GB), and an empty
+    batch returns at once."""
+    q4 = _q(4, 128, 1)
+    f = lib.fused_moe_wna16_noalloc
+    assert lib.fused_moe_wna16_workspace_size(4096, 4096, 14336, 8, 2, q4, 0, 0) > (64 << 20)
+    assert f(FAKE, FAKE, 4096, 4096, 14336, 8, 2, _rt(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, q4, 0,
+             0, FAKE, NULL, NULL, NULL) == WORKSPACE
+    assert b"static scratch" in lib.moe_last_error()
+    assert f(FAKE, FAKE, 0, 4096, 14336, 8, 2, _rt(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, q4, 0,
+             0, FAKE, NULL, NULL, NULL) == OK
+    assert B.NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -18,6 +18,7 @@ __all__ = [
     "moe_wna16_gemm", "moe_wna16_dense_gemm", "moe_wna16_dense_gemm_workspace_size",
     "moe_wna16_batched_gemm", "moe_quant_int8_rows", "moe_w8a8_gemm", "fused_moe_w8a8",
     "fused_moe_wna16_act_order", "fused_moe_wna16_workspace_size", "fused_moe_wna16",
+    "fused_moe_wna16_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wna16.so")
@@ -75,7 +76,13 @@ _SIGS = {
     "fused_moe_wna16": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P, _P,
                          _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _P, ctypes.c_size_t, _P, _P,
                          _P, _P], _I),
+    "fused_moe_wna16_noalloc": ([_P, _P, _I, _I, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P,
+                                 _P, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _P, _P, _P, _P],
+                                _I),
 }
+
+# MOE_NOALLOC_SCRATCH_BYTES of the header: the static scratch of fused_moe_wna16_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -401,4 +408,25 @@ def fused_moe_wna16(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w13
                                  _dtype_code(x.dtype), block_m, _ptr(workspace),
                                  workspace.numel(), _ptr(out), _ptr(topk_weights),
                                  _ptr(topk_ids), _stream(stream)))
+    return out
+
+
+def fused_moe_wna16_noalloc(x, router_logits, topk, rt: MoeRouting, w13, w13_scales, w13_zeros, w2,
+                            w2_scales, w2_zeros, out, block_m=0, topk_weights=None, topk_ids=None,
+                            stream=None):
+    """The whole layer on the library's static scratch: no workspace and nothing allocated here
+    either (out, and topk_weights / topk_ids if wanted, are the caller's)."""
+    quant = _quant_of(w13, w13_zeros)
+    M, H = x.shape
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    _want_layer_io(x, router_logits, E, topk, out, topk_weights, topk_ids)
+    _want_weights("w13", w13, w13_scales, w13_zeros, (E,), 2 * I, H, x.dtype)
+    _want_weights("w2", w2, w2_scales, w2_zeros, (E,), H, I, x.dtype)
+    _check(lib().fused_moe_wna16_noalloc(_ptr(x), _ptr(router_logits), M, H, I, E, topk,
+                                         ctypes.byref(rt), _ptr(w13), _ptr(w13_scales),
+                                         _ptr(w13_zeros), _ptr(w2), _ptr(w2_scales),
+                                         _ptr(w2_zeros), ctypes.byref(quant),
+                                         _dtype_code(x.dtype), block_m, _ptr(out),
+                                         _ptr(topk_weights), _ptr(topk_ids), _stream(stream)))
     return out

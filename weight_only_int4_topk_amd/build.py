@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_wna16.so")
 
-SOURCES = ["api.cpp", "routing.hip", "align.hip", "gemm.hip", "combine.hip", "w8a8.hip"]
+SOURCES = ["api.cpp", "routing.hip", "align.hip", "gemm.hip", "combine.hip", "w8a8.hip",
+           "noalloc.hip"]
 ARCH = os.environ.get("MOE_WNA16_ARCH", "gfx950")
 
 FLAGS = [

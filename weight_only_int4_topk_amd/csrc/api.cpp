@@ -11,19 +11,25 @@
 #include <cstdio>
 #include <string>
 
+#include "api_internal.h"
 #include "launch.h"
 
 namespace {
 
 thread_local std::string g_err;
 
-int fail(int code, const char* fmt, ...) {
+int vfail(int code, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  g_err = buf;
+  return code;
+}
+
+int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vfail(code, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return code;
 }
 
@@ -879,6 +885,29 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
 }
 
 }  // namespace
+
+namespace moe {
+
+int api_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(code, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int fused_wna16(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
+                const moe_routing_t* routing, const void* w13, const void* w13_scales,
+                const void* w13_zeros, const void* w2, const void* w2_scales, const void* w2_zeros,
+                const moe_quant_t* quant, int dtype, int block_m, void* workspace,
+                size_t workspace_bytes, void* out, float* topk_weights_out, int32_t* topk_ids_out,
+                void* stream) {
+  return fused_impl(x, router_logits, M, H, I, E, topk, routing, w13, w13_scales, w13_zeros, w2,
+                    w2_scales, w2_zeros, quant, dtype, block_m, workspace, workspace_bytes, out,
+                    topk_weights_out, topk_ids_out, nullptr, nullptr, stream);
+}
+
+}  // namespace moe
 
 extern "C" {
 
