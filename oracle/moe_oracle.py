@@ -28,6 +28,7 @@ Every reading the pages leave open is listed with its justification in the desig
 from __future__ import annotations
 
 import math
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -269,10 +270,28 @@ class ExpertSource:
         return self._deq("w2", self._i(e))
 
 
-def moe_layer_rows(x, topk_ids, topk_weights, src: ExpertSource, rows=None):
+def _per_expert(experts, fn, workers):
+    """[fn(e) for e in experts], on `workers` threads when > 1 (each call is independent; numpy
+    releases the interpreter lock inside its array operations).  The threads then run the BLAS
+    products single-threaded, so they do not compete with BLAS's own threads."""
+    if workers <= 1:
+        return [fn(e) for e in experts]
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        if threadpool_limits is None:
+            return list(ex.map(fn, experts))
+        with threadpool_limits(1):
+            return list(ex.map(fn, experts))
+
+
+def moe_layer_rows(x, topk_ids, topk_weights, src: ExpertSource, rows=None, workers: int = 1):
     """out[m] = sum_j w[m,j] * W2[e] (SiLU(gate_e x_m) * up_e x_m) for the token rows `rows`.
 
-    Float64 throughout; the per-slot results are summed over j in ascending order.
+    Float64 throughout; the per-slot results are summed over j in ascending order.  The experts
+    are independent, so `workers` > 1 evaluates them on that many threads (same arithmetic).
     Returns (out float64 [len(rows), H], per-slot y float64 [len(rows), topk, H])."""
     x64 = np.asarray(to_numpy(x), dtype=np.float64)
     ids = np.asarray(to_numpy(topk_ids), dtype=np.int64)
@@ -280,17 +299,20 @@ def moe_layer_rows(x, topk_ids, topk_weights, src: ExpertSource, rows=None):
     rows = np.arange(ids.shape[0]) if rows is None else np.asarray(rows)
     k = ids.shape[1]
     sub = ids[rows]
-    y = None
-    for e in sorted(set(sub.reshape(-1).tolist())):
+
+    def expert(e):
         W13 = src.w13(e)
         W2 = src.w2(e)
         I = W13.shape[0] // 2
         rr, jj = np.nonzero(sub == e)
         h = x64[rows[rr]] @ W13.T                 # each row is one token's product with expert e
         a = silu(h[:, :I]) * h[:, I:]
-        ye = a @ W2.T
+        return rr, jj, a @ W2.T
+
+    y = None
+    for rr, jj, ye in _per_expert(sorted(set(sub.reshape(-1).tolist())), expert, workers):
         if y is None:
-            y = np.zeros((len(rows), k, W2.shape[0]), np.float64)
+            y = np.zeros((len(rows), k, ye.shape[1]), np.float64)
         y[rr, jj] = ye
     out = np.zeros((len(rows), y.shape[2]), np.float64)
     for j in range(k):
@@ -445,13 +467,17 @@ def round_to_dtype(x64, dtype: str) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def moe_layer_w8a8_rows(x, topk_ids, topk_weights, layer: dict, dtype: str, rows=None):
+def moe_layer_w8a8_rows(x, topk_ids, topk_weights, layer: dict, dtype: str, rows=None,
+                        workers: int = 1):
     """The layer with int8 experts and per-token int8 activations, as a definition.
 
     For token m and its j-th expert e: (xq, xs) = quant_int8_rows(x[m]);
     h = (W13q[e] @ xq) * xs * W13s[e]; a = SiLU(h[:I]) * h[I:] rounded to the activation dtype (the
     rows the two GEMMs exchange); (aq, as) = quant_int8_rows(a); y = (W2q[e] @ aq) * as * W2s[e];
-    out[m] = sum_j w[m, j] * y_j (j ascending).  Integer sums exact, float64 elsewhere.
+    out[m] = sum_j w[m, j] * y_j (j ascending).  The integer sums are exact: they are formed in
+    float64, where every partial sum of products of codes in [-127, 127] is an integer far below
+    2^53; float64 elsewhere.  The (token, j) pairs of one expert are evaluated together (each row
+    of a product is that pair's own sum), on `workers` threads across experts when > 1.
     layer: w13 int8 [E, 2I, H], w13_scales [E, 2I], w2 int8 [E, H, I], w2_scales [E, H]."""
     xs_all = np.asarray(to_numpy(x), dtype=np.float32)
     ids = np.asarray(to_numpy(topk_ids), dtype=np.int64)
@@ -459,20 +485,29 @@ def moe_layer_w8a8_rows(x, topk_ids, topk_weights, layer: dict, dtype: str, rows
     rows = np.arange(ids.shape[0]) if rows is None else np.asarray(rows)
     L = {k: np.asarray(to_numpy(v)) for k, v in layer.items() if v is not None}
     H = xs_all.shape[1]
+    k = ids.shape[1]
+    sub = ids[rows]
+    assert H <= 131072 and L["w2"].shape[2] <= 131072        # 127^2 * K far below 2^53
+    xq, xsc = quant_int8_rows(xs_all[rows])                  # per token: one row each
+
+    def expert(e):
+        rr, jj = np.nonzero(sub == e)
+        w13q = L["w13"][e].astype(np.float64)
+        I = w13q.shape[0] // 2
+        h = (xq[rr].astype(np.float64) @ w13q.T) * xsc[rr].astype(np.float64)[:, None] * \
+            L["w13_scales"][e].astype(np.float64)[None, :]
+        a = round_to_dtype(silu(h[:, :I]) * h[:, I:], dtype)
+        aq, asc = quant_int8_rows(a.astype(np.float32))
+        y = (aq.astype(np.float64) @ L["w2"][e].astype(np.float64).T) * \
+            asc.astype(np.float64)[:, None] * L["w2_scales"][e].astype(np.float64)[None, :]
+        return rr, jj, y
+
+    ys = np.zeros((len(rows), k, H), np.float64)
+    for rr, jj, y in _per_expert(sorted(set(sub.reshape(-1).tolist())), expert, workers):
+        ys[rr, jj] = y
     out = np.zeros((len(rows), H), np.float64)
-    for i, m in enumerate(rows):
-        xq, xsc = quant_int8_rows(xs_all[m:m + 1])
-        for j in range(ids.shape[1]):
-            e = int(ids[m, j])
-            w13q = L["w13"][e].astype(np.int64)
-            I = w13q.shape[0] // 2
-            h = (w13q @ xq[0].astype(np.int64)).astype(np.float64) * float(xsc[0]) * \
-                L["w13_scales"][e].astype(np.float64)
-            a = round_to_dtype(silu(h[:I]) * h[I:], dtype)
-            aq, asc = quant_int8_rows(a.astype(np.float32)[None, :])
-            y = (L["w2"][e].astype(np.int64) @ aq[0].astype(np.int64)).astype(np.float64) * \
-                float(asc[0]) * L["w2_scales"][e].astype(np.float64)
-            out[i] += wts[m, j] * y
+    for j in range(k):
+        out += wts[rows, j][:, None] * ys[:, j]
     return out
 
 

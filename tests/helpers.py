@@ -1,4 +1,6 @@
 """Shared helpers of the GPU parity tests (not collected by pytest)."""
+import os
+
 import numpy as np
 import torch
 
@@ -9,6 +11,16 @@ import weight_only_int4_topk_amd as B
 # layer-output tolerance: |gpu - ref| <= ATOL + RTOL*|ref| per element, and a relative L2 gate that
 # the elementwise bound alone would not enforce for small-magnitude outputs
 ATOL, RTOL, REL_L2 = 1e-2, 1e-2, 1e-2
+
+# threads for the oracle's per-expert work at full size
+ORACLE_WORKERS = max(1, min(8, os.cpu_count() or 1))
+
+
+def spaced_rows(M, n=256):
+    """n evenly spaced token rows of a batch of M (all of them when M <= n), first and last kept."""
+    if M <= n:
+        return np.arange(M)
+    return np.unique(np.round(np.linspace(0, M - 1, n)).astype(np.int64))
 
 
 def routing_of(wl):
@@ -59,11 +71,12 @@ def expert_subset(layer, experts):
     return {k: (v.index_select(0, idx).cpu() if v is not None else None) for k, v in layer.items()}
 
 
-def fused_vs_oracle(wl, M, seed=0, device="cpu", rows=None, block_m=None):
+def fused_vs_oracle(wl, M, seed=0, device="cpu", rows=None, block_m=None, layer=None):
     """Run the fused layer on the GPU and compare with the oracle (all rows, or the listed rows).
 
     Inputs are drawn on `device` (cpu: bytes identical everywhere; cuda: for full-size layers)."""
-    layer = synth.make_layer(wl, seed=seed, device=device)
+    if layer is None:
+        layer = synth.make_layer(wl, seed=seed, device=device)
     x = synth.make_x(wl, M, seed=seed, device=device)
     lg = synth.make_logits(wl, M, seed=seed, device=device)
     lay_gpu = cuda_layer(layer) if device == "cpu" else layer
@@ -74,6 +87,15 @@ def fused_vs_oracle(wl, M, seed=0, device="cpu", rows=None, block_m=None):
     rows = np.arange(M) if rows is None else np.asarray(rows)
     experts = sorted(set(ids_ref[rows].reshape(-1).tolist()))
     src = O.ExpertSource(expert_subset(lay_gpu, experts), wl.bits, experts)
-    ref, _ = O.moe_layer_rows(x.cpu(), ids_ref, w_ref, src, rows)
+    ref, _ = O.moe_layer_rows(x.cpu(), ids_ref, w_ref, src, rows, workers=ORACLE_WORKERS)
     rel = assert_layer_close(O.to_numpy(out)[rows], ref, f"{wl.name} M={M} seed={seed}")
     return out, ids_ref, rel
+
+
+def assert_align_exact(ids, E, bm):
+    """moe_align_block_size on the GPU against the oracle, all three outputs bit for bit."""
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(np.ascontiguousarray(ids)).cuda(), E, bm)
+    r_st, r_ex, r_T = O.align_block_size(ids, E, bm)
+    assert int(npost.item()) == r_T, f"T {int(npost.item())} != {r_T}"
+    assert np.array_equal(O.to_numpy(st), r_st), "sorted_token_ids differ"
+    assert np.array_equal(O.to_numpy(ex), r_ex), "expert_ids differ"

@@ -10,7 +10,7 @@ import torch
 import oracle as O
 import synth
 import weight_only_int4_topk_amd as B
-from helpers import assert_layer_close, oracle_route, routing_of
+from helpers import ORACLE_WORKERS, assert_layer_close, oracle_route, routing_of, spaced_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,8 @@ def _run(wl, M, seed, device="cpu", rows=None):
     experts = sorted(set(ids[rows].reshape(-1).tolist()))
     idx = torch.tensor(experts, dtype=torch.long, device=lay["w13"].device)
     sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items()}
-    ref, _ = O.moe_layer_rows(x.cpu(), ids, w, GidxSource(sub, experts), rows)
+    ref, _ = O.moe_layer_rows(x.cpu(), ids, w, GidxSource(sub, experts), rows,
+                              workers=ORACLE_WORKERS)
     return out, ref, rows
 
 
@@ -87,17 +88,17 @@ def test_act_order_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_act_order_mixtral_shape_sampled():
+def test_act_order_mixtral_shape_all_tokens():
     wl = synth.WORKLOADS["mixtral"]
-    out, ref, rows = _run(wl, 16, seed=0, device="cuda", rows=[0, 9, 15])
+    out, ref, rows = _run(wl, 16, seed=0, device="cuda")
     assert_layer_close(O.to_numpy(out)[rows], ref, "act-order mixtral")
 
 
 def test_act_order_largest_batch_sampled():
     """The largest batch the act-order layer accepts at the DeepSeek-V3 prefill shape: M = 18724
     keeps the first GEMM's gathered rows (M * topk * H * 2 bytes) under 2 GiB, one token more is
-    refused.  The last token, whose gathered rows end just below 2^31 bytes, against the oracle,
-    its routing exact."""
+    refused.  256 evenly spaced tokens, the last one's gathered rows ending just below 2^31 bytes,
+    against the oracle, their routing exact."""
     wl = synth.WORKLOADS["dsv3_prefill_int4"]
     M = 18724
     assert M * wl.topk * wl.H * 2 < 2**31 <= (M + 1) * wl.topk * wl.H * 2
@@ -112,7 +113,8 @@ def test_act_order_largest_batch_sampled():
                                       lay["w2"], lay["w2_scales"], lay["w2_zeros"], lay["w2_perm"],
                                       topk_weights=tw, topk_ids=ti)
     torch.cuda.synchronize()
-    rows = [M - 1]
+    rows = spaced_rows(M)
+    assert rows[-1] == M - 1
     ids, w = oracle_route(wl, lg[rows])                   # routing is per token
     assert np.array_equal(O.to_numpy(ti)[rows], ids)
     experts = sorted(set(ids.reshape(-1).tolist()))
@@ -120,5 +122,5 @@ def test_act_order_largest_batch_sampled():
     sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items()}
     del lay
     ref, _ = O.moe_layer_rows(x[rows].cpu(), ids, w, GidxSource(sub, experts),
-                              np.arange(len(rows)))
+                              np.arange(len(rows)), workers=ORACLE_WORKERS)
     assert_layer_close(O.to_numpy(out)[rows], ref, f"act-order dsv3 M={M}")

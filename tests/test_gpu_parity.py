@@ -10,8 +10,9 @@ import torch
 import oracle as O
 import synth
 import weight_only_int4_topk_amd as B
-from tests.helpers import (assert_layer_close, assert_weights_close, cuda_layer, expert_subset,
-                           fused_vs_oracle, oracle_route, routing_of, run_fused)
+from tests.helpers import (ORACLE_WORKERS, assert_align_exact, assert_layer_close,
+                           assert_weights_close, cuda_layer, expert_subset, fused_vs_oracle,
+                           oracle_route, routing_of, run_fused, spaced_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,11 +111,14 @@ def test_align_golden(golden):
 # decoded weights (identity probe) and the grouped GEMM
 # ------------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("dt,bits", [("fp16", 4), ("bf16", 4), ("fp16", 8), ("bf16", 8)])
-@pytest.mark.parametrize("bm", [16, 64])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_dequant_identity_probe(dt, bits, bm):
     """One-hot activation rows routed to one expert with weight 1: GEMM row k is the decoded
     column k of that expert, which must equal the oracle's correctly rounded (q - z) * s exactly.
-    BLOCK_M 16 runs the decode-regime kernel (biased codes), 64 the exact-decode kernel."""
+    Every kernel variant: BLOCK_M 16 (biased codes, bias and zero point removed by a second
+    MFMA), 32 (fp16 uint4: the half-precision subtraction (1024+q) - (1024+z); int8 and bf16:
+    biased codes), 64 and 128 (exact decoded weights; bf16 and int8 activations straight into
+    LDS)."""
     wl = synth.Workload("p", E=3, H=512, I=256, topk=1, Ms=(1,), dtype=dt, bits=bits)
     layer = synth.make_layer(wl, seed=5)
     lay = cuda_layer(layer)
@@ -273,25 +277,81 @@ def test_fused_empty_batch():
 # ------------------------------------------------------------------------------------------------
 # full-size layers (drawn on the GPU), sampled tokens against the oracle
 # ------------------------------------------------------------------------------------------------
-# Every decode M of the workloads, so each tile plan the library picks at full size runs once:
-# BLOCK_M 16/32/64, the first GEMM unsplit, split to ~512 workgroups (DeepSeek-V3 TP share at M=1)
-# and split towards one round (TP share at M=16 and 64, Qwen2 shape at M=1), 8-wavefront workgroups.
-@pytest.mark.parametrize("name,M", [("mixtral", 64), ("mixtral", 16), ("mixtral", 4), ("mixtral", 1),
-                                    ("qwen2", 512), ("qwen2", 128), ("qwen2", 16), ("qwen2", 1),
-                                    ("dsv3_tp8", 256), ("dsv3_tp8", 64), ("dsv3_tp8", 16),
-                                    ("dsv3_tp8", 1), ("dsv3_prefill_int4", 4096),
-                                    ("dsv3_prefill_int4", 1024), ("dsv3_prefill_int8", 4096),
-                                    ("dsv3_prefill_int8", 1024)])
-def test_fused_full_size_sampled(name, M):
+# Every M of the Mixtral-, Qwen2- and DeepSeek-V3 TP-share workloads, so each tile plan the library
+# picks at full size runs once: BLOCK_M 16/32/64, the first GEMM unsplit, split to ~512 workgroups
+# (DeepSeek-V3 TP share at M=1) and split towards one round (TP share at M=16 and 64, Qwen2 shape
+# at M=1), 8-wavefront workgroups.  Every token against the oracle; align of the full routing
+# result at the BLOCK_M the layer ran.
+FULL = [("mixtral", 64), ("mixtral", 16), ("mixtral", 4), ("mixtral", 1), ("qwen2", 512),
+        ("qwen2", 128), ("qwen2", 16), ("qwen2", 1), ("dsv3_tp8", 256), ("dsv3_tp8", 64),
+        ("dsv3_tp8", 16), ("dsv3_tp8", 1)]
+
+
+@pytest.mark.parametrize("name,M", FULL)
+def test_fused_full_size_all_tokens(name, M):
     wl = W[name]
-    rows = sorted({0, M // 2, M - 1})
-    out, ids, rel = fused_vs_oracle(wl, M, seed=0, device="cuda", rows=rows)
-    # align of the full routing result is exact too
-    bm = 16
+    print(f"full size {name} M={M}", flush=True)
+    out, ids, rel = fused_vs_oracle(wl, M, seed=0, device="cuda")
+    assert_align_exact(ids, wl.E, B.moe_pick_block_m(M, wl.E, wl.topk, wl.bits, wl.torch_dtype))
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill_int4", "dsv3_prefill_int8"])
+def test_fused_prefill_full_size_spaced_tokens(name):
+    """DeepSeek-V3 full-expert prefill (256 experts, H 7168, I 2048, bf16, grouped sigmoid top-8)
+    at M = 4096 and 1024, in the launch configuration the bench times (the library's BLOCK_M):
+    every token's routing exact, align exact at that BLOCK_M, and 256 evenly spaced tokens of each
+    batch (first and last included) against the oracle.  The smaller batch is the leading rows of
+    the larger one, so one decoding of each expert serves both."""
+    wl = W[name]
+    layer = synth.make_layer(wl, seed=0, device="cuda")
+    Mbig = 4096
+    x = synth.make_x(wl, Mbig, seed=0, device="cuda")
+    lg = synth.make_logits(wl, Mbig, seed=0, device="cuda")
+    ids_all, w_all = oracle_route(wl, lg)
+    outs, rows = {}, {}
+    for M in (4096, 1024):
+        bm = B.moe_pick_block_m(M, wl.E, wl.topk, wl.bits, wl.torch_dtype)
+        print(f"prefill {name} M={M} block_m={bm}", flush=True)
+        out, tw, ti = run_fused(wl, x[:M].contiguous(), lg[:M].contiguous(), layer)
+        assert np.array_equal(O.to_numpy(ti), ids_all[:M]), "topk ids differ"
+        assert_weights_close(tw, w_all[:M])
+        assert_align_exact(ids_all[:M], wl.E, bm)
+        outs[M], rows[M] = O.to_numpy(out), spaced_rows(M)
+    union = np.union1d(rows[4096], rows[1024])
+    experts = sorted(set(ids_all[union].reshape(-1).tolist()))
+    src = O.ExpertSource(expert_subset(layer, experts), wl.bits, experts)
+    del layer
+    ref, _ = O.moe_layer_rows(x.cpu(), ids_all, w_all, src, union, workers=ORACLE_WORKERS)
+    pos = {int(r): i for i, r in enumerate(union)}
+    for M in (4096, 1024):
+        r = rows[M]
+        assert_layer_close(outs[M][r], ref[[pos[int(v)] for v in r]], f"{name} M={M}")
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_grouped_gemm_fp16_tiny_activations(bm):
+    """fp16 activations far below 2^-10 (N(0, (2e-5)^2)): the uint4 kernels store the activations
+    met by the 16x high-nibble pairs divided by 16, which is subnormal there and drops up to 4 low
+    bits.  The GEMM alone (no SiLU, whose fp16 rows would underflow at this scale), weights drawn
+    N(0, 5^2) so the outputs stay normal fp16 numbers, against the oracle at every BLOCK_M."""
+    wl = synth.Workload("tinyact", E=4, H=512, I=512, topk=2, Ms=(40,), x_std=2e-5, w_std=5.0)
+    layer = synth.make_layer(wl, seed=3)
+    lay = cuda_layer(layer)
+    M = 40
+    ns = M * wl.topk
+    A = synth.make_x(wl.with_(H=wl.I), ns, seed=3)          # [slots, I] activations of w2
+    assert float(A.float().abs().max()) < 2.0**-10
+    ids, _ = oracle_route(wl, synth.make_logits(wl, M, seed=3))
     st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), wl.E, bm)
-    r_st, r_ex, r_T = O.align_block_size(ids, wl.E, bm)
-    assert int(npost.item()) == r_T and np.array_equal(O.to_numpy(st), r_st)
-    assert torch.isfinite(out.float()).all()
+    C = B.moe_wna16_gemm(A.cuda(), 1, lay["w2"], lay["w2_scales"], lay["w2_zeros"], st, ex, npost,
+                         bm, ns, act=0)
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm(A, 1, O.ExpertSource(layer, 4).w2, *O.align_block_size(ids, wl.E, bm), bm,
+                         ns)
+    refm = np.stack([ref[s] for s in range(ns)])
+    assert np.abs(refm).max() > 2.0**-14 * 4                  # normal fp16 outputs
+    sc = 1.0 / np.abs(refm).max()                             # make the elementwise bound bite
+    assert_layer_close(O.to_numpy(C).astype(np.float64) * sc, refm * sc, f"tiny activations bm={bm}")
 
 
 @pytest.mark.parametrize("bm", [16, 32])

@@ -6,7 +6,8 @@ import torch
 import oracle as O
 import synth
 import weight_only_int4_topk_amd as B
-from helpers import assert_layer_close, cuda_layer, oracle_route, routing_of
+from helpers import (ORACLE_WORKERS, assert_align_exact, assert_layer_close, cuda_layer,
+                     oracle_route, routing_of, spaced_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,47 +59,71 @@ def test_fused_w8a8_block_sizes_deterministic(bm):
     assert_layer_close(out1, ref, f"w8a8 bm={bm}")
 
 
-def test_fused_w8a8_mixtral_shape_sampled():
-    """Mixtral-shaped int8 experts at M = 16 on the GPU; three tokens checked against the oracle
-    (their experts copied to the host)."""
+def _expert_rows(lay, ids, rows):
+    """The experts the listed tokens use, copied to the host, and ids renumbered to match."""
+    experts = sorted(set(ids[rows].reshape(-1).tolist()))
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
+    remap = np.full(int(ids.max()) + 1, -1, np.int64)
+    remap[experts] = np.arange(len(experts))
+    ids_sub = np.where(np.isin(ids, experts), remap[np.clip(ids, 0, None)], 0)
+    return sub, ids_sub
+
+
+def test_fused_w8a8_mixtral_shape_all_tokens():
+    """Mixtral-shaped int8 experts at M = 16 on the GPU; every token against the oracle (the
+    experts copied to the host)."""
     wl = synth.WORKLOADS["mixtral"].with_(bits=8)
     M = 16
     out, x, ids, w, lay = _run(wl, M, seed=0, device="cuda")
-    rows = [0, 7, 15]
-    experts = sorted(set(ids[rows].reshape(-1).tolist()))
-    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
-    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
-    remap = {e: i for i, e in enumerate(experts)}
-    ids_sub = np.vectorize(lambda e: remap.get(int(e), 0))(ids)
-    ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows)
+    rows = np.arange(M)
+    sub, ids_sub = _expert_rows(lay, ids, rows)
+    ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows,
+                                workers=ORACLE_WORKERS)
     assert_layer_close(O.to_numpy(out)[rows], ref, "w8a8 mixtral")
 
 
-@pytest.mark.parametrize("M", [1024, 4096])
-def test_fused_w8a8_dsv3_full_size_sampled(M):
+def test_fused_w8a8_dsv3_full_size_spaced_tokens():
     """DeepSeek-V3-shaped int8 experts (256 x H 7168 x I 2048, bf16, grouped sigmoid top-8) at the
-    batch sizes the bench times, with the library's block size (64 rows at 1024 tokens, 128 at
-    4096); every token's routing exact, three tokens' outputs against the oracle."""
+    batch sizes the bench times, M = 4096 and 1024, with the library's block size (128 rows at 4096
+    tokens, 64 at 1024): every token's routing exact, align exact at that block size, and 256 evenly
+    spaced tokens of each batch (first and last included) against the oracle.  The smaller batch is
+    the leading rows of the larger one, so the experts are copied and decoded once."""
     wl = synth.WORKLOADS["dsv3_prefill_int8"]
-    assert B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype) == (64 if M == 1024 else 128)
-    out, x, ids, w, lay = _run(wl, M, seed=0, device="cuda")
-    print(f"fused w8a8 dsv3 full size M={M}", flush=True)
-    rows = [0, M // 2 + 3, M - 1]
-    experts = sorted(set(ids[rows].reshape(-1).tolist()))
-    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
-    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
+    lay = synth.make_layer(wl, seed=0, device="cuda")
+    x = synth.make_x(wl, 4096, seed=0, device="cuda")
+    lg = synth.make_logits(wl, 4096, seed=0, device="cuda")
+    ids, w = oracle_route(wl, lg)
+    outs, rows = {}, {}
+    for M in (4096, 1024):
+        bm = B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype)
+        assert bm == (64 if M == 1024 else 128)
+        print(f"fused w8a8 dsv3 full size M={M} block_m={bm}", flush=True)
+        ti = torch.empty((M, wl.topk), dtype=torch.int32, device="cuda")
+        tw = torch.empty((M, wl.topk), dtype=torch.float32, device="cuda")
+        out = B.fused_moe_w8a8(x[:M].contiguous(), lg[:M].contiguous(), wl.topk, routing_of(wl),
+                               lay["w13"], lay["w13_scales"], lay["w2"], lay["w2_scales"],
+                               topk_weights=tw, topk_ids=ti)
+        torch.cuda.synchronize()
+        assert np.array_equal(O.to_numpy(ti), ids[:M])
+        assert_align_exact(ids[:M], wl.E, bm)
+        outs[M], rows[M] = O.to_numpy(out), spaced_rows(M)
+    union = np.union1d(rows[4096], rows[1024])
+    sub, ids_sub = _expert_rows(lay, ids, union)
     del lay
-    remap = {e: i for i, e in enumerate(experts)}
-    ids_sub = np.vectorize(lambda e: remap.get(int(e), 0))(ids)
-    ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=rows)
-    assert_layer_close(O.to_numpy(out)[rows], ref, f"w8a8 dsv3 M={M}")
+    ref = O.moe_layer_w8a8_rows(x.cpu(), ids_sub, w, sub, wl.dtype, rows=union,
+                                workers=ORACLE_WORKERS)
+    pos = {int(r): i for i, r in enumerate(union)}
+    for M in (4096, 1024):
+        r = rows[M]
+        assert_layer_close(outs[M][r], ref[[pos[int(v)] for v in r]], f"w8a8 dsv3 M={M}")
 
 
 def test_fused_w8a8_largest_batch_sampled():
     """The largest batch the w8a8 layer accepts at the DeepSeek-V3 int8 shape: M = 131071 keeps the
     second GEMM's int8 activations (M * topk * I bytes) under 2 GiB, one token more is refused.
-    Its float32 rows then take 30 GB and the combine reads them past 2^34 bytes.  First, middle and
-    last token against the oracle, their routing exact."""
+    Its float32 rows then take 30 GB and the combine reads them past 2^34 bytes.  256 evenly spaced
+    tokens (first and last included) against the oracle, their routing exact."""
     wl = synth.WORKLOADS["dsv3_prefill_int8"]
     M = 131071
     assert M * wl.topk * wl.I < 2**31 <= (M + 1) * wl.topk * wl.I
@@ -111,15 +136,11 @@ def test_fused_w8a8_largest_batch_sampled():
     out = B.fused_moe_w8a8(x, lg, wl.topk, routing_of(wl), lay["w13"], lay["w13_scales"],
                            lay["w2"], lay["w2_scales"], topk_weights=tw, topk_ids=ti)
     torch.cuda.synchronize()
-    rows = [0, M // 2, M - 1]
+    rows = spaced_rows(M)
     ids, w = oracle_route(wl, lg[rows])                   # routing is per token
     assert np.array_equal(O.to_numpy(ti)[rows], ids)
-    experts = sorted(set(ids.reshape(-1).tolist()))
-    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
-    sub = {k: v.index_select(0, idx).cpu() for k, v in lay.items() if v is not None}
+    sub, ids_sub = _expert_rows(lay, ids, np.arange(len(rows)))
     del lay
-    remap = {e: i for i, e in enumerate(experts)}
-    ids_sub = np.vectorize(lambda e: remap[int(e)])(ids)
-    ref = O.moe_layer_w8a8_rows(x[rows].cpu(), ids_sub, w, sub, wl.dtype)
+    ref = O.moe_layer_w8a8_rows(x[rows].cpu(), ids_sub, w, sub, wl.dtype, workers=ORACLE_WORKERS)
     assert_layer_close(O.to_numpy(out)[rows], ref, f"w8a8 dsv3 M={M}")
     assert torch.isfinite(out[-4096:].float()).all()
