@@ -3,18 +3,20 @@
 
 A step is one call of the whole layer (routing, align, w13 grouped GEMM + SiLU*up, w2 grouped GEMM,
 weighted combine) on one batch of M tokens whose inputs are already in HBM.  `value` is tokens/s
-over exactly --steps steps.  The layer exists in L device copies that the steps cycle through, as a
-model's layer stack would, so that the experts a step reads have been evicted from the 256 MiB
-Infinity Cache by the time the same copy comes round again.  Steps are replayed from HIP graphs
-that hold several consecutive layer calls.
+over exactly --steps steps of the Mixtral-shaped layer at M = 64, replayed as one HIP graph that
+holds exactly --steps layer calls (after one graph of --warmup calls).  The layer exists in L device
+copies that the calls cycle through, as a model's layer stack would, so that the experts a call
+reads have been evicted from the 256 MiB Infinity Cache by the time the same copy comes round again.
 
 Also reported: the roofline of the dominant kernel (the w13 grouped GEMM with the SiLU epilogue),
-timed alone with HIP events on the stream it is launched on; an M sweep of the workload; the CPU
-oracle's throughput on a bounded sample of the same batch; the dense uint4 GEMM at the small-n
-benchmark's shapes (m 16, k 8192, n 128 ... 32768); the grouped GEMM over batched-experts
-activations on an expert-parallel share of 32 DeepSeek-V3-shaped experts; w8a8 (per-token int8
-activations) against w8a16 on the DeepSeek-V3 int8 experts; and the layer with GPTQ act-order
-experts beside the plain layer.
+timed alone with HIP events on the stream it is launched on; `workloads`, every M of all five
+workload shapes (the tiny layer, the Mixtral-, Qwen2- and DeepSeek-V3 TP-share decode layers, and
+the DeepSeek-V3 full-expert prefill layer with uint4 and with int8 experts), each with its binding
+roofline; the CPU oracle's throughput on a bounded sample of the headline batch, with all host
+threads and with one; the dense uint4 GEMM at the small-n benchmark's shapes (m 16, k 8192, n 128
+... 32768); the grouped GEMM over batched-experts activations on an expert-parallel share of 32
+DeepSeek-V3-shaped experts; w8a8 (per-token int8 activations) against w8a16 on the DeepSeek-V3
+int8 experts; and the layer with GPTQ act-order experts beside the plain layer.
 """
 from __future__ import annotations
 
@@ -46,8 +48,13 @@ def parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--m", type=int, default=0, help="tokens per step (default: largest decode M)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--sweep-steps", type=int, default=200)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the per-workload table (every M of all five workload shapes)")
+    ap.add_argument("--workloads", default="tiny,mixtral,qwen2,dsv3_tp8,dsv3_prefill_int4,"
+                                           "dsv3_prefill_int8",
+                    help="workloads of the per-workload table (comma-separated)")
+    ap.add_argument("--sweep-steps", type=int, default=200,
+                    help="layer calls per graph in the per-workload table and the side sweeps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the timed batch the CPU oracle runs (0: all of them; at the "
@@ -66,46 +73,59 @@ def parse():
     return ap.parse_args()
 
 
+_HIP = None
+
+
+def _graph_upload(g):
+    """hipGraphUpload of a captured torch graph's executable graph on the current stream."""
+    import ctypes
+
+    import torch
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _HIP.hipGraphUpload.restype = ctypes.c_int
+    rc = _HIP.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()),
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
+
+
 def graph_replay(fns, steps, warmup):
-    """Replay `steps` calls cycling through fns (one per weight copy), in graphs of G calls.
-    Returns (seconds of the timed steps by HIP events on the current stream, wall seconds, G)."""
+    """Time exactly `steps` calls cycling through fns (one per weight copy): one HIP graph holding
+    `warmup` calls is replayed untimed, then one graph holding exactly `steps` calls (uploaded to the
+    device beforehand) is replayed once between HIP events on the current stream.  Returns (seconds by the events, wall seconds,
+    calls per timed graph)."""
     import torch
     L = len(fns)
-    G = L * max(1, 16 // L)
     for f in fns:                          # compile/warm every code path eagerly first
         f()
     torch.cuda.synchronize()
-    chunk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(chunk):
-        for i in range(G):
-            fns[i % L]()
-    singles = []
-    for f in fns:
+
+    def capture(n, first):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            f()
-        singles.append(g)
+            for i in range(n):
+                fns[(first + i) % L]()
+        return g
 
-    def run(n):
-        done = 0
-        while n - done >= G:
-            chunk.replay()
-            done += G
-        while done < n:
-            singles[done % L].replay()
-            done += 1
-
-    run(warmup)
+    timed = capture(steps, warmup)         # continues the rotation where the warmup stops
+    # hand the timed graph's launch packets to the device before timing (hipGraphUpload); without
+    # it the first replay of a graph also pays for that set-up (measured: ~12 % at 20 layer calls)
+    _graph_upload(timed)
+    if warmup > 0:
+        capture(warmup, 0).replay()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     t0 = time.perf_counter()
-    run(steps)
+    timed.replay()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / 1e3, wall, G
+    return start.elapsed_time(end) / 1e3, wall, steps
 
 
 class Bench:
@@ -176,18 +196,29 @@ class Bench:
         us_g1 = t_g1 / steps * 1e6
         flops_layer = 6.0 * wl.H * wl.I * M * wl.topk
         flops_g1 = 4.0 * wl.H * wl.I * M * wl.topk
+        # binding roof of the layer: the larger of its HBM floor (activated experts' bytes at
+        # 8 TB/s) and its MFMA floor (6 H I M k flops at 2.5 PFLOP/s)
+        t_hbm = act_bytes / (HBM_PEAK_GBPS * 1e9)
+        t_mfma = flops_layer / (MFMA_PEAK_TFLOPS * 1e12)
         res = dict(
             M=M, block_m=bm, active_experts=active, layer_copies=L, graph_calls=G,
             us_per_layer=round(us_layer, 2), tokens_per_s=round(M / (us_layer * 1e-6), 1),
             layer_GBps=round(act_bytes / (us_layer * 1e-6) / 1e9, 1),
-            layer_hbm_frac=round(act_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            layer_mfma_frac=round(flops_layer / (us_layer * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            layer_hbm_frac=round(t_hbm / (us_layer * 1e-6), 4),
+            layer_mfma_frac=round(t_mfma / (us_layer * 1e-6), 4),
+            bound="mfma" if t_mfma > t_hbm else "hbm",
+            frac=round(max(t_hbm, t_mfma) / (us_layer * 1e-6), 4),
             w13_us=round(us_g1, 2),
             w13_GBps=round(w13_bytes / (us_g1 * 1e-6) / 1e9, 1),
             w13_TFLOPs=round(flops_g1 / (us_g1 * 1e-6) / 1e12, 2),
             active_weight_bytes=act_bytes, w13_bytes=w13_bytes,
         )
         return res, t_layer, wall, (x, lg)
+
+    def release(self):
+        self.copies = []
+        self.layer = None
+        self.torch.cuda.empty_cache()
 
 
 DENSE_NS = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
@@ -391,9 +422,30 @@ def committed_traffic(workload, M):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name", else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(bench, M, x, lg, ntok):
-    """The oracle as it stands on the first ntok tokens of the batch (host cores)."""
+    """The oracle as it stands on the first ntok tokens of the batch (host cores): once with the
+    BLAS threads it starts with, once with one thread."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
     torch, wl = bench.torch, bench.wl
@@ -406,20 +458,24 @@ def cpu_baseline(bench, M, x, lg, ntok):
     sub = {k: (v.index_select(0, idx).cpu() if v is not None else None)
            for k, v in bench.layer.items()}
     xs = x[: len(rows)].cpu()
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    ids, w = O.route(lg_np, wl.topk, wl.score, wl.renormalize, wl.num_groups, wl.topk_groups,
-                     wl.scale)
-    O.moe_layer_rows(xs, ids, w, O.ExpertSource(sub, wl.bits, experts))
-    dt = time.perf_counter() - t0
+    cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+
+    def run():
+        t0 = time.perf_counter()
+        ids, w = O.route(lg_np, wl.topk, wl.score, wl.renormalize, wl.num_groups,
+                         wl.topk_groups, wl.scale)
+        O.moe_layer_rows(xs, ids, w, O.ExpertSource(sub, wl.bits, experts))
+        return time.perf_counter() - t0
+
+    dt = run()
+    with threadpool_limits(1):
+        dt1 = run()
     return {"value": round(len(rows) / dt, 4), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{len(rows)} of the {M} tokens of the timed batch ({len(experts)} experts): "
-                      f"routing, float64 decoding of those experts and their FFN, {dt:.1f} s"}
+                      f"routing, float64 decoding of those experts and their FFN, {dt:.1f} s",
+            "one_thread_value": round(len(rows) / dt1, 4), "one_thread_s": round(dt1, 2),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main():
@@ -438,12 +494,7 @@ def main():
 
     res, t_layer, wall, (x, lg) = bench.measure(M, args.steps, args.warmup)
     log(f"[bench] M={M}: {res}")
-    sweep = []
-    if not args.no_sweep:
-        for m in wl.Ms:
-            r = res if m == M else bench.measure(m, args.sweep_steps, max(10, args.warmup // 4))[0]
-            sweep.append(r)
-            log(f"[bench] sweep M={m}: {r}")
+    sweep_warm = max(10, args.warmup // 4)
 
     hbm_frac = res["w13_GBps"] / HBM_PEAK_GBPS
     mfma_frac = res["w13_TFLOPs"] / MFMA_PEAK_TFLOPS
@@ -476,13 +527,32 @@ def main():
         cpu = cpu_baseline(bench, M, x, lg, args.cpu_tokens)
         log(f"[bench] cpu baseline: {cpu}")
 
+    # every M of every workload shape, each with its binding roofline (the headline workload's
+    # layer copies are reused)
+    table = []
+    if not args.no_sweep:
+        for name in [n for n in args.workloads.split(",") if n]:
+            b = bench if name == wl.name else Bench(synth.WORKLOADS[name], args.seed)
+            for m in b.wl.Ms:
+                r = res if (b is bench and m == M) else b.measure(m, args.sweep_steps, sweep_warm)[0]
+                r = {"workload": name, **r}
+                if name == "tiny":
+                    r["note"] = "parity workload: its 1.6 MB of experts stay cache-resident"
+                table.append(r)
+                log(f"[bench] {name} M={m}: {r}")
+            if b is not bench:
+                b.release()
+                del b
+
     act_order = None
     if not args.no_act_order and wl.bits == 4:
         act_order = act_order_sweep(bench, [m for m in wl.Ms if m <= 64] or [M], args.sweep_steps,
-                                    max(10, args.warmup // 4))
+                                    sweep_warm)
         for r in act_order:
-            plain = next((s["us_per_layer"] for s in sweep if s["M"] == r["M"]), None)
+            plain = next((t["us_per_layer"] for t in table
+                          if t["workload"] == wl.name and t["M"] == r["M"]), None)
             r["plain_us_per_layer"] = plain
+    bench.release()
     dense = None if args.no_dense else dense_sweep(args.sweep_steps, max(10, args.warmup // 4))
     batched = None if args.no_batched else batched_sweep(args.sweep_steps, max(10, args.warmup // 4))
     w8a8 = None if args.no_w8a8 else w8a8_sweep(max(20, args.sweep_steps // 4),
@@ -507,10 +577,11 @@ def main():
         "config": {"workload": f"{wl.name}: {wl.notes}", "E": wl.E, "H": wl.H, "I": wl.I,
                    "topk": wl.topk, "M": M, "bits": wl.bits, "block_m": res["block_m"],
                    "layer_copies": res["layer_copies"], "active_experts": res["active_experts"],
-                   "layer_GBps": res["layer_GBps"], "layer_hbm_frac": res["layer_hbm_frac"]},
+                   "layer_GBps": res["layer_GBps"], "layer_hbm_frac": res["layer_hbm_frac"],
+                   "timed_graph_calls": res["graph_calls"]},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "sweep": sweep,
+        "workloads": table,
         "act_order": act_order,
         "dense_w4a16": dense,
         "batched_experts": batched,
