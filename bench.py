@@ -92,40 +92,54 @@ def _graph_upload(g):
         raise RuntimeError(f"hipGraphUpload failed ({rc})")
 
 
+class GraphTimer:
+    """Exactly `steps` calls cycling through fns (one per weight copy), captured as one HIP graph
+    (uploaded to the device), and `warmup` calls captured as another.  time() replays the warmup
+    graph untimed, then the timed graph once between HIP events on the current stream, and returns
+    (seconds by the events, wall seconds, calls in the timed graph)."""
+
+    def __init__(self, fns, steps, warmup):
+        import torch
+        self.torch = torch
+        L = len(fns)
+        for f in fns:                      # compile/warm every code path eagerly first
+            f()
+        torch.cuda.synchronize()
+
+        def capture(n, first):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    fns[(first + i) % L]()
+            return g
+
+        # the graphs hold raw device pointers: keep the calls (and so every tensor they use) alive
+        # for as long as the graphs may be replayed
+        self.fns = list(fns)
+        self.timed = capture(steps, warmup)   # continues the rotation where the warmup stops
+        _graph_upload(self.timed)
+        self.warm = capture(warmup, 0) if warmup > 0 else None
+        self.steps = steps
+
+    def time(self):
+        torch = self.torch
+        if self.warm is not None:
+            self.warm.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        t0 = time.perf_counter()
+        self.timed.replay()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(end) / 1e3, wall, self.steps
+
+
 def graph_replay(fns, steps, warmup):
-    """Time exactly `steps` calls cycling through fns (one per weight copy): one HIP graph holding
-    `warmup` calls is replayed untimed, then one graph holding exactly `steps` calls (uploaded to the
-    device beforehand) is replayed once between HIP events on the current stream.  Returns (seconds by the events, wall seconds,
-    calls per timed graph)."""
-    import torch
-    L = len(fns)
-    for f in fns:                          # compile/warm every code path eagerly first
-        f()
-    torch.cuda.synchronize()
-
-    def capture(n, first):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fns[(first + i) % L]()
-        return g
-
-    timed = capture(steps, warmup)         # continues the rotation where the warmup stops
-    # hand the timed graph's launch packets to the device before timing (hipGraphUpload); without
-    # it the first replay of a graph also pays for that set-up (measured: ~12 % at 20 layer calls)
-    _graph_upload(timed)
-    if warmup > 0:
-        capture(warmup, 0).replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    t0 = time.perf_counter()
-    timed.replay()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / 1e3, wall, steps
+    """GraphTimer(fns, steps, warmup).time()."""
+    return GraphTimer(fns, steps, warmup).time()
 
 
 class Bench:
@@ -158,7 +172,9 @@ class Bench:
         cap = max(2, int((64 << 30) // self.layer_bytes))
         return min(L, cap)
 
-    def measure(self, M, steps, warmup):
+    def measure(self, M, steps, warmup, defer=False):
+        """Time the layer (and its w13 GEMM alone) at M tokens.  defer: capture the graphs now and
+        return a function that times them later (with the GPU busy right before)."""
         torch, synth, B, wl = self.torch, self.synth, self.B, self.wl
         x = synth.make_x(wl, M, seed=self.seed, device="cuda")
         lg = synth.make_logits(wl, M, seed=self.seed, device="cuda")
@@ -181,7 +197,7 @@ class Bench:
                                              c["w13_zeros"], c["w2"], c["w2_scales"],
                                              c["w2_zeros"], block_m=0, workspace=ws, out=out)
 
-        t_layer, wall, G = graph_replay([layer_fn(c) for c in self.copies[:L]], steps, warmup)
+        g_layer = GraphTimer([layer_fn(c) for c in self.copies[:L]], steps, warmup)
 
         # the dominant kernel alone: w13 grouped GEMM with the SiLU epilogue, same tiles
         st, ex, npost = B.moe_align_block_size(ti, wl.E, bm)
@@ -191,7 +207,18 @@ class Bench:
             return lambda: B.moe_wna16_gemm(x, wl.topk, c["w13"], c["w13_scales"], c["w13_zeros"],
                                             st, ex, npost, bm, M * wl.topk, act=1, C=inter)
 
-        t_g1, _, _ = graph_replay([gemm1_fn(c) for c in self.copies[:L]], steps, warmup)
+        g_g1 = GraphTimer([gemm1_fn(c) for c in self.copies[:L]], steps, warmup)
+
+        def finish():
+            t_g1, _, _ = g_g1.time()
+            t_layer, wall, G = g_layer.time()
+            return self._result(M, bm, active, L, G, t_layer, t_g1, steps, act_bytes, w13_bytes), \
+                t_layer, wall, (x, lg)
+
+        return finish if defer else finish()
+
+    def _result(self, M, bm, active, L, G, t_layer, t_g1, steps, act_bytes, w13_bytes):
+        wl = self.wl
         us_layer = t_layer / steps * 1e6
         us_g1 = t_g1 / steps * 1e6
         flops_layer = 6.0 * wl.H * wl.I * M * wl.topk
@@ -213,7 +240,7 @@ class Bench:
             w13_TFLOPs=round(flops_g1 / (us_g1 * 1e-6) / 1e12, 2),
             active_weight_bytes=act_bytes, w13_bytes=w13_bytes,
         )
-        return res, t_layer, wall, (x, lg)
+        return res
 
     def release(self):
         self.copies = []
@@ -491,10 +518,62 @@ def main():
     decode = [m for m in wl.Ms if m <= 64]
     M = args.m or (max(decode) if decode else max(wl.Ms))
     bench = Bench(wl, args.seed)
-
-    res, t_layer, wall, (x, lg) = bench.measure(M, args.steps, args.warmup)
-    log(f"[bench] M={M}: {res}")
     sweep_warm = max(10, args.warmup // 4)
+
+    # The headline's graphs are captured now and timed last, right after the other GPU work: after
+    # the GPU has idled (host-side set-up, the CPU baseline) its first milliseconds of work run at a
+    # lower clock (measured: the first two replays of a 20-call graph 215-233 us per call, later
+    # ones 201-209 us), which a 5-step warmup does not cover.
+    finish_headline = bench.measure(M, args.steps, args.warmup, defer=True)
+    x = synth.make_x(wl, M, seed=args.seed, device="cuda")
+    lg = synth.make_logits(wl, M, seed=args.seed, device="cuda")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(bench, M, x, lg, args.cpu_tokens)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    if args.calibrate_copy:
+        import torch
+        src = torch.empty(512 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 5 x 512 MiB device-to-device")
+
+    # every M of every workload shape, each with its binding roofline (the headline workload's
+    # layer copies are reused)
+    table = []
+    if not args.no_sweep:
+        for name in [n for n in args.workloads.split(",") if n]:
+            b = bench if name == wl.name else Bench(synth.WORKLOADS[name], args.seed)
+            for m in b.wl.Ms:
+                r = {"workload": name, **b.measure(m, args.sweep_steps, sweep_warm)[0]}
+                if name == "tiny":
+                    r["note"] = "parity workload: its 1.6 MB of experts stay cache-resident"
+                table.append(r)
+                log(f"[bench] {name} M={m}: {r}")
+            if b is not bench:
+                b.release()
+                del b
+
+    act_order = None
+    if not args.no_act_order and wl.bits == 4:
+        act_order = act_order_sweep(bench, [m for m in wl.Ms if m <= 64] or [M], args.sweep_steps,
+                                    sweep_warm)
+        for r in act_order:
+            plain = next((t["us_per_layer"] for t in table
+                          if t["workload"] == wl.name and t["M"] == r["M"]), None)
+            r["plain_us_per_layer"] = plain
+    dense = None if args.no_dense else dense_sweep(args.sweep_steps, sweep_warm)
+    batched = None if args.no_batched else batched_sweep(args.sweep_steps, sweep_warm)
+    w8a8 = None if args.no_w8a8 else w8a8_sweep(max(20, args.sweep_steps // 4),
+                                                 max(5, args.warmup // 8))
+
+    res, t_layer, wall, _ = finish_headline()
+    log(f"[bench] headline M={M}: {res}")
+    bench.release()
 
     hbm_frac = res["w13_GBps"] / HBM_PEAK_GBPS
     mfma_frac = res["w13_TFLOPs"] / MFMA_PEAK_TFLOPS
@@ -512,51 +591,6 @@ def main():
                  "avg_launch_us": res["w13_us"],
                  "algorithmic_per_launch": (res["w13_bytes"] if roof["bound"] == "hbm"
                                             else 4.0 * wl.H * wl.I * M * wl.topk)})
-
-    if args.calibrate_copy:
-        import torch
-        src = torch.empty(512 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] calibration copy: 5 x 512 MiB device-to-device")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(bench, M, x, lg, args.cpu_tokens)
-        log(f"[bench] cpu baseline: {cpu}")
-
-    # every M of every workload shape, each with its binding roofline (the headline workload's
-    # layer copies are reused)
-    table = []
-    if not args.no_sweep:
-        for name in [n for n in args.workloads.split(",") if n]:
-            b = bench if name == wl.name else Bench(synth.WORKLOADS[name], args.seed)
-            for m in b.wl.Ms:
-                r = res if (b is bench and m == M) else b.measure(m, args.sweep_steps, sweep_warm)[0]
-                r = {"workload": name, **r}
-                if name == "tiny":
-                    r["note"] = "parity workload: its 1.6 MB of experts stay cache-resident"
-                table.append(r)
-                log(f"[bench] {name} M={m}: {r}")
-            if b is not bench:
-                b.release()
-                del b
-
-    act_order = None
-    if not args.no_act_order and wl.bits == 4:
-        act_order = act_order_sweep(bench, [m for m in wl.Ms if m <= 64] or [M], args.sweep_steps,
-                                    sweep_warm)
-        for r in act_order:
-            plain = next((t["us_per_layer"] for t in table
-                          if t["workload"] == wl.name and t["M"] == r["M"]), None)
-            r["plain_us_per_layer"] = plain
-    bench.release()
-    dense = None if args.no_dense else dense_sweep(args.sweep_steps, max(10, args.warmup // 4))
-    batched = None if args.no_batched else batched_sweep(args.sweep_steps, max(10, args.warmup // 4))
-    w8a8 = None if args.no_w8a8 else w8a8_sweep(max(20, args.sweep_steps // 4),
-                                                 max(5, args.warmup // 8))
 
     value = M * args.steps / t_layer
     line = {

@@ -263,11 +263,10 @@ size_t fused_moe_wna16_act_order_workspace_size(int M, int H, int I, int E, int 
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits and activations of `dtype`: the smallest of {16, 32, 64, 128} that holds 1.5x the average
  * number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots share one
- * block and its weights are streamed once; uint4 stops at 64 (a 128-row block leaves too little LDS
- * for a second workgroup per compute unit beside its staged scales), and fp16 uint4 takes 32 where
- * up to 128 rows would be needed (its 64-row kernel stages activations through registers, which
- * measured slower than two 32-row blocks).  Returns -1 for non-positive sizes, other bit widths or
- * other dtypes. */
+ * block and its weights are streamed once; fp16 uint4 stops at 64, and takes 32 where up to 128
+ * rows would be needed (its 64-row kernel stages activations through registers, which measured
+ * slower than two 32-row blocks).  128-row blocks run on the 32x32 matrix cores.  Returns -1 for
+ * non-positive sizes, other bit widths or other dtypes. */
 int moe_pick_block_m(int M, int E, int topk, int bits, int dtype);
 
 /* Workspace bytes fused_moe_wna16 needs for these sizes (block_m 0 = library's choice). */

@@ -72,7 +72,8 @@ def test_pick_block_m(lib):
     assert lib.moe_pick_block_m(16, 8, 2, 4, fp16) == 16       # 4 slots per expert
     assert lib.moe_pick_block_m(64, 8, 2, 4, fp16) == 32       # 16 per expert -> 24 needed
     assert lib.moe_pick_block_m(1024, 256, 8, 4, bf16) == 64   # 32 per expert -> 48 needed
-    assert lib.moe_pick_block_m(4096, 256, 8, 4, bf16) == 64   # uint4 stops at 64
+    assert lib.moe_pick_block_m(4096, 256, 8, 4, bf16) == 128  # 128 per expert -> 192 needed
+    assert lib.moe_pick_block_m(4096, 256, 8, 4, fp16) == 64   # fp16 uint4 stops at 64
     assert lib.moe_pick_block_m(4096, 256, 8, 8, bf16) == 128
     assert lib.moe_pick_block_m(1024, 256, 8, 8, bf16) == 64
     # fp16 uint4: 32 rows where up to 128 would be needed (Qwen2 shape at M = 512: 64 per expert)

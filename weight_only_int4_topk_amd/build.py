@@ -16,8 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_wna16.so")
 
-SOURCES = ["api.cpp", "routing.hip", "align.hip", "gemm.hip", "combine.hip", "w8a8.hip",
-           "noalloc.hip"]
+SOURCES = ["api.cpp", "routing.hip", "align.hip", "gemm.hip", "prefill.hip", "combine.hip",
+           "w8a8.hip", "noalloc.hip"]
 ARCH = os.environ.get("MOE_WNA16_ARCH", "gfx950")
 
 FLAGS = [

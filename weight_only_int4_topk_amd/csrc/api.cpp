@@ -110,21 +110,26 @@ struct Plan {
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
 };
 
-// uint4 stops at 64: the fp16 128-row kernel stages activations through registers and runs at two
-// wavefronts per SIMD (Qwen2-shaped layer at M = 512: GEMMs 798 us at 128 rows, 497 us at 64); in
-// bf16 the two are within a few percent (DeepSeek-V3 expert at M = 4096).  int8 keeps 128.  fp16
-// uint4 where 64 rows would be picked for up to 128 needed: 32 rows (the fp16 64-row kernel also
-// stages activations through registers; Qwen2 shape at M = 512, ~72 slots per expert: 555 -> 529
-// us per layer; bf16 and int8 measured equal or slower at 32).
+// fp16 uint4 stops at 64: its 128-row blocks run the 32x32 prefill kernel with spilled registers
+// (and the 16-row kernel at 128 rows stages activations through registers at two wavefronts per
+// SIMD: Qwen2-shaped layer at M = 512, GEMMs 798 us at 128 rows, 497 us at 64).  bf16 uint4 and
+// int8 take 128 rows where that many are needed (the 32x32 prefill kernel: DeepSeek-V3 prefill
+// layer at 4096 tokens, uint4 4.50 against 4.78 ms at 64 rows).  fp16 uint4 where 64 rows would
+// be picked for up to 128 needed: 32 rows (the fp16 64-row kernel also stages activations through
+// registers; Qwen2 shape at M = 512, ~72 slots per expert: 555 -> 529 us per layer; bf16 and int8
+// measured equal or slower at 32).
 int pick_block_m(int M, int topk, int E, int bits, int dtype) {
   const int64_t slots = (int64_t)M * topk;
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, slots));
   const int64_t avg = (slots + active - 1) / active;
   const int64_t need = avg + avg / 2;
-  const int top = bits == 4 ? 64 : 128;
+  const int top = (bits == 4 && dtype == MOE_DTYPE_FP16) ? 64 : 128;
   for (int bm : {16, 32})
     if (need <= bm) return bm;
   if (bits == 4 && dtype == MOE_DTYPE_FP16 && need <= 128) return 32;
+  // bf16 uint4: 128 rows only where more than 128 are needed (the 64-row kernel measured, and is
+  // kept, below that)
+  if (bits == 4 && need <= 128) return 64;
   return need <= 64 ? 64 : top;
 }
 

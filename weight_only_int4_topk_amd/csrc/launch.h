@@ -77,6 +77,14 @@ size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c);
 constexpr size_t kGemmLdsLimit = 160 * 1024;
 hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
 
+// The prefill tiling (prefill.hip): block_m 128 on the 32x32 matrix cores, 8 wavefronts of
+// prefill_nt(c, N) column tiles of 32.  launch_gemm takes it wherever prefill_fits(c, N).
+bool prefill_fits(const GemmConfig& c, int N);
+int prefill_nt(const GemmConfig& c, int N);
+int prefill_wg_cols(const GemmConfig& c, int N);
+size_t prefill_lds_bytes(const GemmConfig& c);
+hipError_t launch_prefill(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
+
 // out[r, c] = sum_z partial[z, r, c] (z ascending) over rows x cols, rounded to dtype.
 hipError_t launch_split_reduce(const float* partial, int split, int rows, int cols, int dtype,
                                void* out, hipStream_t stream);
