@@ -425,6 +425,248 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillBufs = 2;
 
+// ------------------------------------------------------------------------------------------------
+// w8a8: int8 activations (one float32 scale per row) x int8 weights (one scale per output column),
+// same blocking on v_mfma_i32_32x32x32_i8 (measured 4.35 POP/s on all compute units, against
+// 2.7 for the 16x16x64 form).  A k-block is 64 k (64 bytes of a weight row, 64 bytes of an
+// activation row); lane half h of a column tile loads bytes [32 h, 32 h + 32) of its weight row, so
+// MFMA step s (32 k) takes k = 32 h + 16 s + (0..15) from lane half h: the load's bytes as they are
+// (no decode) for B, and the same 16 bytes of the activation row (logical chunk 2 h + s) for A.
+// Integer sums are exact; the epilogue scales by the row's and the column's scale in float32.
+// ------------------------------------------------------------------------------------------------
+typedef int32_t i32x16_t __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4v_t __attribute__((ext_vector_type(4)));
+
+template <int DT, int MT, int NT, int WAVES, int ACT, int OUTF32>
+__global__ void __launch_bounds__(WAVES * 64, 2) w8a8_mma32_kernel(W8A8Params p) {
+  constexpr int THREADS = WAVES * kWave;
+  constexpr int BM = 32 * MT;
+  constexpr int KB = 64;                          // k (bytes) per k-block
+  constexpr int STEPS = 2;                        // 32x32x32 MFMAs per k-block and tile pair
+  constexpr int VPR = KB / 16;                    // 16-byte chunks of an activation row per k-block
+  constexpr int NCH = BM * VPR;                   // chunks of the tile per k-block
+  constexpr int AV = (NCH + THREADS - 1) / THREADS;
+  static_assert(NCH % kWave == 0 && (NCH >= THREADS ? NCH % THREADS == 0 : true),
+                "whole wavefronts of activation chunks");
+  static_assert(!ACT || NT % 2 == 0, "SiLU epilogue: gate and up tiles in pairs");
+  constexpr int NOUT = ACT ? NT / 2 : NT;
+  constexpr int WG_COLS = WAVES * NOUT * 32;
+  constexpr int LPK = 2 * NT;                     // weight loads per lane and k-block
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_a0[BM * KB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_a1[BM * KB];
+  __shared__ int s_slot[BM];
+  __shared__ float s_as[BM];
+  // 64-byte rows: four rows share a 256-byte bank window, so rows r, r + 4, r + 8, r + 12 take
+  // distinct chunk positions: a fragment read (same logical chunk, 16 rows) hits 16 bank groups
+  auto swz = [](int r) -> int { return (r >> 2) & 3; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int N = p.N, K = p.K;
+  const int n_out = ACT ? N / 2 : N;
+  const int n_chunks = n_out / WG_COLS;
+  const int nc = (int)blockIdx.x % n_chunks;
+  const int blk = (int)blockIdx.x / n_chunks;
+  if (blk * BM >= p.num_post[0]) return;
+  const int e = p.expert_ids[blk];
+  if ((unsigned)e >= (unsigned)p.E) return;
+  if (tid < BM) {
+    const int sl = p.sorted_ids[blk * BM + tid];
+    const bool ok = (unsigned)sl < (unsigned)p.num_slots;
+    s_slot[tid] = ok ? sl : -1;
+    s_as[tid] = ok ? p.a_scales[sl / p.a_row_div] : 0.0f;
+  }
+  const int kb_total = K / KB;
+  const int c32 = lane & 31;
+  const int h = lane >> 5;
+  int col[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if constexpr (ACT) {
+      const int g0 = nc * WG_COLS + wave * NOUT * 32;
+      col[t] = t < NOUT ? g0 + t * 32 : N / 2 + g0 + (t - NOUT) * 32;
+    } else {
+      col[t] = nc * WG_COLS + (wave * NT + t) * 32;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.B + (size_t)e * N * K), (short)0, (int)((size_t)N * K), kRsrc3);
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.A, (short)0, (int)((size_t)p.num_a_rows * K), kRsrc3);
+  uint32_t vw[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) vw[t] = (uint32_t)(col[t] + c32) * (uint32_t)K + h * 32;
+
+  // activation chunks: slot idx = tid + i * THREADS of the unpadded tile (row idx / VPR, physical
+  // chunk idx % VPR holding logical chunk (idx % VPR) ^ swz(row)); a wavefront past the tile's
+  // chunks loads nothing
+  static_assert(NCH < THREADS || (THREADS / VPR) % 16 == 0, "one column offset for all loads");
+  uint32_t arow[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int idx = tid + i * THREADS;
+    const int r = idx / VPR;
+    int sl = -1;
+    if (idx < NCH) sl = p.sorted_ids[blk * BM + r];
+    const int row = (unsigned)sl < (unsigned)p.num_slots ? sl / p.a_row_div : -1;
+    arow[i] = row >= 0 ? (uint32_t)row * (uint32_t)K : 0x80000000u;
+  }
+  const uint32_t acol = (uint32_t)((tid % VPR) ^ swz(tid / VPR)) * 16;
+  auto dma_a = [&](int kb, uint8_t* buf) {
+    const uint32_t kbase = (uint32_t)(kb * KB);
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      if (NCH >= THREADS || wave * kWave < NCH) {
+        const uint32_t off = (arow[i] < 0x80000000u && kb < kb_total) ? arow[i] + kbase + acol
+                                                                       : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs_a,
+            (__attribute__((address_space(3))) void*)(buf + (size_t)(wave * kWave + i * THREADS) * 16),
+            16, off, 0, 0, 0);
+      }
+    }
+  };
+  u32x4_t wq[2][NT][2];
+  auto load_kb = [&](int slot, int kb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wq[slot][t][j] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_w, vw[t] + j * 16, kb * KB, 0));
+  };
+
+  i32x16_t acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][t][i] = 0;
+
+  const int kb_last = kb_total - 1;
+  dma_a(0, s_a0);
+  load_kb(0, 0);
+  load_kb(1, min(1, kb_last));
+  wait_vmcnt_p<2 * LPK>();
+  barrier_lds_p();
+  int n_valid = 0;
+#pragma unroll
+  for (int q = 0; q < BM / kWave; ++q)
+    n_valid += __builtin_popcountll(__ballot(s_slot[q * kWave + lane] >= 0));
+  const int mt_valid = __builtin_amdgcn_readfirstlane((n_valid + 31) / 32);
+  dma_a(1, s_a1);
+
+  const int n_iter = (kb_total + 1) / 2;
+  auto kloop = [&](auto ma_c) {
+    constexpr int MA = decltype(ma_c)::value;
+    for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kb = it * 2 + j;
+        const uint8_t* abuf = j ? s_a1 : s_a0;
+        if (kb < kb_total) {
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st) {
+            const int cl = 2 * h + st;
+#pragma unroll
+            for (int m = 0; m < MA; ++m) {
+              const int row = m * 32 + c32;
+              const u32x4_t a = *(const u32x4_t*)(abuf + row * KB + ((cl ^ swz(row)) * 16));
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+                acc[m][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                    __builtin_bit_cast(i32x4v_t, a), __builtin_bit_cast(i32x4v_t, wq[j][t][st]),
+                    acc[m][t], 0, 0, 0);
+            }
+          }
+        }
+        load_kb(j, min(kb + 2, kb_last));
+        wait_vmcnt_p<LPK>();
+        barrier_lds_p();
+        dma_a(kb + 2, j ? s_a1 : s_a0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  static_assert(MT == 2 || MT == 4, "block_m 64 or 128");
+  if constexpr (MT == 2) {
+    if (mt_valid >= 2) kloop(std::integral_constant<int, 2>{});
+    else kloop(std::integral_constant<int, 1>{});
+  } else {
+    if (mt_valid >= 4) kloop(std::integral_constant<int, 4>{});
+    else if (mt_valid == 3) kloop(std::integral_constant<int, 3>{});
+    else if (mt_valid == 2) kloop(std::integral_constant<int, 2>{});
+    else kloop(std::integral_constant<int, 1>{});
+  }
+  wait_vmcnt_p<0>();
+
+  // epilogue: register i of lane l holds row 8 (i / 4) + 4 h + i % 4 of each 32-row tile
+  const uint16_t* wsc = (const uint16_t*)p.w_scales + (size_t)e * N;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m >= mt_valid) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = m * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+      const int slot = s_slot[r];
+      if (slot < 0) continue;
+      const float sa = s_as[r];
+      const float wscale = p.topk_w ? p.topk_w[slot] : 1.0f;
+#pragma unroll
+      for (int t = 0; t < NOUT; ++t) {
+        const int cc = col[t] + c32;
+        if constexpr (ACT) {
+          const float g = (float)acc[m][t][i] * sa * bits_to_float<DT>(wsc[cc]);
+          const float u = (float)acc[m][t + NOUT][i] * sa * bits_to_float<DT>(wsc[N / 2 + cc]);
+          ((uint16_t*)p.C)[(size_t)slot * (N / 2) + cc] =
+              float_to_bits<DT>(g / (1.0f + __expf(-g)) * u * wscale);
+        } else if constexpr (OUTF32) {
+          const float v = (float)acc[m][t][i] * sa * bits_to_float<DT>(wsc[cc]);
+          ((float*)p.C)[(size_t)slot * N + cc] = v * wscale;
+        } else {
+          const float v = (float)acc[m][t][i] * sa * bits_to_float<DT>(wsc[cc]);
+          ((uint16_t*)p.C)[(size_t)slot * N + cc] = float_to_bits<DT>(v * wscale);
+        }
+      }
+    }
+  }
+}
+
+template <int DT, int MT, int NT>
+hipError_t launch_w8a8_32(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
+  constexpr int WV = kPrefillWaves;
+  const int n_out = act ? p.N / 2 : p.N;
+  const int wg_cols = WV * (act ? NT / 2 : NT) * 32;
+  const long long grid = (long long)(n_out / wg_cols) * p.num_blocks;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 block(WV * kWave);
+  if (act) {
+    if constexpr (NT % 2 == 0)
+      hipLaunchKernelGGL((w8a8_mma32_kernel<DT, MT, NT, WV, 1, 0>), dim3((unsigned)grid), block, 0,
+                         stream, p);
+    else
+      return hipErrorInvalidValue;
+  } else if (out_f32) {
+    hipLaunchKernelGGL((w8a8_mma32_kernel<DT, MT, NT, WV, 0, 1>), dim3((unsigned)grid), block, 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((w8a8_mma32_kernel<DT, MT, NT, WV, 0, 0>), dim3((unsigned)grid), block, 0,
+                       stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int MT>
+hipError_t launch_w8a8_32_nt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
+  if (act || p.N % (kPrefillWaves * 64) == 0) return launch_w8a8_32<DT, MT, 2>(p, act, out_f32, stream);
+  return launch_w8a8_32<DT, MT, 1>(p, act, out_f32, stream);
+}
+
+
 template <int DT, int BITS, int MT, int NT, int WAVES, int NBUF>
 hipError_t launch_nt(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
   const int n_out = c.act ? p.N / 2 : p.N;
@@ -486,6 +728,22 @@ bool prefill_fits(const GemmConfig& c, int N) {
 size_t prefill_lds_bytes(const GemmConfig& c) {
   const int kb = c.bits == 4 ? 128 : 64;
   return sizeof(uint16_t) * kPrefillBufs * (size_t)c.block_m * kb + sizeof(int) * (size_t)c.block_m;
+}
+
+bool w8a8_mma32_fits(int block_m, int act, int N) {
+  if (block_m != 64 && block_m != 128) return false;
+  if (act) return (N / 2) % (kPrefillWaves * 32) == 0;
+  return N % (kPrefillWaves * 32) == 0;
+}
+
+hipError_t launch_w8a8_mma32(const W8A8Params& p, int block_m, int act, int dtype, int out_f32,
+                             hipStream_t stream) {
+  if (!w8a8_mma32_fits(block_m, act, p.N)) return hipErrorInvalidValue;
+  if (dtype == 0)
+    return block_m == 64 ? launch_w8a8_32_nt<0, 2>(p, act, out_f32, stream)
+                         : launch_w8a8_32_nt<0, 4>(p, act, out_f32, stream);
+  return block_m == 64 ? launch_w8a8_32_nt<1, 2>(p, act, out_f32, stream)
+                       : launch_w8a8_32_nt<1, 4>(p, act, out_f32, stream);
 }
 
 hipError_t launch_prefill(const GemmParams& p_in, const GemmConfig& c, hipStream_t stream) {

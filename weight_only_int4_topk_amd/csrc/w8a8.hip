@@ -277,6 +277,8 @@ hipError_t launch_quant_rows(const void* x, int rows, int K, int dtype, int8_t* 
 
 hipError_t launch_w8a8_gemm(const W8A8Params& p, int block_m, int act, int dtype,
                             hipStream_t stream, int out_f32) {
+  if (w8a8_mma32_fits(block_m, act, p.N))
+    return launch_w8a8_mma32(p, block_m, act, dtype, out_f32, stream);
   return dtype == 0 ? launch_w8a8_dt<0>(p, block_m, act, out_f32, stream)
                     : launch_w8a8_dt<1>(p, block_m, act, out_f32, stream);
 }
