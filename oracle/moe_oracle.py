@@ -40,6 +40,7 @@ __all__ = [
     "align_capacity", "align_block_size", "silu", "ExpertSource", "moe_layer", "moe_layer_rows",
     "grouped_gemm", "dense_gemm", "batched_gemm", "quant_int8_rows", "w8a8_grouped_gemm",
     "round_to_dtype", "moe_layer_w8a8_rows", "dequant_uint4_gidx", "to_numpy",
+    "AWQ_PACK_ORDER", "unpack_gptq", "unpack_awq", "canonical_from_checkpoint",
 ]
 
 
@@ -526,3 +527,71 @@ def dequant_uint4_gidx(qweight, scales, zeros, g_idx) -> np.ndarray:
     assert q.shape[1] == g.shape[0] and g.min() >= 0 and g.max() < s.shape[1]
     return (q - z[:, g]) * s[:, g]
 
+
+
+# ================================================================================================
+# GPTQ / AWQ checkpoint storage -> the canonical storage
+# ================================================================================================
+# The review thread of "[Kernel] add triton fused moe kernel for gptq/awq" asks for a weight format
+# that accepts GPTQ and AWQ checkpoints, and the small-n GEMM of "[Kernel] optimize performance of
+# gptq marlin kernel when n is small" takes a g_idx and sort_indices; the pages print neither
+# checkpoint's packing.  The reading used (the layouts those checkpoint families ship), per expert:
+#   GPTQ: qweight int32 [K/8, N], code (k, n) in bits 4 (k % 8) .. + 3 of word [k / 8, n];
+#         qzeros int32 [K/128, N/8], zero (g, n) in bits 4 (n % 8) of word [g, n / 8];
+#         scales [K/128, N]; optional g_idx int32 [K] (act-order: the group of input column k).
+#   AWQ:  qweight int32 [K, N/8], code (k, n) in nibble j of word [k, n / 8] where column
+#         n % 8 = AWQ_PACK_ORDER[j]; qzeros int32 [K/128, N/8] packed the same way; scales [K/128, N].
+# Zero points are stored as they are (no offset); decoded weight (q - z) * s.
+AWQ_PACK_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def _nibble(words, j):
+    return (np.asarray(words, dtype=np.int64) >> (4 * j)) & 0xF
+
+
+def unpack_gptq(qweight, qzeros):
+    """GPTQ words -> (q uint8 [K, N], z uint8 [K/128, N]) for one expert."""
+    qw = np.asarray(to_numpy(qweight)).astype(np.int64) & 0xFFFFFFFF
+    qz = np.asarray(to_numpy(qzeros)).astype(np.int64) & 0xFFFFFFFF
+    K8, N = qw.shape
+    q = np.empty((8 * K8, N), np.uint8)
+    for j in range(8):                       # k = 8 * row + j
+        q[j::8, :] = _nibble(qw, j)
+    G, N8 = qz.shape
+    z = np.empty((G, 8 * N8), np.uint8)
+    for j in range(8):                       # n = 8 * word + j
+        z[:, j::8] = _nibble(qz, j)
+    return q, z
+
+
+def unpack_awq(qweight, qzeros):
+    """AWQ words -> (q uint8 [K, N], z uint8 [K/128, N]) for one expert."""
+    qw = np.asarray(to_numpy(qweight)).astype(np.int64) & 0xFFFFFFFF
+    qz = np.asarray(to_numpy(qzeros)).astype(np.int64) & 0xFFFFFFFF
+    K, N8 = qw.shape
+    q = np.empty((K, 8 * N8), np.uint8)
+    z = np.empty((qz.shape[0], 8 * N8), np.uint8)
+    for j, c in enumerate(AWQ_PACK_ORDER):   # nibble j holds column 8 * word + c
+        q[:, c::8] = _nibble(qw, j)
+        z[:, c::8] = _nibble(qz, j)
+    return q, z
+
+
+def canonical_from_checkpoint(q, z, scales, g_idx=None):
+    """(q [K, N], z [G, N], scales [G, N], g_idx [K] or None) of one expert -> the canonical storage
+    (qweight uint8 [N, K/2] with k = 2j in the low nibble of byte j, scales [N, G], zeros uint8
+    [N, G/2] with group 2j in the low nibble of byte j) and, with g_idx, perm int32 [K]: the stable
+    argsort of g_idx, the storage then holding column perm[j] at position j (the sorted storage of
+    the act-order layer, whose group g is positions 128 g .. 128 g + 127)."""
+    q = np.asarray(q, dtype=np.uint8)
+    z = np.asarray(z, dtype=np.uint8)
+    perm = None
+    if g_idx is not None:
+        perm = np.argsort(np.asarray(to_numpy(g_idx)).astype(np.int64), kind="stable")
+        q = q[perm, :]
+    qt = q.T                                  # [N, K]
+    packed = (qt[:, 0::2] | (qt[:, 1::2] << 4)).astype(np.uint8)
+    zt = z.T                                  # [N, G]
+    zpacked = (zt[:, 0::2] | (zt[:, 1::2] << 4)).astype(np.uint8)
+    sc = np.ascontiguousarray(np.asarray(to_numpy(scales)).T)
+    return packed, sc, zpacked, (None if perm is None else perm.astype(np.int32))

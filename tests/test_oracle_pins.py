@@ -586,3 +586,75 @@ def test_dequant_gidx_sorted_columns_give_the_grouped_storage():
     perm = np.argsort(g_idx, kind="stable")
     sorted_w = O.dequant_uint4(_pack_nibbles(q[:, perm]), s, _pack_nibbles(z))
     np.testing.assert_array_equal(w[:, perm], sorted_w)
+
+
+# ---- GPTQ / AWQ checkpoint storage -> canonical storage ----------------------------------------
+def _pack_words(vals):
+    """[..., 8] nibble values -> int32 words (value i in bits 4i..4i+3), written out directly."""
+    v = np.asarray(vals, dtype=np.int64)
+    w = np.zeros(v.shape[:-1], np.int64)
+    for i in range(8):
+        w |= v[..., i] << (4 * i)
+    return w.astype(np.uint32).view(np.int32)
+
+
+def _golden_expert():
+    K, N = 256, 8
+    k = np.arange(K)[:, None]
+    n = np.arange(N)[None, :]
+    q = (k + 3 * n) % 16                                        # [K, N]
+    g = np.arange(K // 128)[:, None]
+    z = (g + n + 1) % 16                                        # [G, N]
+    s = (0.125 * (g + 1) + 0.0078125 * n).astype(np.float16)    # [G, N]
+    return q, z, s
+
+
+def test_gptq_awq_unpack_golden(golden):
+    """The hand-worked words of tests/golden/gptq_awq_layout.txt: the test packs whole tensors by
+    the stated layout (its own code), checks those words, and the oracle unpacks them back."""
+    g = golden("gptq_awq_layout.txt")
+    q, z, s = _golden_expert()
+    K, N = q.shape
+    # GPTQ: word [k8, n] = codes k = 8 k8 .. 8 k8 + 7; zeros word [g, n8] = columns 8 n8 ..
+    gq = _pack_words(q.reshape(K // 8, 8, N).transpose(0, 2, 1))
+    gz = _pack_words(z.reshape(z.shape[0], N // 8, 8))
+    # AWQ: word [k, n8], nibble j = column 8 n8 + order[j]
+    order = list(O.AWQ_PACK_ORDER)
+    aq = _pack_words(q.reshape(K, N // 8, 8)[..., order])
+    az = _pack_words(z.reshape(z.shape[0], N // 8, 8)[..., order])
+    h = lambda v: int(v) & 0xFFFFFFFF
+    assert h(gq[0, 0]) == int(g["gptq.qweight[0,0]"][0], 16)
+    assert h(gq[1, 1]) == int(g["gptq.qweight[1,1]"][0], 16)
+    assert h(gz[0, 0]) == int(g["gptq.qzeros[0,0]"][0], 16)
+    assert h(aq[0, 0]) == int(g["awq.qweight[0,0]"][0], 16)
+    assert h(az[1, 0]) == int(g["awq.qzeros[1,0]"][0], 16)
+    for unpack, (wq, wz) in ((O.unpack_gptq, (gq, gz)), (O.unpack_awq, (aq, az))):
+        uq, uz = unpack(wq, wz)
+        np.testing.assert_array_equal(uq, q)
+        np.testing.assert_array_equal(uz, z)
+
+
+def test_canonical_from_checkpoint_golden(golden):
+    g = golden("gptq_awq_layout.txt")
+    q, z, s = _golden_expert()
+    B, sc, zz, perm = O.canonical_from_checkpoint(q, z, s)
+    assert perm is None
+    assert B[1, 0] == int(g["canon.B[1,0]"][0], 16)
+    assert B[0, 5] == int(g["canon.B[0,5]"][0], 16)
+    assert zz[2, 0] == int(g["canon.zeros[2,0]"][0], 16)
+    assert float(sc[3, 1]) == float(g["canon.scales[3,1]"][0])
+    # the canonical storage decodes to (q - z) * s of the checkpoint, element by element
+    w = O.dequant_uint4(B, sc, zz)
+    for (kk, nn) in [(0, 0), (255, 7), (130, 3)]:
+        assert w[nn, kk] == (q[kk, nn] - z[kk // 128, nn]) * float(s[kk // 128, nn])
+    # act-order
+    g_idx = (np.arange(256) // 2) % 2
+    B2, sc2, zz2, perm = O.canonical_from_checkpoint(q, z, s, g_idx)
+    assert perm[0:4].tolist() == [int(v) for v in g["act.perm.0_to_3"][0].split()]
+    assert perm[128:132].tolist() == [int(v) for v in g["act.perm.128_to_131"][0].split()]
+    assert B2[0, 1] == int(g["act.B[0,1]"][0], 16)
+    assert B2[0, 64] == int(g["act.B[0,64]"][0], 16)
+    # the sorted storage with its permutation decodes like the GPTQ definition with g_idx
+    qpacked_orig = (q.T[:, 0::2] | (q.T[:, 1::2] << 4)).astype(np.uint8)
+    w_gidx = O.dequant_uint4_gidx(qpacked_orig, s.T, zz2, g_idx)
+    np.testing.assert_array_equal(O.dequant_uint4(B2, sc2, zz2), w_gidx[:, perm])
