@@ -260,6 +260,34 @@ int fused_moe_wna16_act_order(const void* x, const float* router_logits, int M, 
 size_t fused_moe_wna16_act_order_workspace_size(int M, int H, int I, int E, int topk, int dtype,
                                                 int block_m);
 
+/* GPTQ / AWQ checkpoint storage of E experts -> the canonical uint4 storage above, on the device.
+ * "[Kernel] add triton fused moe kernel for gptq/awq" (review thread) asks for a weight format that
+ * accepts GPTQ and AWQ checkpoints; the pages print neither checkpoint's packing, and the layouts
+ * read here are the ones those checkpoint families ship, per expert (N output rows, K inputs):
+ *   format 0 (GPTQ): qweight int32 [E, K/8, N], code (k, n) in bits 4 (k % 8) .. + 3 of word
+ *     [k / 8, n]; qzeros int32 [E, K/128, N/8], zero (g, n) in bits 4 (n % 8) of word [g, n / 8];
+ *     scales dtype [E, K/128, N]; g_idx int32 [E, K] (act-order: input column k is in group
+ *     g_idx[k]) or NULL.
+ *   format 1 (AWQ): qweight int32 [E, K, N/8], code (k, n) in nibble j of word [k, n / 8] where
+ *     n % 8 = (0, 2, 4, 6, 1, 3, 5, 7)[j]; qzeros int32 [E, K/128, N/8] packed the same way;
+ *     scales dtype [E, K/128, N]; g_idx must be NULL.
+ *   Zero points are taken as stored (decoded weight (q - z) * s; no "z - 1" offset).
+ * Writes B uint8 [E, N, K/2], scales_out dtype [E, N, K/128], zeros_out uint8 [E, N, K/256].  With
+ * g_idx it also writes perm_out int32 [E, K], the stable argsort of each expert's g_idx, and B holds
+ * the columns in that order: the sorted storage fused_moe_wna16_act_order takes (w13 of a gate and
+ * an up matrix sharing one g_idx: repack each into its rows of w13, or repack a [E, 2I]-row
+ * checkpoint).  Each group must hold exactly 128 columns; otherwise a short group is padded with the
+ * column index K (read as zero by the act-order layer), columns past a full group or with g_idx
+ * outside [0, K/128) are left out, and each such column adds 1 to *invalid_out (a device int32 the
+ * caller zeroes first; NULL: not counted).
+ * Limits: K % 256 == 0, N % 8 == 0, K <= 16384 with g_idx.  Alignment: B 16 bytes, scales_out 4,
+ * zeros_out and scales 2, int32 arrays 4.  Asynchronous on stream; allocates nothing. */
+enum { MOE_FORMAT_GPTQ = 0, MOE_FORMAT_AWQ = 1 };
+int moe_repack_uint4(int format, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                     const int32_t* g_idx, int E, int N, int K, int dtype, uint8_t* B,
+                     void* scales_out, uint8_t* zeros_out, int32_t* perm_out, int32_t* invalid_out,
+                     void* stream);
+
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
  * bits and activations of `dtype`: the smallest of {16, 32, 64, 128} that holds 1.5x the average
  * number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots share one

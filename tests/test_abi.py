@@ -392,3 +392,21 @@ def test_noalloc_scratch_limit(lib):
     assert f(FAKE, FAKE, 0, 4096, 14336, 8, 2, _rt(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, q4, 0,
              0, FAKE, NULL, NULL, NULL) == OK
     assert B.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_repack_validation(lib):
+    f = lib.moe_repack_uint4
+    def r(fmt=0, qw=FAKE, qz=FAKE, sc=FAKE, g=NULL, E=2, N=64, K=256, dt=0, b=FAKE, so=FAKE, zo=FAKE,
+          perm=NULL, inv=NULL):
+        return f(fmt, qw, qz, sc, g, E, N, K, dt, b, so, zo, perm, inv, NULL)
+    assert r(fmt=2) == INVALID
+    assert r(dt=3) == UNSUPPORTED
+    assert r(K=300) == UNSUPPORTED
+    assert r(N=60) == UNSUPPORTED                               # N % 8
+    assert r(fmt=1, g=FAKE, perm=FAKE) == UNSUPPORTED           # AWQ has no act-order
+    assert r(g=FAKE) == INVALID                                 # g_idx without perm_out
+    assert r(perm=FAKE) == INVALID                              # perm_out without g_idx
+    assert r(g=FAKE, perm=FAKE, K=16384 + 256) == UNSUPPORTED   # group ids staged in LDS
+    assert r(qw=NULL) == INVALID
+    assert r(b=ctypes.c_void_p(0x100008)) == INVALID            # B must be 16-byte aligned
+    assert r(E=0) == INVALID

@@ -18,7 +18,8 @@ __all__ = [
     "moe_wna16_gemm", "moe_wna16_dense_gemm", "moe_wna16_dense_gemm_workspace_size",
     "moe_wna16_batched_gemm", "moe_quant_int8_rows", "moe_w8a8_gemm", "fused_moe_w8a8",
     "fused_moe_wna16_act_order", "fused_moe_wna16_workspace_size", "fused_moe_wna16",
-    "fused_moe_wna16_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "fused_moe_wna16_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_repack_uint4", "FORMAT_GPTQ",
+    "FORMAT_AWQ",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wna16.so")
@@ -80,6 +81,9 @@ _SIGS = {
                                  _P, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _P, _P, _P, _P],
                                 _I),
 }
+
+_SIGS["moe_repack_uint4"] = ([_I, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I)
+FORMAT_GPTQ, FORMAT_AWQ = 0, 1
 
 # MOE_NOALLOC_SCRATCH_BYTES of the header: the static scratch of fused_moe_wna16_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -430,3 +434,30 @@ def fused_moe_wna16_noalloc(x, router_logits, topk, rt: MoeRouting, w13, w13_sca
                                          _dtype_code(x.dtype), block_m, _ptr(out),
                                          _ptr(topk_weights), _ptr(topk_ids), _stream(stream)))
     return out
+
+
+def moe_repack_uint4(fmt, qweight, qzeros, scales, g_idx=None, invalid=None, stream=None):
+    """GPTQ (fmt 0) / AWQ (fmt 1) checkpoint tensors of E experts -> (B, scales, zeros[, perm]) in
+    the canonical storage (with g_idx: the act-order sorted storage and its permutation)."""
+    if qweight.dtype != torch.int32 or qzeros.dtype != torch.int32:
+        raise MoeError(-1, "qweight and qzeros must be int32")
+    E = qweight.shape[0]
+    if fmt == FORMAT_GPTQ:
+        K, N = qweight.shape[1] * 8, qweight.shape[2]
+    else:
+        K, N = qweight.shape[1], qweight.shape[2] * 8
+    G = K // 128
+    _want(qweight, (E, K // 8, N) if fmt == FORMAT_GPTQ else (E, K, N // 8), torch.int32, "qweight")
+    _want(qzeros, (E, G, N // 8), torch.int32, "qzeros")
+    _want(scales, (E, G, N), scales.dtype, "scales")
+    _want(g_idx, (E, K), torch.int32, "g_idx")
+    _want(invalid, (1,), torch.int32, "invalid")
+    dev = qweight.device
+    B = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    so = torch.empty((E, N, G), dtype=scales.dtype, device=dev)
+    zo = torch.empty((E, N, G // 2), dtype=torch.uint8, device=dev)
+    perm = torch.empty((E, K), dtype=torch.int32, device=dev) if g_idx is not None else None
+    _check(lib().moe_repack_uint4(fmt, _ptr(qweight), _ptr(qzeros), _ptr(scales), _ptr(g_idx), E, N,
+                                  K, _dtype_code(scales.dtype), _ptr(B), _ptr(so), _ptr(zo),
+                                  _ptr(perm), _ptr(invalid), _stream(stream)))
+    return (B, so, zo) if perm is None else (B, so, zo, perm)

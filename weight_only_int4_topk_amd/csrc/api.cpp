@@ -743,6 +743,34 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
   return MOE_OK;
 }
 
+int moe_repack_uint4(int format, const int32_t* qweight, const int32_t* qzeros, const void* scales,
+                     const int32_t* g_idx, int E, int N, int K, int dtype, uint8_t* B,
+                     void* scales_out, uint8_t* zeros_out, int32_t* perm_out,
+                     int32_t* invalid_out, void* stream) {
+  if (format != MOE_FORMAT_GPTQ && format != MOE_FORMAT_AWQ)
+    return fail(MOE_ERR_INVALID_ARG, "format = %d (0 GPTQ, 1 AWQ)", format);
+  if (int rc = check_dtype(dtype)) return rc;
+  if (E <= 0 || N <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "E=%d N=%d K=%d", E, N, K);
+  if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
+  if (N % 8) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 8", N);
+  if (format == MOE_FORMAT_AWQ && g_idx)
+    return fail(MOE_ERR_UNSUPPORTED, "AWQ checkpoints carry no g_idx (act-order is GPTQ's)");
+  if ((g_idx == nullptr) != (perm_out == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "g_idx and perm_out go together (both or neither)");
+  if (g_idx && K > 16384)
+    return fail(MOE_ERR_UNSUPPORTED, "act-order repack: K = %d > 16384 (group ids staged in LDS)", K);
+  if (!qweight || !qzeros || !scales || !B || !scales_out || !zeros_out)
+    return fail(MOE_ERR_INVALID_ARG, "NULL checkpoint or output pointer");
+  if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(B, 16) ||
+      !aligned(scales_out, 4) || !aligned(zeros_out, 2) || (g_idx && !aligned(g_idx, 4)) ||
+      (perm_out && !aligned(perm_out, 4)) || (invalid_out && !aligned(invalid_out, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned pointer argument");
+  hipError_t e = moe::launch_repack_uint4(format, qweight, qzeros, scales, g_idx, E, N, K, B,
+                                          scales_out, zeros_out, perm_out, invalid_out,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "repack launch");
+}
+
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
                                       const moe_quant_t* quant, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || !quant) return 0;

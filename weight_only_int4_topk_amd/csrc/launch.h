@@ -121,6 +121,12 @@ hipError_t launch_w8a8_mma32(const W8A8Params& p, int block_m, int act, int dtyp
 hipError_t launch_gather_cols(const void* in, int div, const int32_t* ids, int E,
                               const int32_t* perm, int K, int slots, int dtype, void* out,
                               hipStream_t stream);
+// GPTQ (format 0) / AWQ (format 1) checkpoint storage of E experts -> canonical uint4 storage;
+// g_idx non-NULL (GPTQ act-order): perm_out [E, K] and the sorted storage (repack.hip)
+hipError_t launch_repack_uint4(int format, const int32_t* qweight, const int32_t* qzeros,
+                               const void* scales, const int32_t* g_idx, int E, int N, int K,
+                               uint8_t* B, void* scales_out, uint8_t* zeros_out, int32_t* perm_out,
+                               int32_t* invalid, hipStream_t stream);
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);
 // inter[s, i] = SiLU(sum_z partial[z, s, i]) * sum_z partial[z, s, I + i] (first GEMM split over K)
