@@ -311,8 +311,10 @@ size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, cons
  *   out           device dtype [M, H]
  *   topk_weights_out / topk_ids_out: optional device [M, topk] copies of the routing result
  *   block_m       0 = library's choice, else one of {16, 32, 64, 128}
- * Launches: routing, align, GEMM1 (+SiLU*up), GEMM2 (split over K into float32 partials),
- * combine.  Deterministic: identical inputs give bitwise identical outputs.
+ * Launches: routing and align (one launch for M <= 4), GEMM1 (+SiLU*up; split over K into float32
+ * partials and a SiLU*up pass when its workgroups would not fill the chip), GEMM2 (split over K into
+ * float32 partials at small M; unsplit with block_m 64, it writes dtype rows times the routing
+ * weight), combine (float32 sums in a fixed order).  Deterministic: identical inputs give bitwise identical outputs.
  * Limits: those of the calls above with N = 2I and N = H; H % 256 == 0, I % 256 == 0,
  * M * topk <= 2^24, and below 2^31 bytes (32-bit offsets): x (M * H * 2), the intermediate rows
  * (M * topk * I * 2) and one expert's w13. */

@@ -387,8 +387,9 @@ def test_fused_zero_activations_give_zero():
 def test_fused_largest_batch_sampled():
     """The largest batch the layer accepts at the DeepSeek-V3 prefill shape: M = 65535 keeps the
     intermediate rows (M * topk * I * 2 bytes) under 2 GiB, one token more is refused.  The second
-    GEMM's float32 partials then hold 3.8e9 values (15 GB), so their offsets and the combine's pass
-    2^32 bytes.  Three tokens (first, middle, last) against the oracle, routing included."""
+    GEMM's float32 rows then hold 3.8e9 values (15 GB), so their offsets and the combine's pass
+    2^32 bytes.  256 evenly spaced tokens (first and last included) against the oracle, routing
+    included."""
     wl = W["dsv3_prefill_int4"]
     M = 65535
     assert M * wl.topk * wl.I * 2 < 2**31 <= (M + 1) * wl.topk * wl.I * 2
@@ -397,12 +398,14 @@ def test_fused_largest_batch_sampled():
     lg = synth.make_logits(wl, M, seed=0, device="cuda")
     print(f"fused largest batch M={M}", flush=True)
     out, tw, ti = run_fused(wl, x, lg, layer)
-    rows = [0, M // 2, M - 1]
+    rows = spaced_rows(M)
     ids_ref, w_ref = oracle_route(wl, lg[rows])          # routing is per token
     assert np.array_equal(O.to_numpy(ti)[rows], ids_ref), "topk ids differ"
     assert_weights_close(tw[rows], w_ref)
     experts = sorted(set(ids_ref.reshape(-1).tolist()))
     src = O.ExpertSource(expert_subset(layer, experts), wl.bits, experts)
-    ref, _ = O.moe_layer_rows(x[rows].cpu(), ids_ref, w_ref, src, np.arange(len(rows)))
+    del layer
+    ref, _ = O.moe_layer_rows(x[rows].cpu(), ids_ref, w_ref, src, np.arange(len(rows)),
+                              workers=ORACLE_WORKERS)
     assert_layer_close(O.to_numpy(out)[rows], ref, f"dsv3 prefill M={M}")
     assert torch.isfinite(out[-4096:].float()).all()

@@ -122,8 +122,8 @@ def test_fused_w8a8_dsv3_full_size_spaced_tokens():
 def test_fused_w8a8_largest_batch_sampled():
     """The largest batch the w8a8 layer accepts at the DeepSeek-V3 int8 shape: M = 131071 keeps the
     second GEMM's int8 activations (M * topk * I bytes) under 2 GiB, one token more is refused.
-    Its float32 rows then take 30 GB and the combine reads them past 2^34 bytes.  256 evenly spaced
-    tokens (first and last included) against the oracle, their routing exact."""
+    Its float32 rows then take 30 GB and the combine reads them past 2^34 bytes.  256
+    evenly spaced tokens (first and last included) against the oracle, their routing exact."""
     wl = synth.WORKLOADS["dsv3_prefill_int8"]
     M = 131071
     assert M * wl.topk * wl.I < 2**31 <= (M + 1) * wl.topk * wl.I

@@ -658,8 +658,8 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
   if (H > kW8A8MaxK || I > kW8A8MaxK)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d or I = %d > %d (int32 sums)", H, I, kW8A8MaxK);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");
-  // 32-bit buffer offsets: the int8 activations of either GEMM, one expert's weights (the float32
-  // rows of the second GEMM and the combine use 64-bit addresses)
+  // 32-bit buffer offsets: the int8 activations of either GEMM, one expert's weights (the rows the
+  // second GEMM writes and the combine reads use 64-bit addresses)
   if ((int64_t)M * H >= ((int64_t)1 << 31) || (int64_t)M * topk * I >= ((int64_t)1 << 31) ||
       (int64_t)2 * I * H >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "int8 activations or one expert's weights exceed 2 GiB");
@@ -831,7 +831,13 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   // wavefront so the workgroup count matches the estimate the split was chosen for
   moe::GemmConfig c1{dtype, quant->bits, pl.bm, split1 ? 0 : 1, split1 ? 1 : 0,
                      split1 ? 2 : pl.ntw1, split1 ? 4 : pl.wv1};
-  moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, 1, pl.ntw2, pl.wv2};
+  // second GEMM unsplit with 64-row blocks: rows weighted in its epilogue and written in the
+  // activation dtype, half the bytes of float32 rows for the combine to read back (DeepSeek-V3
+  // prefill at 1024 tokens: layer -1.2 to -1.6 %, same box, same process).  Not with 128-row
+  // blocks, whose 32x32 result layout leaves each lane one 2-byte column per row: there the
+  // half-line writes cost more than the bytes saved (4096 tokens: +1 to +3 %).
+  const bool rows2 = pl.split2 == 1 && pl.bm == 64;
+  moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, rows2 ? 0 : 1, pl.ntw2, pl.wv2};
   if (int rc = fit_lds(H, pl.split1, c1, "gemm1")) return rc;
   if (int rc = fit_lds(I, pl.split2, c2, "gemm2")) return rc;
 
@@ -909,10 +915,12 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   g2.K = I;
   g2.C = part;
   g2.split_k = pl.split2;
+  g2.topk_w = rows2 ? tw : nullptr;
   e = moe::launch_gemm(g2, c2, st);
   if (e != hipSuccess) return hip_fail(e, "gemm2 launch");
 
-  e = moe::launch_combine(part, pl.split2, tw, M, topk, H, dtype, out, st);
+  e = rows2 ? moe::launch_combine_rows(part, M, topk, H, dtype, out, st)
+            : moe::launch_combine(part, pl.split2, tw, M, topk, H, dtype, out, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return MOE_OK;
 }

@@ -127,6 +127,46 @@ __global__ void __launch_bounds__(256) combine_quarters_kernel(const float* __re
   }
 }
 
+// The second GEMM unsplit, its rows already weighted and rounded to the activation dtype: out[m] =
+// sum_j y[m * topk + j] in float32, j ascending, rounded once.  Half the bytes of the float32 rows
+// (DeepSeek-V3 prefill at 4096 tokens: 470 MB instead of 940 MB written and read back).  Each
+// thread sums 8 columns of one token, the topk rows loaded kBatch at a time.
+template <int DT>
+__global__ void __launch_bounds__(256) combine_rows_kernel(const uint16_t* __restrict__ y, int M,
+                                                           int topk, int H,
+                                                           uint16_t* __restrict__ out) {
+  const int h8 = H / 8;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)M * h8) return;
+  const int m = (int)(idx / h8);
+  const int c = (int)(idx - (size_t)m * h8) * 8;
+  const uint16_t* src = y + (size_t)m * topk * H + c;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < topk; j0 += kBatch) {
+    u32x4_t t[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (j0 + q < topk) t[q] = *(const u32x4_t*)(src + (size_t)(j0 + q) * H);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (j0 + q < topk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = t[q][i];
+          acc[2 * i] += bits_to_float<DT>((uint16_t)(w & 0xFFFFu));
+          acc[2 * i + 1] += bits_to_float<DT>((uint16_t)(w >> 16));
+        }
+      }
+    }
+  }
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = DT == 0 ? f32x2_to_f16x2(acc[2 * i], acc[2 * i + 1])
+                   : f32x2_to_bf16x2(acc[2 * i], acc[2 * i + 1]);
+  *(u32x4_t*)(out + (size_t)m * H + c) = o;
+}
+
 // First GEMM split over K: inter[s, i] = SiLU(g) * u with g = sum_z partial[z, s, i] and
 // u = sum_z partial[z, s, I + i] (z ascending), rounded to dtype; four columns per thread.
 template <int DT>
@@ -277,6 +317,24 @@ hipError_t launch_combine(const float* partial, int split, const float* topk_w, 
   else
     hipLaunchKernelGGL(combine_kernel<1>, dim3(grid), dim3(256), 0, stream, partial, split, stride,
                        topk_w, M, topk, H, (uint16_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_combine_rows(const void* y, int M, int topk, int H, int dtype, void* out,
+                               hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const size_t total = (size_t)M * (H / 8);
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(combine_rows_kernel<0>, dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t*)y, M, topk, H, (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(combine_rows_kernel<1>, dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t*)y, M, topk, H, (uint16_t*)out);
   return hipGetLastError();
 }
 

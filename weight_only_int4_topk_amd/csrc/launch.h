@@ -129,6 +129,10 @@ hipError_t launch_repack_uint4(int format, const int32_t* qweight, const int32_t
                                int32_t* invalid, hipStream_t stream);
 hipError_t launch_combine(const float* partial, int split, const float* topk_w, int M, int topk,
                           int H, int dtype, void* out, hipStream_t stream);
+// out[m] = sum_j y[m * topk + j] (j ascending, float32) for dtype rows y [M * topk, H] that already
+// carry their routing weight (the second GEMM unsplit); H % 8 == 0
+hipError_t launch_combine_rows(const void* y, int M, int topk, int H, int dtype, void* out,
+                               hipStream_t stream);
 // inter[s, i] = SiLU(sum_z partial[z, s, i]) * sum_z partial[z, s, I + i] (first GEMM split over K)
 hipError_t launch_act_combine(const float* partial, int split, int slots, int I, int dtype,
                               void* inter, hipStream_t stream);
