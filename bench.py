@@ -360,16 +360,19 @@ def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
         x = synth.make_x(wl, M, seed=seed, device="cuda")
         lg = synth.make_logits(wl, M, seed=seed, device="cuda")
         tw, ti = B.moe_topk_softmax(lg, wl.topk, rt)
-        bm = B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype)   # the layers' choice
-        st, ex, npost = B.moe_align_block_size(ti, wl.E, bm)
+        # the layers' choices: the w8a16 layer's block size, at most 128 rows for w8a8
+        bm16 = B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype)
+        bm8 = min(128, bm16)
+        st, ex, npost = B.moe_align_block_size(ti, wl.E, bm8)
+        st16, ex16, np16 = B.moe_align_block_size(ti, wl.E, bm16)
         q, sa = B.moe_quant_int8_rows(x)
         ns = M * wl.topk
         h = torch.empty((ns, wl.I), dtype=wl.torch_dtype, device="cuda")
         t_q = graph_replay([lambda: B.moe_quant_int8_rows(x, q, sa)], steps, warmup)[0] / steps
         f8 = [(lambda c=c: B.moe_w8a8_gemm(q, sa, wl.topk, c["w13"], c["w13_scales"], st, ex, npost,
-                                           bm, ns, wl.torch_dtype, act=1, C=h)) for c in copies]
-        f16 = [(lambda c=c: B.moe_wna16_gemm(x, wl.topk, c["w13"], c["w13_scales"], None, st, ex,
-                                             npost, bm, ns, act=1, C=h)) for c in copies]
+                                           bm8, ns, wl.torch_dtype, act=1, C=h)) for c in copies]
+        f16 = [(lambda c=c: B.moe_wna16_gemm(x, wl.topk, c["w13"], c["w13_scales"], None, st16, ex16,
+                                             np16, bm16, ns, act=1, C=h)) for c in copies]
         t8 = graph_replay(f8, steps, warmup)[0] / steps
         t16 = graph_replay(f16, steps, warmup)[0] / steps
         # the whole layer both ways, same weights, routing computed inside
@@ -387,7 +390,8 @@ def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
         tl8 = graph_replay(l8, steps, warmup)[0] / steps
         tl16 = graph_replay(l16, steps, warmup)[0] / steps
         ops = 4.0 * wl.H * wl.I * ns
-        out.append({"M": M, "block_m": bm, "quant_us": round(t_q * 1e6, 2),
+        out.append({"M": M, "block_m_w8a8": bm8, "block_m_w8a16": bm16,
+                    "quant_us": round(t_q * 1e6, 2),
                     "w8a8_w13_us": round(t8 * 1e6, 2), "w8a8_TOPs": round(ops / t8 / 1e12, 1),
                     "w8a8_int8_mfma_frac": round(ops / t8 / 1e12 / 5000.0, 4),
                     "w8a16_w13_us": round(t16 * 1e6, 2), "w8a16_TFLOPs": round(ops / t16 / 1e12, 1),
@@ -587,7 +591,8 @@ def main():
     if traffic is not None:
         roof["traffic"] = round(traffic / (res["w13_us"] * 1e-6) / 1e9, 1)
         roof["traffic_bytes_per_launch"] = traffic
-    roof.update({"kernel": f"wna16_gemm_kernel (w13 + SiLU*up, block_m {res['block_m']})",
+    kname = "prefill_gemm_kernel" if res["block_m"] >= 128 else "wna16_gemm_kernel"
+    roof.update({"kernel": f"{kname} (w13 + SiLU*up, block_m {res['block_m']})",
                  "avg_launch_us": res["w13_us"],
                  "algorithmic_per_launch": (res["w13_bytes"] if roof["bound"] == "hbm"
                                             else 4.0 * wl.H * wl.I * M * wl.topk)})

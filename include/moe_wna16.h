@@ -110,7 +110,7 @@ int64_t moe_align_capacity(int numel, int E, int block_m);
  * Ids outside [0, E) are not listed (a slot of another shard).  The result is deterministic.
  * numel = 0 writes T = 0 (and sentinels / -1 over any capacity given); with capacity 0 the
  * sorted_token_ids and expert_ids pointers may be NULL.
- * Limits: 1 <= E <= 1024, block_m in {16, 32, 64, 128}, numel <= 2^24,
+ * Limits: 1 <= E <= 1024, block_m in {16, 32, 64, 128, 256}, numel <= 2^24,
  * capacity >= moe_align_capacity(numel, E, block_m) (else MOE_ERR_CAPACITY). */
 int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
                          int32_t* sorted_token_ids, int32_t* expert_ids,
@@ -131,12 +131,12 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
  *     with the same block_m; capacity = length of sorted_token_ids.
  * Rows of C whose slot is not listed are not written.  num_slots = 0 returns MOE_OK at once
  * (no pointer is checked or touched).
- * Limits: K % 256 == 0, N % 128 == 0, block_m in
- * {16, 32, 64, 128}, num_a_rows * a_row_div >= num_slots.  uint4 at block_m 16 and 32: a
+ * Limits: K % 256 == 0, N % 128 == 0, block_m in {16, 32, 64, 128, 256} (256: N % 256 == 0,
+ * else MOE_ERR_UNSUPPORTED), num_a_rows * a_row_div >= num_slots.  uint4 at block_m 16 and 32: a
  * workgroup stages the scales and zero points of its whole K range in LDS beside its activation
  * tiles (160 KiB in all), which allows K up to 36,096 at block_m 16 and 35,840 at block_m 32;
- * longer K returns MOE_ERR_UNSUPPORTED before any launch (block_m 64 and 128 hold two k-blocks of
- * them at a time and have no such limit). */
+ * longer K returns MOE_ERR_UNSUPPORTED before any launch (block_m 64, 128 and 256 hold two
+ * k-blocks of them at a time and have no such limit). */
 int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, const void* scales,
                    const void* zeros, const moe_quant_t* quant, int E, int N, int K, int dtype,
                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
@@ -289,12 +289,13 @@ int moe_repack_uint4(int format, const int32_t* qweight, const int32_t* qzeros, 
                      void* stream);
 
 /* The block_m fused_moe_wna16 uses when called with block_m = 0, for weights of `bits` (4 or 8)
- * bits and activations of `dtype`: the smallest of {16, 32, 64, 128} that holds 1.5x the average
- * number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots share one
- * block and its weights are streamed once; fp16 uint4 stops at 64, and takes 32 where up to 128
- * rows would be needed (its 64-row kernel stages activations through registers, which measured
- * slower than two 32-row blocks).  128-row blocks run on the 32x32 matrix cores.  Returns -1 for
- * non-positive sizes, other bit widths or other dtypes. */
+ * bits and activations of `dtype`: the smallest of {16, 32, 64, 128, 256} that holds 1.5x the
+ * average number of slots per active expert (min(E, M*topk) experts), so a typical expert's slots
+ * share one block and its weights are streamed and decoded once; bf16 uint4 keeps 64 up to 128
+ * needed rows; fp16 uint4 stops at 64, and takes 32 where up to 128 rows would be needed (its
+ * 64-row kernel stages activations through registers, which measured slower than two 32-row
+ * blocks).  128- and 256-row blocks run on the 32x32 matrix cores.  fused_moe_w8a8 caps the choice
+ * at 128.  Returns -1 for non-positive sizes, other bit widths or other dtypes. */
 int moe_pick_block_m(int M, int E, int topk, int bits, int dtype);
 
 /* Workspace bytes fused_moe_wna16 needs for these sizes (block_m 0 = library's choice). */
@@ -310,7 +311,7 @@ size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, cons
  *   workspace     device buffer of at least fused_moe_wna16_workspace_size(...) bytes
  *   out           device dtype [M, H]
  *   topk_weights_out / topk_ids_out: optional device [M, topk] copies of the routing result
- *   block_m       0 = library's choice, else one of {16, 32, 64, 128}
+ *   block_m       0 = library's choice, else one of {16, 32, 64, 128, 256}
  * Launches: routing and align (one launch for M <= 4), GEMM1 (+SiLU*up; split over K into float32
  * partials and a SiLU*up pass when its workgroups would not fill the chip), GEMM2 (split over K into
  * float32 partials at small M; unsplit with block_m 64, it writes dtype rows times the routing

@@ -72,9 +72,11 @@ def test_pick_block_m(lib):
     assert lib.moe_pick_block_m(16, 8, 2, 4, fp16) == 16       # 4 slots per expert
     assert lib.moe_pick_block_m(64, 8, 2, 4, fp16) == 32       # 16 per expert -> 24 needed
     assert lib.moe_pick_block_m(1024, 256, 8, 4, bf16) == 64   # 32 per expert -> 48 needed
-    assert lib.moe_pick_block_m(4096, 256, 8, 4, bf16) == 128  # 128 per expert -> 192 needed
+    assert lib.moe_pick_block_m(4096, 256, 8, 4, bf16) == 256  # 128 per expert -> 192 needed
     assert lib.moe_pick_block_m(4096, 256, 8, 4, fp16) == 64   # fp16 uint4 stops at 64
-    assert lib.moe_pick_block_m(4096, 256, 8, 8, bf16) == 128
+    assert lib.moe_pick_block_m(4096, 256, 8, 8, bf16) == 256
+    assert lib.moe_pick_block_m(2048, 256, 8, 8, bf16) == 128  # 64 per expert -> 96 needed
+    assert lib.moe_pick_block_m(2048, 256, 8, 4, bf16) == 64
     assert lib.moe_pick_block_m(1024, 256, 8, 8, bf16) == 64
     # fp16 uint4: 32 rows where up to 128 would be needed (Qwen2 shape at M = 512: 64 per expert)
     assert lib.moe_pick_block_m(512, 64, 8, 4, fp16) == 32
@@ -97,6 +99,8 @@ def test_align_capacity_formula(lib):
 def test_align_validation(lib):
     f = lib.moe_align_block_size
     assert f(FAKE, 8, 4, 48, FAKE, FAKE, FAKE, 100, NULL) == UNSUPPORTED   # block_m 48
+    assert f(FAKE, 8, 4, 512, FAKE, FAKE, FAKE, 10000, NULL) == UNSUPPORTED  # block_m 512
+    assert f(FAKE, 8, 4, 256, FAKE, FAKE, FAKE, 8 + 4 * 255 - 1, NULL) == CAPACITY  # 256 accepted
     assert f(FAKE, 8, 0, 16, FAKE, FAKE, FAKE, 100, NULL) == INVALID
     assert f(FAKE, 8, 2048, 16, FAKE, FAKE, FAKE, 100, NULL) == UNSUPPORTED
     assert f(FAKE, 8, 4, 4 * 4, NULL, FAKE, FAKE, 100, NULL) == INVALID    # sorted NULL
@@ -135,6 +139,11 @@ def test_gemm_validation(lib):
     assert _gemm(lib, K=300) == UNSUPPORTED
     assert _gemm(lib, N=1000) == UNSUPPORTED
     assert _gemm(lib, bm=24) == UNSUPPORTED
+    assert _gemm(lib, bm=512) == UNSUPPORTED
+    # 256-row blocks run the prefill kernel only: whole 256-column workgroups of N
+    assert _gemm(lib, bm=256, N=1152) == UNSUPPORTED
+    assert b"256" in lib.moe_last_error()
+    assert _gemm(lib, bm=256, slots=0) == OK
     assert _gemm(lib, act=2) == INVALID
     assert _gemm(lib, rows=15) == INVALID                      # 15 rows * 2 < 32 slots
     assert _gemm(lib, A=ctypes.c_void_p(0x100008)) == INVALID  # A not 16-byte aligned
@@ -155,6 +164,7 @@ def test_fused_validation_and_workspace(lib):
     ws = lib.fused_moe_wna16_workspace_size(16, 256, 512, 8, 2, q4, 0, 16)
     assert ws > 16 * 2 * 512 * 2                              # at least the intermediate rows
     assert lib.fused_moe_wna16_workspace_size(16, 256, 512, 8, 2, q4, 0, 24) == 0
+    assert lib.fused_moe_wna16_workspace_size(16, 256, 512, 8, 2, q4, 0, 256) > ws
     assert (lib.fused_moe_wna16_workspace_size(64, 4096, 14336, 8, 2, q4, 0, 0)
             > lib.fused_moe_wna16_workspace_size(1, 4096, 14336, 8, 2, q4, 0, 0))
 
@@ -264,6 +274,7 @@ def test_w8a8_validation(lib):
                                  a["bm"], a["slots"], a["tw"], a["act"], a["C"], NULL)
 
     assert w8(bm=24) == UNSUPPORTED
+    assert w8(bm=256) == UNSUPPORTED                            # int8 activations: up to 128 rows
     assert w8(slots=0, rows=0, A=NULL, sa=NULL, C=NULL, st=NULL, ex=NULL, npost=NULL) == OK
     assert w8(K=320) == UNSUPPORTED
     assert w8(N=1000) == UNSUPPORTED

@@ -177,7 +177,7 @@ def test_fused_tiny_layer(seed):
     assert rel < 5e-3
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 def test_fused_tiny_block_sizes(bm):
     fused_vs_oracle(W["tiny"], 16, seed=0, block_m=bm)
 
@@ -212,6 +212,32 @@ SMALL = {
 def test_fused_small_variants(name):
     wl = SMALL[name]
     fused_vs_oracle(wl, wl.Ms[0], seed=4)
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16_int4", "prefill_bf16_int8", "prefill_odd_rows_bf16",
+                                  "prefill_odd_rows_fp16", "tiny_int8_fp16"])
+def test_fused_block_m_256(name):
+    """256-row blocks (eight 32-row tiles, one column tile per wavefront; with SiLU the mixed
+    gate/up tile): blocks holding 1 to 8 listed row tiles, odd zero-point rows, fp16 and bf16."""
+    wl = SMALL[name]
+    fused_vs_oracle(wl, wl.Ms[0], seed=4, block_m=256)
+
+
+@pytest.mark.parametrize("dtype,bits", [("bf16", 4), ("bf16", 8), ("fp16", 4)])
+def test_fused_block_m_256_hot_expert(dtype, bits):
+    """One expert takes every token's first choice: 600 slots in blocks of 256 (two full blocks
+    of eight row tiles and a tail of three), the other experts partly filled blocks."""
+    wl = synth.Workload("hot256", E=8, H=1024, I=512, topk=2, Ms=(600,), dtype=dtype, bits=bits)
+    layer = synth.make_layer(wl, seed=7)
+    x = synth.make_x(wl, 600, seed=7)
+    lg = synth.make_logits(wl, 600, seed=7)
+    lg[:, 5] += 50.0
+    out, tw, ti = run_fused(wl, x.cuda(), lg.cuda(), cuda_layer(layer), block_m=256)
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    assert_align_exact(ids_ref, wl.E, 256)
+    ref = O.moe_layer(x, ids_ref, w_ref, O.ExpertSource(layer, bits))
+    assert_layer_close(out, ref, f"hot expert, block_m 256, {dtype} int{bits}")
 
 
 def test_fused_one_hot_expert_load():

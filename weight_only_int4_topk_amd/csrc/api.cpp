@@ -40,6 +40,8 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+// uint4 / int8 weight-only GEMMs and layers also take 256-row blocks (the 32x32 prefill kernel)
+bool valid_block_m_wna16(int bm) { return valid_block_m(bm) || bm == 256; }
 
 int check_dtype(int dtype) {
   if (dtype != MOE_DTYPE_FP16 && dtype != MOE_DTYPE_BF16)
@@ -110,27 +112,26 @@ struct Plan {
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_inter, off_part, total;
 };
 
-// fp16 uint4 stops at 64: its 128-row blocks run the 32x32 prefill kernel with spilled registers
-// (and the 16-row kernel at 128 rows stages activations through registers at two wavefronts per
-// SIMD: Qwen2-shaped layer at M = 512, GEMMs 798 us at 128 rows, 497 us at 64).  bf16 uint4 and
-// int8 take 128 rows where that many are needed (the 32x32 prefill kernel: DeepSeek-V3 prefill
-// layer at 4096 tokens, uint4 4.50 against 4.78 ms at 64 rows).  fp16 uint4 where 64 rows would
-// be picked for up to 128 needed: 32 rows (the fp16 64-row kernel also stages activations through
-// registers; Qwen2 shape at M = 512, ~72 slots per expert: 555 -> 529 us per layer; bf16 and int8
-// measured equal or slower at 32).
+// fp16 uint4 stops at 64 (the 16-row kernel at 128 rows stages activations through registers at
+// two wavefronts per SIMD: Qwen2-shaped layer at M = 512, GEMMs 798 us at 128 rows, 497 us at 64).
+// fp16 uint4 where 64 rows would be picked for up to 128 needed: 32 rows (the fp16 64-row kernel
+// also stages activations through registers; Qwen2 shape at M = 512, ~72 slots per expert: 555 ->
+// 529 us per layer; bf16 and int8 measured equal or slower at 32).  bf16 uint4 and int8 beyond 128
+// needed rows: 256-row blocks, which hold a whole expert's slots at the DeepSeek-V3 prefill shape
+// (101 to 159 slots per expert at 4096 tokens), so each weight is decoded once for all of them
+// (first GEMM, uint4: 2.90 ms at 128 rows, where about half the experts spill a short second block
+// that decodes every weight again, 2.63 ms at 256; int8 weights 2.91 -> 2.83 ms); int8 takes 128
+// rows from 64 needed, bf16 uint4 keeps 64 rows up to 128 needed (measured against 128).
 int pick_block_m(int M, int topk, int E, int bits, int dtype) {
   const int64_t slots = (int64_t)M * topk;
   const int64_t active = std::max<int64_t>(1, std::min<int64_t>(E, slots));
   const int64_t avg = (slots + active - 1) / active;
   const int64_t need = avg + avg / 2;
-  const int top = (bits == 4 && dtype == MOE_DTYPE_FP16) ? 64 : 128;
   for (int bm : {16, 32})
     if (need <= bm) return bm;
-  if (bits == 4 && dtype == MOE_DTYPE_FP16 && need <= 128) return 32;
-  // bf16 uint4: 128 rows only where more than 128 are needed (the 64-row kernel measured, and is
-  // kept, below that)
-  if (bits == 4 && need <= 128) return 64;
-  return need <= 64 ? 64 : top;
+  if (bits == 4 && dtype == MOE_DTYPE_FP16) return need <= 128 ? 32 : 64;
+  if (need <= 64 || (bits == 4 && need <= 128)) return 64;
+  return need <= 128 ? 128 : 256;
 }
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -325,8 +326,8 @@ int moe_align_block_size(const int32_t* topk_ids, int numel, int E, int block_m,
                          int32_t* num_tokens_post_padded, int64_t capacity, void* stream) {
   if (numel < 0 || E <= 0) return fail(MOE_ERR_INVALID_ARG, "numel = %d, E = %d", numel, E);
   if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E = %d > 1024", E);
-  if (!valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
+  if (!valid_block_m_wna16(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128, 256)", block_m);
   if (numel > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "numel = %d > 2^24", numel);
   // an empty batch still gets its padded total (0) written; its id buffers may then be empty
   if ((numel > 0 && !topk_ids) || (capacity > 0 && (!sorted_token_ids || !expert_ids)) ||
@@ -374,10 +375,12 @@ int moe_wna16_gemm(const void* A, int num_a_rows, int a_row_div, const void* B, 
                 num_a_rows, a_row_div, num_slots);
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL)
     return fail(MOE_ERR_INVALID_ARG, "act = %d", act);
-  if (!valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
+  if (!valid_block_m_wna16(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128, 256)", block_m);
   if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
   if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
+  if (block_m == 256 && N % 256)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m 256 needs N = %d to be a multiple of 256", N);
   if ((int64_t)num_a_rows * K * 2 >= ((int64_t)1 << 31) ||
       (int64_t)N * (quant->bits == 4 ? K / 2 : K) >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "A or one expert's weights exceed 2 GiB");
@@ -617,7 +620,8 @@ struct PlanW8 {
 PlanW8 make_plan_w8(int M, int H, int I, int E, int topk, int dtype, int block_m) {
   PlanW8 p{};
   const int64_t slots = (int64_t)M * topk;
-  p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E, 8, dtype);
+  // the int8-activation GEMM takes at most 128-row blocks
+  p.bm = block_m > 0 ? block_m : std::min(128, pick_block_m(M, topk, E, 8, dtype));
   p.cap = align_capacity(slots, E, p.bm);
   const int64_t nblk = (p.cap + p.bm - 1) / p.bm;
   size_t off = 0;
@@ -774,7 +778,7 @@ int moe_repack_uint4(int format, const int32_t* qweight, const int32_t* qzeros, 
 size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk,
                                       const moe_quant_t* quant, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0 || !quant) return 0;
-  if (block_m != 0 && !valid_block_m(block_m)) return 0;
+  if (block_m != 0 && !valid_block_m_wna16(block_m)) return 0;
   return make_plan(M, H, I, E, topk, quant->bits, dtype, block_m).total;
 }
 
@@ -800,8 +804,8 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   if (int rc = check_quant(quant)) return rc;
   if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d H=%d I=%d", M, H, I);
   if (int rc = check_routing(routing, E, topk)) return rc;
-  if (block_m != 0 && !valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128)", block_m);
+  if (block_m != 0 && !valid_block_m_wna16(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128, 256)", block_m);
   if (H % 256 || I % 256)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");

@@ -884,6 +884,7 @@ int gemm_wg_cols(const GemmConfig& c) {
 
 hipError_t launch_gemm(const GemmParams& p_in, const GemmConfig& c, hipStream_t stream) {
   if (prefill_fits(c, p_in.N)) return launch_prefill(p_in, c, stream);
+  if (c.block_m > 128) return hipErrorInvalidValue;  // 256-row blocks: the prefill kernel only
   GemmParams p = p_in;
   const int kb_total = p.K / (c.bits == 4 ? 128 : 64);
   if (p.split_k < 1 || p.split_k > kb_total || (p.split_k > 1 && !c.out_f32))

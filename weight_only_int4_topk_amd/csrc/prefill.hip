@@ -122,9 +122,13 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
   constexpr int VPR = KB / 8;                     // 16-byte chunks of an activation row per k-block
   constexpr int AV = BM * VPR / THREADS;          // direct-to-LDS loads per thread per k-block
   static_assert(AV >= 1 && BM * VPR % THREADS == 0, "whole activation chunks per thread");
-  static_assert(!ACT || NT % 2 == 0, "SiLU epilogue: gate and up tiles in pairs");
-  constexpr int NOUT = ACT ? NT / 2 : NT;
-  constexpr int WG_COLS = WAVES * NOUT * 32;      // output columns of a workgroup
+  // SiLU epilogue: gate and up tiles in pairs, or (one tile per wavefront) a mixed tile whose
+  // lanes 0-15 hold 16 gate rows and lanes 16-31 the matching up rows
+  static_assert(!ACT || NT % 2 == 0 || NT == 1, "SiLU epilogue: paired or mixed tiles");
+  constexpr bool MIXED = ACT && NT == 1;
+  constexpr int NOUT = ACT ? (MIXED ? 1 : NT / 2) : NT;
+  constexpr int TCOLS = MIXED ? 16 : 32;          // output columns of a column tile
+  constexpr int WG_COLS = WAVES * NOUT * TCOLS;   // output columns of a workgroup
   static_assert(NBUF == 2 || NBUF == 3, "two or three activation buffers");
   // k-blocks per unrolled iteration: every buffer and weight slot index a compile-time constant
   constexpr int U = NBUF == 3 ? 6 : 2;
@@ -190,17 +194,25 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
 
   const int c32 = lane & 31;
   const int h = lane >> 5;
+  // col[t]: first output column of tile t (of the gate half with the SiLU epilogue); wrow[t]: the
+  // weight row lane l streams for tile t
   auto col_of = [&](int t) -> int {
-    if constexpr (ACT) {
+    if constexpr (MIXED) {
+      return nc * WG_COLS + wave * 16;
+    } else if constexpr (ACT) {
       const int g0 = nc * WG_COLS + wave * NOUT * 32;
       return t < NOUT ? g0 + t * 32 : N / 2 + g0 + (t - NOUT) * 32;
     } else {
       return nc * WG_COLS + (wave * NT + t) * 32;
     }
   };
-  int col[NT];
+  int col[NT], wrow[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) col[t] = col_of(t);
+  for (int t = 0; t < NT; ++t) {
+    col[t] = col_of(t);
+    if constexpr (MIXED) wrow[t] = c32 < 16 ? col[t] + c32 : N / 2 + col[t] + (c32 - 16);
+    else wrow[t] = col[t] + c32;
+  }
 
   const uint32_t row_bytes = BITS == 4 ? (uint32_t)K / 2 : (uint32_t)K;
   const uint32_t srow_bytes = BITS == 4 ? (uint32_t)(K / 128) * 2 : 2u;
@@ -218,7 +230,7 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
   uint32_t vw[NT], vs[NT], vz[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const uint32_t n = (uint32_t)(col[t] + c32);
+    const uint32_t n = (uint32_t)wrow[t];
     vw[t] = n * row_bytes + h * 32;
     vs[t] = n * srow_bytes;
     vz[t] = n * zrow_bytes;
@@ -277,7 +289,7 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       sf8[t] = bits_to_float<DT>(
-          (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)(col[t] + c32) * 2, 0, 0));
+          (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs_s, (uint32_t)wrow[t] * 2, 0, 0));
       cf8[t] = -128.0f * sf8[t];  // exact: 8-bit times the scale's significand
     }
   }
@@ -376,18 +388,54 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
       }
     }
   };
-  static_assert(MT == 2 || MT == 4, "block_m 64 or 128");
+  static_assert(MT == 2 || MT == 4 || MT == 8, "block_m 64, 128 or 256");
   if constexpr (MT == 2) {
     if (mt_valid >= 2) kloop(std::integral_constant<int, 2>{});
     else kloop(std::integral_constant<int, 1>{});
-  } else {
+  } else if constexpr (MT == 4) {
     if (mt_valid >= 4) kloop(std::integral_constant<int, 4>{});
     else if (mt_valid == 3) kloop(std::integral_constant<int, 3>{});
     else if (mt_valid == 2) kloop(std::integral_constant<int, 2>{});
     else kloop(std::integral_constant<int, 1>{});
+  } else {
+    switch (mt_valid) {
+      case 8: kloop(std::integral_constant<int, 8>{}); break;
+      case 7: kloop(std::integral_constant<int, 7>{}); break;
+      case 6: kloop(std::integral_constant<int, 6>{}); break;
+      case 5: kloop(std::integral_constant<int, 5>{}); break;
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      default: kloop(std::integral_constant<int, 1>{}); break;
+    }
   }
   // direct loads still in flight must land before the workgroup's LDS is handed on
   wait_vmcnt_p<0>();
+
+  if constexpr (MIXED) {
+    // lane c (c < 16) of each 32-lane half holds gate column col + c, lane c + 16 the up column:
+    // every lane fetches its partner's value, lanes c < 16 write
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= mt_valid) continue;
+      float up[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) up[i] = __shfl_xor(acc[m][0][i], 16, kWave);
+      if (c32 < 16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = m * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+          const int slot = s_slot[r];
+          if (slot < 0) continue;
+          const float wscale = p.topk_w ? p.topk_w[slot] : 1.0f;
+          const float g = acc[m][0][i];
+          const float v = g / (1.0f + __expf(-g)) * up[i] * wscale;
+          ((uint16_t*)p.C)[(size_t)slot * (N / 2) + col[0] + c32] = float_to_bits<DT>(v);
+        }
+      }
+    }
+    return;
+  }
 
   // epilogue: register i of lane l holds row 8 (i / 4) + 4 h + i % 4 of each 32-row tile, column
   // l % 32 of each column tile
@@ -403,7 +451,7 @@ __global__ void __launch_bounds__(WAVES * 64, 2) prefill_gemm_kernel(GemmParams 
 #pragma unroll
       for (int t = 0; t < NOUT; ++t) {
         const int cc = col[t] + c32;
-        if constexpr (ACT) {
+        if constexpr (ACT && !MIXED) {
           const float g = acc[m][t][i];
           const float up = acc[m][t + NOUT][i];
           const float v = g / (1.0f + __expf(-g)) * up * wscale;
@@ -676,11 +724,8 @@ hipError_t launch_nt(const GemmParams& p, const GemmConfig& c, hipStream_t strea
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 block(WAVES * kWave);
   if (c.act) {
-    if constexpr (NT % 2 == 0)
-      hipLaunchKernelGGL((prefill_gemm_kernel<DT, BITS, MT, NT, WAVES, NBUF, 1, 0>),
-                         dim3((unsigned)grid), block, 0, stream, p);
-    else
-      return hipErrorInvalidValue;  // the SiLU epilogue pairs gate and up tiles
+    hipLaunchKernelGGL((prefill_gemm_kernel<DT, BITS, MT, NT, WAVES, NBUF, 1, 0>),
+                       dim3((unsigned)grid), block, 0, stream, p);
   } else if (c.out_f32) {
     hipLaunchKernelGGL((prefill_gemm_kernel<DT, BITS, MT, NT, WAVES, NBUF, 0, 1>),
                        dim3((unsigned)grid), block, 0, stream, p);
@@ -693,36 +738,45 @@ hipError_t launch_nt(const GemmParams& p, const GemmConfig& c, hipStream_t strea
 
 template <int DT, int BITS, int MT>
 hipError_t launch_mt_p(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
-  if (prefill_nt(c, p.N) == 2)
-    return launch_nt<DT, BITS, MT, 2, kPrefillWaves, kPrefillBufs>(p, c, stream);
-  return launch_nt<DT, BITS, MT, 1, kPrefillWaves, kPrefillBufs>(p, c, stream);
+  if constexpr (MT == 8) {
+    return launch_nt<DT, BITS, MT, 1, kPrefillWaves, kPrefillBufs>(p, c, stream);
+  } else {
+    if (prefill_nt(c, p.N) == 2)
+      return launch_nt<DT, BITS, MT, 2, kPrefillWaves, kPrefillBufs>(p, c, stream);
+    return launch_nt<DT, BITS, MT, 1, kPrefillWaves, kPrefillBufs>(p, c, stream);
+  }
 }
 
 template <int DT, int BITS>
 hipError_t launch_bits_p(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
+  if (c.block_m == 256) return launch_mt_p<DT, BITS, 8>(p, c, stream);
   return launch_mt_p<DT, BITS, 4>(p, c, stream);
 }
 
 }  // namespace
 
-// Column tiles of 32 per wavefront: 2 (gate and up with the SiLU epilogue, or 64 weight rows),
-// or 1 where N holds no whole number of workgroups of 2
+// Column tiles of 32 per wavefront.  block_m 128: 2 (gate and up with the SiLU epilogue, or 64
+// weight rows), or 1 where N holds no whole number of workgroups of 2.  block_m 256: 1 (eight
+// 32-row accumulator tiles per column tile take the registers two tiles would need; with the SiLU
+// epilogue the tile is mixed: 16 gate rows and the 16 matching up rows).
 int prefill_nt(const GemmConfig& c, int N) {
+  if (c.block_m == 256) return 1;
   if (c.act) return 2;
   return N % (kPrefillWaves * 64) == 0 ? 2 : 1;
 }
 
 int prefill_wg_cols(const GemmConfig& c, int N) {
-  return c.act ? kPrefillWaves * 32 : kPrefillWaves * 32 * prefill_nt(c, N);
+  if (c.act) return kPrefillWaves * (c.block_m == 256 ? 16 : 32);
+  return kPrefillWaves * 32 * prefill_nt(c, N);
 }
 
-// block_m 128 only: at 64 rows (about 32 slots per expert in the DeepSeek-V3 layer at 1024 tokens,
-// often a single 32-row tile) the exact decode is repeated for too few rows and the 16-row kernel
-// with biased codes is faster (measured: first GEMM 1.57 against 1.40 ms)
+// block_m 128 and 256 only: at 64 rows (about 32 slots per expert in the DeepSeek-V3 layer at 1024
+// tokens, often a single 32-row tile) the exact decode is repeated for too few rows and the 16-row
+// kernel with biased codes is faster (measured: first GEMM 1.57 against 1.40 ms)
 bool prefill_fits(const GemmConfig& c, int N) {
-  if (c.block_m != 128) return false;
-  if (c.act) return (N / 2) % (kPrefillWaves * 32) == 0;
-  return N % (kPrefillWaves * 32) == 0;
+  if (c.block_m != 128 && c.block_m != 256) return false;
+  if (c.act) return (N / 2) % prefill_wg_cols(c, N) == 0;
+  return N % prefill_wg_cols(c, N) == 0;
 }
 
 size_t prefill_lds_bytes(const GemmConfig& c) {
