@@ -205,6 +205,10 @@ SMALL = {
     "prefill_odd_rows_bf16": synth.Workload("pob", E=16, H=1792, I=1280, topk=4, Ms=(300,),
                                             dtype="bf16"),
     "prefill_odd_rows_fp16": synth.Workload("pof", E=16, H=1792, I=1280, topk=4, Ms=(300,)),
+    # K = I = 256 with enough second-GEMM workgroups: each streams two column chunks in turn
+    # against one staged activation tile (16 chunks, ~126 blocks)
+    "column_groups": synth.Workload("cg", E=128, H=4096, I=256, topk=8, Ms=(64,), score="sigmoid",
+                                    num_groups=8, topk_groups=4, scale=2.5),
 }
 
 

@@ -255,6 +255,21 @@ Plan make_plan(int M, int H, int I, int E, int topk, int bits, int dtype, int bl
   return p;
 }
 
+// Column chunks per second-GEMM workgroup.  With K = I = 256 (a tensor-parallel share of many
+// small experts) a 16-row workgroup streams two k-blocks per column chunk, and its start-up (slot
+// ids, activation rows, metadata, the first weight latency) costs as much as the stream; streaming
+// several chunks against one staged activation tile pays it once.  Four chunks where that still
+// leaves >= 512 workgroups, else two, else one (measured on the DeepSeek-V3 TP share, layer per
+// call: M = 16 103 -> 95 us, M = 64 189 -> 175 us, M = 256 249 -> 233 us at four; two at M = 1,
+// 224 -> 112 workgroups, 29.8 -> 31.7 us, so none there; seven or fourteen slower).
+int pick_cgroup(const moe::GemmConfig& c, int N, int K, int split, int64_t blocks) {
+  if (!moe::gemm_cgroup_fits(c, K, split)) return 1;
+  const int n_chunks = N / moe::gemm_wg_cols(c);
+  for (int g : {4, 2})
+    if (n_chunks % g == 0 && blocks * (n_chunks / g) >= 512) return g;
+  return 1;
+}
+
 // ------------------------------------------------------------------------------------------------
 // dense GEMM (one expert, every row a slot)
 // ------------------------------------------------------------------------------------------------
@@ -842,6 +857,7 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   // half-line writes cost more than the bytes saved (4096 tokens: +1 to +3 %).
   const bool rows2 = pl.split2 == 1 && pl.bm == 64;
   moe::GemmConfig c2{dtype, quant->bits, pl.bm, 0, rows2 ? 0 : 1, pl.ntw2, pl.wv2};
+  c2.cgroup = pick_cgroup(c2, H, I, pl.split2, estimate_active_blocks(M, topk, E, pl.bm));
   if (int rc = fit_lds(H, pl.split1, c1, "gemm1")) return rc;
   if (int rc = fit_lds(I, pl.split2, c2, "gemm2")) return rc;
 

@@ -260,7 +260,7 @@ struct Shape {
   static constexpr int U = MT >= 4 ? U0 / gcd_c(U0, 2 * KBC) * (2 * KBC) : U0;
 };
 
-template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32, int WAVES>
+template <int DT, int BITS, int MT, int NTW, int ACT, int OUTF32, int WAVES, int MULTI = 0>
 __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p) {
   constexpr int THREADS = WAVES * kWave;
   using S = Shape<BITS, MT, NTW, THREADS>;
@@ -289,6 +289,12 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   // decode regime: biased codes with MFMA-side bias removal (fewer VALU ops per weight); prefill:
   // exact decoded weights, no extra MFMAs (the matrix cores are the bottleneck there)
   constexpr bool BIASED = MT <= 2;
+  // MULTI: the workgroup streams p.cgroup column chunks in turn against one activation tile (the
+  // whole K range of a short K, staged once), writing each chunk's float32 partials as it ends:
+  // the start-up of a workgroup (slot ids, activation rows, metadata, the first weight latency) is
+  // paid once per cgroup chunks instead of once per chunk
+  static_assert(!MULTI || (BIASED && BITS == 4 && MT == 1 && !ACT && OUTF32),
+                "column groups: uint4, 16-row blocks, float32 partials");
   // the activation k order in LDS follows the weight decode: permuted for the shift-and-mask
   // decodes (fp16, and bf16 biased codes), natural for the bf16 exact decode and for int8
   constexpr bool PERM_A = BITS == 4 && (DT == 0 || BIASED);
@@ -332,12 +338,14 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   const int n_out = ACT ? N / 2 : N;
   const int n_chunks = n_out / WG_COLS;
   const int split = p.split_k;
+  const int G = MULTI ? p.cgroup : 1;  // column chunks of this workgroup
+  const int n_groups = n_chunks / G;
 
   int bid = blockIdx.x;
   const int z = bid % split;
   bid /= split;
-  const int nc = bid % n_chunks;
-  const int blk = bid / n_chunks;
+  const int nc = (bid % n_groups) * G;  // first column chunk
+  const int blk = bid / n_groups;
   // Row maps.  Aligned: slots listed by sorted_ids, expert per block from expert_ids.  Dense: rows
   // are slots 0..num_slots-1 in order, one expert.  Batched: block blk covers rows j*BM.. of expert
   // blk / bpe (j = blk % bpe), slot = row index e * max_tokens + j*BM + r, valid below the expert's
@@ -374,6 +382,8 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   const int kb_beg = z * kb_per;
   const int kb_end = min(kb_total, kb_beg + kb_per);
   const int kb_last = min(max(kb_beg, kb_end - 1), kb_total - 1);  // always a real k-block
+  // staged metadata row pitch (dwords): R + 2, or G * R + 2 for column groups
+  const int RPM = MULTI ? G * R + 2 : RP;
 
   // rows of the workgroup: local row lr = (wave * NTW + t) * 16 + r
   auto col_of = [&](int w, int t) -> int {
@@ -528,7 +538,7 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
     if constexpr (BITS == 4) {
       const int mrow = RING ? (idx & 1) : min(kb_beg + idx, kb_last) - kb_beg;
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) mf[t] = s_meta[mrow * RP + (wave * NTW + t) * 16 + rsub];
+      for (int t = 0; t < NTW; ++t) mf[t] = s_meta[mrow * RPM + (wave * NTW + t) * 16 + rsub];
     }
   };
   // RING: thread tid serves workgroup row tid % R for one k-block, in register set X % 2 for
@@ -577,18 +587,22 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
     ring_store(0, 0);
     ring_load(0, 2);
   } else if constexpr (BITS == 4) {
+    // MULTI: rows of chunk g at g * R + lr, row pitch G * R + 2
     const int kb0 = kb_beg & ~1;
     const int npair = (kb_end - kb0 + 1) >> 1;
-    for (int item = tid; item < R * npair; item += THREADS) {
-      const int lr = item / npair;
-      const int j = item - lr * npair;
-      const uint32_t n = (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + (lr % 16));
+    for (int item = tid; item < G * R * npair; item += THREADS) {
+      const int gl = item / npair;
+      const int j = item - gl * npair;
+      const int g = MULTI ? gl / R : 0;
+      const int lr = gl - g * R;
+      const uint32_t n =
+          (uint32_t)(col_of(lr / (NTW * 16), (lr / 16) % NTW) + g * WG_COLS + (lr % 16));
       const int kb = kb0 + 2 * j;
       const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs_s, n * srow_bytes + kb * 2, 0, 0);
       const uint32_t zb = __builtin_amdgcn_raw_buffer_load_b8(rs_z, n * zrow_bytes + (kb >> 1), 0, 0);
-      if (kb >= kb_beg) s_meta[(kb - kb_beg) * RP + lr] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
+      if (kb >= kb_beg) s_meta[(kb - kb_beg) * RPM + gl] = (sc & 0xFFFFu) | ((zb & 0xFu) << 16);
       if (kb + 1 < kb_end)
-        s_meta[(kb + 1 - kb_beg) * RP + lr] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
+        s_meta[(kb + 1 - kb_beg) * RPM + gl] = (sc >> 16) | (((zb >> 4) & 0xFu) << 16);
     }
   }
 
@@ -597,11 +611,130 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   barrier_lds();  // publishes the staged scales and chunk 0
   if constexpr (DIRECT) {
     dma_a(1, 1);
-  } else {
+  } else if constexpr (!MULTI) {
 #pragma unroll
     for (int q = 1; q <= AQ; ++q) load_a(q % AQ, q);
   }
   load_meta(0);
+
+  // biased uint4 codes of one k-block (weights in wq[slot], metadata meta[t] = scale | zero << 16,
+  // fragments from a_s(step, row tile)): the bias and the zero point are removed either by a
+  // broadcast MFMA (BM 16: the matrix cores have room) or, for fp16 at BM 32, by one exact
+  // half-precision subtraction per two weights ((1024 + q) - (1024 + z) = q - z), which halves the
+  // MFMAs where they would otherwise bound the kernel.  The scale is applied per k-block.
+  auto biased_u4_kb = [&](int slot, const uint32_t* meta, auto&& a_s) {
+    constexpr bool SUBZ = DT == 0 && MT == 2;
+    floatx4_t accg[MT][NTW];
+    u32x4_t bz[NTW];
+    float sf[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const uint32_t z = meta[t] >> 16;
+      const uint32_t zz = (kZeroBase | z) * 0x10001u;
+      const uint32_t zh = DT == 0 ? (kZeroBase | (z << 4)) * 0x10001u : zz;
+      bz[t] = u32x4_t{zz, zh, zz, zh};
+      sf[t] = bits_to_float<DT>((uint16_t)(meta[t] & 0xFFFFu));
+    }
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      u32x4_t b[NTW];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        b[t] = bias_u4<DT>(wq[slot][t][st], kMask, kMaskHi, kMagic);
+        if constexpr (SUBZ) {
+          // element copies first: a bit_cast of a vector element reads element 0
+          const uint32_t b0 = b[t][0], b1 = b[t][1], b2 = b[t][2], b3 = b[t][3];
+          const uint32_t zlo = bz[t][0], zhi = bz[t][1];
+          b[t] = u32x4_t{h2_add(b0, zlo), h2_add(b1, zhi), h2_add(b2, zlo), h2_add(b3, zhi)};
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          accg[m][t] = Mfma<DT>::run(a_s(st, m), b[t], st == 0 ? zero4 : accg[m][t]);
+          if constexpr (!SUBZ) accg[m][t] = Mfma<DT>::run(a_s(st, m), bz[t], accg[m][t]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(sf[t], accg[m][t][i], acc[m][t][i]);
+  };
+
+  // epilogue: lane holds rows 4*(lane/16)+i of each 16-row tile, column lane%16 (plus coff, the
+  // column offset of a column group's chunk)
+  auto store_out = [&](int coff) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = m * 16 + grp * 4 + i;
+        const int slot = s_slot[r];
+        if (slot < 0) continue;
+        const float wscale = p.topk_w ? p.topk_w[slot] : 1.0f;
+#pragma unroll
+        for (int t = 0; t < NOUT; ++t) {
+          const int cc = col[t] + rsub + coff;
+          if constexpr (ACT) {
+            const float g = acc[m][t][i];
+            const float up = acc[m][t + NOUT][i];
+            const float v = g / (1.0f + __expf(-g)) * up * wscale;
+            ((uint16_t*)p.C)[(size_t)slot * (N / 2) + cc] = float_to_bits<DT>(v);
+          } else if constexpr (OUTF32) {
+            ((float*)p.C)[((size_t)z * p.num_slots + slot) * N + cc] = acc[m][t][i] * wscale;
+          } else {
+            ((uint16_t*)p.C)[(size_t)slot * N + cc] = float_to_bits<DT>(acc[m][t][i] * wscale);
+          }
+        }
+      }
+    }
+  };
+
+  if constexpr (MULTI) {
+    // Column groups: the whole K range of this split is activation chunk 0 (buffer 0, staged by
+    // the prologue); k-block sequence idx = g * kb_n + kbi runs over the G chunks, the weight
+    // prefetch running on across chunk edges (chunk g's rows sit g * WG_COLS rows further, a
+    // uniform offset); at the end of each chunk its partials are written and the sums cleared.
+    const int kb_n = kb_end - kb_beg;  // even (K % 256 == 0, unsplit) and at most one chunk
+    const int total = G * kb_n;
+    const uint32_t gstep = (uint32_t)WG_COLS * row_bytes;
+    for (int it = 0; it < total; it += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int idx = it + j;
+        const int g = idx / kb_n;
+        const int kbi = idx - g * kb_n;
+        const uint16_t* abase = frag_base(kbi, 0);
+        auto a_s = [&](int st, int m) -> u32x4_t {
+          return *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
+        };
+        uint32_t meta[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          meta[t] = s_meta[kbi * RPM + g * R + (wave * NTW + t) * 16 + rsub];
+        biased_u4_kb(j, meta, a_s);
+        const int nidx = min(idx + PF, total - 1);
+        const int ng = nidx / kb_n;
+        const uint32_t soff = (uint32_t)ng * gstep + (uint32_t)(kb_beg + nidx - ng * kb_n) * 64;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          wq[j][t] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_w, vw[t], soff, 0));
+        if (kbi == kb_n - 1) {
+          store_out(g * WG_COLS);
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) acc[m][t] = zero4;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return;
+  }
 
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
   // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
@@ -630,49 +763,7 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int t = 0; t < NTW; ++t) meta[t] = mf[t];
       if constexpr (BIASED && BITS == 4) {
-        // magic-biased codes; the bias and the zero point are removed either by a broadcast MFMA
-        // (BM 16: the matrix cores have room) or, for fp16 at BM 32, by one exact half-precision
-        // subtraction per two weights ((1024 + q) - (1024 + z) = q - z), which halves the MFMAs
-        // where they would otherwise bound the kernel.  The scale is applied per k-block.
-        constexpr bool SUBZ = DT == 0 && MT == 2;
-        floatx4_t accg[MT][NTW];
-        u32x4_t bz[NTW];
-        float sf[NTW];
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-          const uint32_t z = meta[t] >> 16;
-          const uint32_t zz = (kZeroBase | z) * 0x10001u;
-          const uint32_t zh = DT == 0 ? (kZeroBase | (z << 4)) * 0x10001u : zz;
-          bz[t] = u32x4_t{zz, zh, zz, zh};
-          sf[t] = bits_to_float<DT>((uint16_t)(meta[t] & 0xFFFFu));
-        }
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-          u32x4_t b[NTW];
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            b[t] = bias_u4<DT>(wq[slot][t][st], kMask, kMaskHi, kMagic);
-            if constexpr (SUBZ) {
-              // element copies first: a bit_cast of a vector element reads element 0
-              const uint32_t b0 = b[t][0], b1 = b[t][1], b2 = b[t][2], b3 = b[t][3];
-              const uint32_t zlo = bz[t][0], zhi = bz[t][1];
-              b[t] = u32x4_t{h2_add(b0, zlo), h2_add(b1, zhi), h2_add(b2, zlo), h2_add(b3, zhi)};
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int t = 0; t < NTW; ++t) {
-              accg[m][t] = Mfma<DT>::run(a_s(st, m), b[t], st == 0 ? zero4 : accg[m][t]);
-              if constexpr (!SUBZ) accg[m][t] = Mfma<DT>::run(a_s(st, m), bz[t], accg[m][t]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int t = 0; t < NTW; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][t][i] = __builtin_fmaf(sf[t], accg[m][t][i], acc[m][t][i]);
+        biased_u4_kb(slot, meta, a_s);
       } else if constexpr (BIASED) {
         // int8: biased codes accumulate over all of K; row sums (ones MFMA) remove the bias at the end
 #pragma unroll
@@ -773,42 +864,28 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
     }
   }
 
-  // epilogue: lane holds rows 4*(lane/16)+i of each 16-row tile, column lane%16
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = m * 16 + grp * 4 + i;
-      const int slot = s_slot[r];
-      if (slot < 0) continue;
-      const float wscale = p.topk_w ? p.topk_w[slot] : 1.0f;
-#pragma unroll
-      for (int t = 0; t < NOUT; ++t) {
-        const int cc = col[t] + rsub;
-        if constexpr (ACT) {
-          const float g = acc[m][t][i];
-          const float up = acc[m][t + NOUT][i];
-          const float v = g / (1.0f + __expf(-g)) * up * wscale;
-          ((uint16_t*)p.C)[(size_t)slot * (N / 2) + cc] = float_to_bits<DT>(v);
-        } else if constexpr (OUTF32) {
-          ((float*)p.C)[((size_t)z * p.num_slots + slot) * N + cc] = acc[m][t][i] * wscale;
-        } else {
-          ((uint16_t*)p.C)[(size_t)slot * N + cc] = float_to_bits<DT>(acc[m][t][i] * wscale);
-        }
-      }
-    }
-  }
+  store_out(0);
 }
 
 template <int DT, int BITS, int MT, int NTW, int WV>
 hipError_t launch_ntw(const GemmParams& p, const GemmConfig& c, hipStream_t stream) {
   const int n_out = c.act ? p.N / 2 : p.N;
   const int n_chunks = n_out / gemm_wg_cols(c);
-  const long long grid = (long long)n_chunks * p.num_blocks * p.split_k;
+  if (c.cgroup < 1 || n_chunks % c.cgroup) return hipErrorInvalidValue;
+  const long long grid = (long long)(n_chunks / c.cgroup) * p.num_blocks * p.split_k;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const size_t lds = gemm_meta_lds_bytes(p.K, p.split_k, c);
   if (gemm_lds_bytes(p.K, p.split_k, c) > kGemmLdsLimit) return hipErrorInvalidValue;
+  if (c.cgroup > 1) {
+    if (!gemm_cgroup_fits(c, p.K, p.split_k)) return hipErrorInvalidValue;
+    if constexpr (BITS == 4 && MT == 1) {
+      hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 0, 1, WV, 1>), dim3((unsigned)grid),
+                         dim3(WV * kWave), lds, stream, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   if (c.act)
     hipLaunchKernelGGL((wna16_gemm_kernel<DT, BITS, MT, NTW, 1, 0, WV>), dim3((unsigned)grid),
                        dim3(WV * kWave), lds, stream, p);
@@ -856,7 +933,13 @@ size_t gemm_meta_lds_bytes(int K, int split_k, const GemmConfig& c) {
   if (c.block_m >= 64) return (size_t)(waves * ntw * 16 + 2) * 2 * 4;  // two-slot ring
   const int kb_total = K / 128;
   const int kb_per = (kb_total + split_k - 1) / split_k;
-  return (size_t)(waves * ntw * 16 + 2) * kb_per * 4;  // row pitch R + 2 dwords
+  // row pitch R + 2 dwords (column groups: cgroup * R + 2)
+  return (size_t)((c.cgroup > 1 ? c.cgroup : 1) * waves * ntw * 16 + 2) * kb_per * 4;
+}
+
+bool gemm_cgroup_fits(const GemmConfig& c, int K, int split_k) {
+  using S = Shape<4, 1, 4>;
+  return c.bits == 4 && c.block_m == 16 && !c.act && c.out_f32 && split_k == 1 && K <= S::KC;
 }
 
 template <int BITS, int MT>
@@ -892,6 +975,7 @@ hipError_t launch_gemm(const GemmParams& p_in, const GemmConfig& c, hipStream_t 
   p.dec_mask = 0x000F000Fu;
   p.dec_mask_hi = (c.dtype == 0 && c.bits == 4) ? 0x00F000F0u : 0x000F000Fu;
   p.dec_magic = c.dtype == 0 ? 0x64006400u : 0x43004300u;
+  p.cgroup = c.cgroup;
   if (c.dtype == 0)
     return c.bits == 4 ? launch_bits<0, 4>(p, c, stream) : launch_bits<0, 8>(p, c, stream);
   return c.bits == 4 ? launch_bits<1, 4>(p, c, stream) : launch_bits<1, 8>(p, c, stream);

@@ -56,6 +56,7 @@ struct GemmParams {
   uint32_t dec_mask;          // set by launch_gemm: low nibble-pair mask of the decode
   uint32_t dec_mask_hi;       // set by launch_gemm: high nibble-pair mask (fp16 uint4 decode)
   uint32_t dec_magic;         // set by launch_gemm: magic bias in both 16-bit halves
+  int cgroup;                 // set by launch_gemm: column chunks per workgroup (GemmConfig)
 };
 
 struct GemmConfig {
@@ -66,7 +67,14 @@ struct GemmConfig {
   int out_f32;   // 1: float partials [split, num_slots, N]
   int ntw;       // column tiles of 16 per wavefront: 2, or 4 (block_m 16 only)
   int waves = 4; // wavefronts per workgroup: 4, or 8 (block_m 32 with 2 tiles only; honoured there)
+  // column chunks one workgroup streams in turn, its activation rows staged once (1: one chunk).
+  // > 1 only where gemm_cgroup_fits: a short K whose whole range is one activation chunk.
+  int cgroup = 1;
 };
+
+// Column chunks per workgroup > 1 is possible: uint4, block_m 16, no SiLU epilogue, float32
+// partials, unsplit, and K within one activation chunk of the 16-row kernel (256).
+bool gemm_cgroup_fits(const GemmConfig& c, int K, int split_k);
 
 // Columns of output one workgroup covers (N % this must be 0; act: gate columns).
 int gemm_wg_cols(const GemmConfig& c);
