@@ -43,6 +43,8 @@
 //     loses up to 4 low bits (a relative error up to 2^-7 on such tiny activations);
 //   - the block_m >= 64 decode forms 16 (q - z) s in fp16, which overflows to inf for a group
 //     scale above 65504 / 240 (about 273, decoded weights beyond about 4000 in magnitude).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -622,9 +624,10 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   // broadcast MFMA (BM 16: the matrix cores have room) or, for fp16 at BM 32, by one exact
   // half-precision subtraction per two weights ((1024 + q) - (1024 + z) = q - z), which halves the
   // MFMAs where they would otherwise bound the kernel.  The scale is applied per k-block.
-  auto biased_u4_kb = [&](int slot, const uint32_t* meta, auto&& a_s) {
+  auto biased_u4_kb = [&](auto ma_c, int slot, const uint32_t* meta, auto&& a_s) {
+    constexpr int MA = decltype(ma_c)::value;  // row tiles holding listed slots
     constexpr bool SUBZ = DT == 0 && MT == 2;
-    floatx4_t accg[MT][NTW];
+    floatx4_t accg[MA][NTW];
     u32x4_t bz[NTW];
     float sf[NTW];
 #pragma unroll
@@ -649,7 +652,7 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
         }
       }
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MA; ++m)
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
           accg[m][t] = Mfma<DT>::run(a_s(st, m), b[t], st == 0 ? zero4 : accg[m][t]);
@@ -657,7 +660,7 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
         }
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MA; ++m)
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
 #pragma unroll
@@ -715,7 +718,7 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
           meta[t] = s_meta[kbi * RPM + g * R + (wave * NTW + t) * 16 + rsub];
-        biased_u4_kb(j, meta, a_s);
+        biased_u4_kb(std::integral_constant<int, MT>{}, j, meta, a_s);
         const int nidx = min(idx + PF, total - 1);
         const int ng = nidx / kb_n;
         const uint32_t soff = (uint32_t)ng * gstep + (uint32_t)(kb_beg + nidx - ng * kb_n) * 64;
@@ -739,111 +742,130 @@ __global__ void __launch_bounds__(WAVES * kWave) wna16_gemm_kernel(GemmParams p)
   // Whole unrolled iterations only: k-blocks past kb_end are virtual (zero activations, weights of
   // the last real k-block), so they add exact zeros.  Any exit inside the unrolled body would merge
   // into the loop header and make the compiler drain the prefetch at the top of every iteration.
-  const int n_iter = (kb_end - kb_beg + U - 1) / U;
-  for (int it = 0; it < n_iter; ++it) {
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int idx = it * U + j;
-      const int kb = kb_beg + idx;
-      const int slot = j % PF;
-      const int jc = j % KBC;
-      const int c = idx / KBC;
-      // buffer of chunk c: a constant where U / KBC is even (always for DIRECT)
-      const int cb = (U / KBC) % 2 == 0 ? (j / KBC) & 1 : c & 1;
-      // this k-block's activation fragments
-      const uint16_t* abase = frag_base(jc, cb);
-      auto a_s = [&](int st, int m) -> u32x4_t {
-        if constexpr (DIRECT) {
-          const int cl = jc * (KB / 8) + grp * (KB / 32) + st;  // logical chunk within the row
-          return *(const u32x4_t*)(abuf(cb) + (m * 16 + rsub) * LDA + ((cl ^ swz(rsub)) * 8));
-        }
-        else return *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
-      };
-      uint32_t meta[NTW];
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) meta[t] = mf[t];
-      if constexpr (BIASED && BITS == 4) {
-        biased_u4_kb(slot, meta, a_s);
-      } else if constexpr (BIASED) {
-        // int8: biased codes accumulate over all of K; row sums (ones MFMA) remove the bias at the end
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m) rsum[m] = Mfma<DT>::run(a_s(st, m), ones, rsum[m]);
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            const u32x4_t bb = bias_s8<DT>(wq[slot][t][2 * st], wq[slot][t][2 * st + 1]);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m][t] = Mfma<DT>::run(a_s(st, m), bb, acc[m][t]);
+  // the k loop for MA row tiles holding listed slots (a compile-time count: tiles past the block's
+  // last listed slot, the tail of an expert's last block, are neither read nor multiplied)
+  auto main_loop = [&](auto ma_c) {
+    constexpr int MA = decltype(ma_c)::value;
+    const int n_iter = (kb_end - kb_beg + U - 1) / U;
+    for (int it = 0; it < n_iter; ++it) {
+  #pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int idx = it * U + j;
+        const int kb = kb_beg + idx;
+        const int slot = j % PF;
+        const int jc = j % KBC;
+        const int c = idx / KBC;
+        // buffer of chunk c: a constant where U / KBC is even (always for DIRECT)
+        const int cb = (U / KBC) % 2 == 0 ? (j / KBC) & 1 : c & 1;
+        // this k-block's activation fragments
+        const uint16_t* abase = frag_base(jc, cb);
+        auto a_s = [&](int st, int m) -> u32x4_t {
+          if constexpr (DIRECT) {
+            const int cl = jc * (KB / 8) + grp * (KB / 32) + st;  // logical chunk within the row
+            return *(const u32x4_t*)(abuf(cb) + (m * 16 + rsub) * LDA + ((cl ^ swz(rsub)) * 8));
           }
-        }
-      } else {
-        DecodeK dk[NTW];
-        if constexpr (BITS == 4) {
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) dk[t] = make_decode<DT, 4>(meta[t] & 0xFFFFu, meta[t] >> 16);
-        }
-        // fragments of step s + 1 are read while step s decodes and multiplies (where the
-        // registers allow: not for fp16 BM 128, whose activation staging needs them)
-        constexpr bool STEP_AHEAD = DIRECT || MT <= 4;
-        u32x4_t acur[MT];
-        if constexpr (STEP_AHEAD) {
-#pragma unroll
-          for (int m = 0; m < MT; ++m) acur[m] = a_s(0, m);
-        }
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-          u32x4_t anext[MT];
-          if constexpr (STEP_AHEAD) {
-            if (st + 1 < STEPS) {
-#pragma unroll
-              for (int m = 0; m < MT; ++m) anext[m] = a_s(st + 1, m);
+          else return *(const u32x4_t*)(abase + m * 16 * LDA + st * 8);
+        };
+        uint32_t meta[NTW];
+  #pragma unroll
+        for (int t = 0; t < NTW; ++t) meta[t] = mf[t];
+        if constexpr (BIASED && BITS == 4) {
+          biased_u4_kb(ma_c, slot, meta, a_s);
+        } else if constexpr (BIASED) {
+          // int8: biased codes accumulate over all of K; row sums (ones MFMA) remove the bias at the end
+  #pragma unroll
+          for (int st = 0; st < STEPS; ++st) {
+  #pragma unroll
+            for (int m = 0; m < MA; ++m) rsum[m] = Mfma<DT>::run(a_s(st, m), ones, rsum[m]);
+  #pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+              const u32x4_t bb = bias_s8<DT>(wq[slot][t][2 * st], wq[slot][t][2 * st + 1]);
+  #pragma unroll
+              for (int m = 0; m < MA; ++m) acc[m][t] = Mfma<DT>::run(a_s(st, m), bb, acc[m][t]);
             }
           }
-          u32x4_t b[NTW];
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            if constexpr (BITS == 4)
-              b[t] = decode_u4<DT>(wq[slot][t][st], dk[t], kMask, kMaskHi, kMagic);
-            else
-              b[t] = decode_s8<DT>(wq[slot][t][2 * st], wq[slot][t][2 * st + 1], dk8[t]);
-          }
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int t = 0; t < NTW; ++t)
-              acc[m][t] = Mfma<DT>::run(STEP_AHEAD ? acur[m] : a_s(st, m), b[t], acc[m][t]);
-          if constexpr (STEP_AHEAD) {
-            if (st + 1 < STEPS) {
-#pragma unroll
-              for (int m = 0; m < MT; ++m) acur[m] = anext[m];
-            }
-          }
-        }
-      }
-      load_kb(slot, min(kb + PF, kb_last));
-      if (jc == KBC - 1) {
-        if constexpr (DIRECT) {
-          // end of chunk c: chunk c+1 was requested before this chunk's KBC weight prefetches, so
-          // waiting for all but those leaves it in LDS; then chunk c+2 into the buffer of chunk c
-          wait_vmcnt<KBC * NTW>();
-          if constexpr (RING) ring_store((j + 1) & 1, idx + 1);
-          barrier_lds();
-          if constexpr (RING) ring_load((j + 1) & 1, idx + 3);
-          dma_a(c + 2, cb);
         } else {
-          // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
-          const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
-          store_a(q, cb ^ 1);
-          if constexpr (RING) ring_store((j + 1) & 1, idx + 1);
-          barrier_lds();
-          if constexpr (RING) ring_load((j + 1) & 1, idx + 3);
-          load_a(q, c + 1 + AQ);
+          DecodeK dk[NTW];
+          if constexpr (BITS == 4) {
+  #pragma unroll
+            for (int t = 0; t < NTW; ++t) dk[t] = make_decode<DT, 4>(meta[t] & 0xFFFFu, meta[t] >> 16);
+          }
+          // fragments of step s + 1 are read while step s decodes and multiplies (where the
+          // registers allow: not for fp16 BM 128, whose activation staging needs them)
+          constexpr bool STEP_AHEAD = DIRECT || MT <= 4;
+          u32x4_t acur[MA];
+          if constexpr (STEP_AHEAD) {
+  #pragma unroll
+            for (int m = 0; m < MA; ++m) acur[m] = a_s(0, m);
+          }
+  #pragma unroll
+          for (int st = 0; st < STEPS; ++st) {
+            u32x4_t anext[MA];
+            if constexpr (STEP_AHEAD) {
+              if (st + 1 < STEPS) {
+  #pragma unroll
+                for (int m = 0; m < MA; ++m) anext[m] = a_s(st + 1, m);
+              }
+            }
+            u32x4_t b[NTW];
+  #pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+              if constexpr (BITS == 4)
+                b[t] = decode_u4<DT>(wq[slot][t][st], dk[t], kMask, kMaskHi, kMagic);
+              else
+                b[t] = decode_s8<DT>(wq[slot][t][2 * st], wq[slot][t][2 * st + 1], dk8[t]);
+            }
+  #pragma unroll
+            for (int m = 0; m < MA; ++m)
+  #pragma unroll
+              for (int t = 0; t < NTW; ++t)
+                acc[m][t] = Mfma<DT>::run(STEP_AHEAD ? acur[m] : a_s(st, m), b[t], acc[m][t]);
+            if constexpr (STEP_AHEAD) {
+              if (st + 1 < STEPS) {
+  #pragma unroll
+                for (int m = 0; m < MA; ++m) acur[m] = anext[m];
+              }
+            }
+          }
         }
+        load_kb(slot, min(kb + PF, kb_last));
+        if (jc == KBC - 1) {
+          if constexpr (DIRECT) {
+            // end of chunk c: chunk c+1 was requested before this chunk's KBC weight prefetches, so
+            // waiting for all but those leaves it in LDS; then chunk c+2 into the buffer of chunk c
+            wait_vmcnt<KBC * NTW>();
+            if constexpr (RING) ring_store((j + 1) & 1, idx + 1);
+            barrier_lds();
+            if constexpr (RING) ring_load((j + 1) & 1, idx + 3);
+            dma_a(c + 2, cb);
+          } else {
+            // end of chunk c: publish chunk c+1 (zeros past the range), then fetch chunk c+1+AQ
+            const int q = ((j / KBC) + 1) % AQ;  // == (c + 1) % AQ, as U is a multiple of KBC * AQ
+            store_a(q, cb ^ 1);
+            if constexpr (RING) ring_store((j + 1) & 1, idx + 1);
+            barrier_lds();
+            if constexpr (RING) ring_load((j + 1) & 1, idx + 3);
+            load_a(q, c + 1 + AQ);
+          }
+        }
+        load_meta(idx + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetches where they are issued
       }
-      load_meta(idx + 1);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetches where they are issued
     }
+  };
+  // 64-row blocks with activations straight into LDS (bf16 uint4, int8) only: with 16 or 32 rows,
+  // or activations staged through registers (fp16 uint4), the extra loop copies cost a wavefront
+  // per SIMD of registers (BLOCK_M 32: 128 -> 155; fp16 uint4 BLOCK_M 64: 152 -> 216)
+  if constexpr (MT == 4 && DIRECT) {
+    // listed slots are a prefix of the block (s_slot published by the prologue's barrier)
+    const int n_valid = __builtin_popcountll(__ballot(lane < BM && s_slot[lane] >= 0));
+    const int mt_valid = __builtin_amdgcn_readfirstlane((n_valid + 15) / 16);
+    if (mt_valid >= 4) main_loop(std::integral_constant<int, 4>{});
+    else if (mt_valid == 3) main_loop(std::integral_constant<int, 3>{});
+    else if (mt_valid == 2) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 1>{});
+  } else {
+    main_loop(std::integral_constant<int, MT>{});
   }
 
   // LDS-destination loads still in flight (chunks past the range) must land before the workgroup's
