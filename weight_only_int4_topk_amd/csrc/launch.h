@@ -62,7 +62,7 @@ struct GemmParams {
 struct GemmConfig {
   int dtype;     // 0 fp16, 1 bf16
   int bits;      // 4 or 8
-  int block_m;   // 16, 32, 64, 128
+  int block_m;   // 16, 32, 64, 128, 256
   int act;       // 0 none, 1 silu-mul
   int out_f32;   // 1: float partials [split, num_slots, N]
   int ntw;       // column tiles of 16 per wavefront: 2, or 4 (block_m 16 only)
@@ -85,8 +85,8 @@ size_t gemm_lds_bytes(int K, int split_k, const GemmConfig& c);
 constexpr size_t kGemmLdsLimit = 160 * 1024;
 hipError_t launch_gemm(const GemmParams& p, const GemmConfig& c, hipStream_t stream);
 
-// The prefill tiling (prefill.hip): block_m 128 on the 32x32 matrix cores, 8 wavefronts of
-// prefill_nt(c, N) column tiles of 32.  launch_gemm takes it wherever prefill_fits(c, N).
+// The prefill tiling (prefill.hip): block_m 128 and 256 on the 32x32 matrix cores, 8 wavefronts
+// of prefill_nt(c, N) column tiles of 32.  launch_gemm takes it wherever prefill_fits(c, N).
 bool prefill_fits(const GemmConfig& c, int N);
 int prefill_nt(const GemmConfig& c, int N);
 int prefill_wg_cols(const GemmConfig& c, int N);

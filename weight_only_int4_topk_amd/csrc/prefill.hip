@@ -1,5 +1,5 @@
-// Grouped GEMM over all experts for the prefill regime (block_m 128) on the 32 x 32 matrix cores
-// of gfx950.
+// Grouped GEMM over all experts for the prefill regime (block_m 128 and 256) on the 32 x 32 matrix
+// cores of gfx950.
 //
 // The same operation as wna16_gemm_kernel (one launch over every expert, "[Kernel] add triton
 // fused moe kernel for gptq/awq", PR description; uint4 g128 with integer zero points or int8 with
@@ -13,7 +13,8 @@
 //               one K split.  The block's activation rows go from memory straight into LDS, one k-block
 //               at a time, double-buffered.
 //   wavefront = NT column tiles of 32 weight rows (with the SiLU epilogue: a gate tile and the
-//               matching up tile), every row tile of the block.
+//               matching up tile, or at NT = 1 one mixed tile of 16 gate rows and the 16 matching
+//               up rows), every row tile of the block.
 //   k-block   = 64 bytes of a weight row: 128 k of uint4 (one group) or 64 k of int8.  Lane l of a
 //               column tile loads 32 bytes of row (l % 32) at byte 32 (l / 32), so lane half h
 //               covers k in [64 h, 64 h + 64) (int8: [32 h, 32 h + 32)) of the k-block.
