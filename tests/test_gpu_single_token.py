@@ -1,0 +1,110 @@
+"""The layer for one token (M = 1, uint4, block_m left to the library): routing, then one dot
+product per weight row in two launches (SiLU(gate) * up; the second product with the top-k
+combine).  Against the oracle, every element, with the tolerance of the other layer tests; the
+shapes cover each groups-per-lane variant of both launches, quantisation groups that do not fill a
+wavefront, and the fallback to the grouped GEMMs where the staged activations exceed LDS."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_only_int4_topk_amd as B
+from tests.helpers import (assert_layer_close, cuda_layer, fused_vs_oracle, oracle_route,
+                           routing_of, run_fused)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+CASES = {
+    "tiny_fp16": W["tiny"].with_(block_m=0),
+    "tiny_bf16": W["tiny"].with_(block_m=0, dtype="bf16"),
+    "sigmoid_groups_bf16": synth.Workload("sg1", E=64, H=512, I=256, topk=8, Ms=(1,), dtype="bf16",
+                                          score="sigmoid", num_groups=8, topk_groups=4, scale=2.5),
+    "softmax_bias": synth.Workload("sb1", E=64, H=768, I=512, topk=8, Ms=(1,), logit_bias=True),
+    "no_renorm": synth.Workload("nr1", E=32, H=512, I=256, topk=4, Ms=(1,), renormalize=False),
+    "one_expert": synth.Workload("d11", E=1, H=512, I=512, topk=1, Ms=(1,)),
+    "all_experts": synth.Workload("ae1", E=4, H=256, I=256, topk=4, Ms=(1,)),
+    "topk3": synth.Workload("k31", E=16, H=1024, I=768, topk=3, Ms=(1,), dtype="bf16"),
+    # 14 and 10 groups per row: lanes without a group in both launches
+    "odd_groups_fp16": synth.Workload("og1", E=16, H=1792, I=1280, topk=4, Ms=(1,)),
+    "odd_groups_bf16": synth.Workload("og2", E=16, H=1792, I=1280, topk=4, Ms=(1,), dtype="bf16"),
+    # 96 groups per first-launch row: two steps of two groups per lane
+    "wide_h": synth.Workload("wh1", E=4, H=12288, I=512, topk=2, Ms=(1,), dtype="bf16"),
+    # 256 groups per first-launch row: four steps
+    "widest_h": synth.Workload("wh2", E=2, H=32768, I=256, topk=1, Ms=(1,)),
+    # 256 groups per second-launch row over 64 lanes: two steps of two groups per lane; with
+    # topk 2 the staged intermediate rows take 128 KiB of LDS
+    "widest_i": synth.Workload("wi1", E=2, H=256, I=32768, topk=2, Ms=(1,), dtype="bf16"),
+    # the same with topk 4 exceeds LDS: the grouped GEMMs run instead
+    "widest_i_fallback": synth.Workload("wi2", E=4, H=256, I=32768, topk=4, Ms=(1,)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_single_token_vs_oracle(name, seed):
+    print(f"single token {name} seed={seed}", flush=True)
+    fused_vs_oracle(CASES[name], 1, seed=seed)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp16", "sigmoid_groups_bf16", "odd_groups_fp16"])
+def test_single_token_grouped_gemm_path(name):
+    """An explicit block_m keeps one token on the grouped GEMMs: both paths against the oracle."""
+    fused_vs_oracle(CASES[name], 1, seed=3, block_m=16)
+
+
+def test_single_token_zero_activations_give_zero():
+    """x = 0: every group's dot product and activation sum are exactly zero, so is the output."""
+    wl = CASES["odd_groups_bf16"]
+    layer = cuda_layer(synth.make_layer(wl, seed=2))
+    x = torch.zeros((1, wl.H), dtype=wl.torch_dtype, device="cuda")
+    lg = synth.make_logits(wl, 1, seed=2).cuda()
+    out, _, _ = run_fused(wl, x, lg, layer)
+    assert (out.float() == 0).all()
+
+
+def test_single_token_fp16_tiny_activations():
+    """fp16 activations of order 2e-5 (many subnormal) against weights N(0, 5^2): the dot products
+    take the activations as they are, so the output matches the oracle to the usual tolerance
+    relative to its largest element."""
+    wl = synth.Workload("ta1", E=4, H=512, I=512, topk=2, Ms=(1,), x_std=2e-5, w_std=5.0)
+    layer = synth.make_layer(wl, seed=3)
+    x = synth.make_x(wl, 1, seed=3)
+    lg = synth.make_logits(wl, 1, seed=3)
+    out, tw, ti = run_fused(wl, x.cuda(), lg.cuda(), cuda_layer(layer))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    ref = O.moe_layer(x, ids_ref, w_ref, O.ExpertSource(layer, 4))
+    sc = 1.0 / np.abs(ref).max()
+    assert_layer_close(O.to_numpy(out).astype(np.float64) * sc, np.asarray(ref) * sc,
+                       "tiny activations, one token")
+
+
+def test_single_token_deterministic_and_graph_replay():
+    wl = CASES["sigmoid_groups_bf16"]
+    layer = cuda_layer(synth.make_layer(wl, seed=1))
+    x = synth.make_x(wl, 1, seed=1).cuda()
+    lg = synth.make_logits(wl, 1, seed=1).cuda()
+    out1, _, _ = run_fused(wl, x, lg, layer)
+    out2, _, _ = run_fused(wl, x, lg, layer)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    ws = torch.empty((B.fused_moe_wna16_workspace_size(1, wl.H, wl.I, wl.E, wl.topk, B.QUANT_INT4,
+                                                       wl.torch_dtype, 0),), dtype=torch.uint8,
+                     device="cuda")
+    gout = torch.empty_like(out1)
+    run = lambda: B.fused_moe_wna16(x, lg, wl.topk, routing_of(wl), layer["w13"],
+                                    layer["w13_scales"], layer["w13_zeros"], layer["w2"],
+                                    layer["w2_scales"], layer["w2_zeros"], block_m=0,
+                                    workspace=ws, out=gout)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        gout.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gout.view(torch.int16), out1.view(torch.int16)), f"replay {i}"
+        run_fused(wl, x, lg, layer)  # eager work between replays

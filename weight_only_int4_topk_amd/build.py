@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_wna16.so")
 
 SOURCES = ["api.cpp", "routing.hip", "align.hip", "gemm.hip", "prefill.hip", "combine.hip",
-           "w8a8.hip", "noalloc.hip", "repack.hip"]
+           "w8a8.hip", "noalloc.hip", "repack.hip", "gemv.hip"]
 ARCH = os.environ.get("MOE_WNA16_ARCH", "gfx950")
 
 FLAGS = [

@@ -845,6 +845,42 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   const size_t need = pl.total + (act_order ? act_order_bytes(M, H, I, topk) : 0);
   if (workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* tw = topk_weights_out ? topk_weights_out : (float*)(ws + pl.off_w);
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(ws + pl.off_ids);
+  void* inter = ws + pl.off_inter;
+  const moe::RoutingParams rp{routing->score, routing->renormalize, routing->num_groups,
+                              routing->topk_groups, routing->scale};
+  hipError_t e;
+
+  // one token, uint4, tile size left to the library: one dot product per weight row in two
+  // launches (gemv.hip), the routing inside the first, the top-k combine inside the second
+  if (M == 1 && quant->bits == 4 && !act_order && block_m == 0 &&
+      moe::single_fits(H, I, E, topk)) {
+    moe::SingleParams sp{};
+    sp.x = x;
+    sp.logits = router_logits;
+    sp.rp = rp;
+    sp.topk_ids = ids;
+    sp.topk_w = tw;
+    sp.w13 = (const uint8_t*)w13;
+    sp.s13 = w13_scales;
+    sp.z13 = (const uint8_t*)w13_zeros;
+    sp.w2 = (const uint8_t*)w2;
+    sp.s2 = w2_scales;
+    sp.z2 = (const uint8_t*)w2_zeros;
+    sp.E = E;
+    sp.H = H;
+    sp.I = I;
+    sp.topk = topk;
+    sp.inter = inter;
+    sp.out = out;
+    e = moe::launch_single(sp, dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "single-token launch");
+    return MOE_OK;
+  }
+
   const bool split1 = pl.split1 > 1;
   // split: plain columns (gate rows, then up rows) into float32 partials, 2 column tiles per
   // wavefront so the workgroup count matches the estimate the split was chosen for
@@ -861,20 +897,12 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   if (int rc = fit_lds(H, pl.split1, c1, "gemm1")) return rc;
   if (int rc = fit_lds(I, pl.split2, c2, "gemm2")) return rc;
 
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  float* tw = topk_weights_out ? topk_weights_out : (float*)(ws + pl.off_w);
-  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(ws + pl.off_ids);
   int32_t* sorted = (int32_t*)(ws + pl.off_sorted);
   int32_t* eids = (int32_t*)(ws + pl.off_eids);
   int32_t* npost = (int32_t*)(ws + pl.off_npost);
-  void* inter = ws + pl.off_inter;
   float* part = (float*)(ws + pl.off_part);
   const int slots = M * topk;
 
-  const moe::RoutingParams rp{routing->score, routing->renormalize, routing->num_groups,
-                              routing->topk_groups, routing->scale};
-  hipError_t e;
   if (moe::route_align_fits(M, E)) {
     e = moe::launch_route_align(router_logits, M, E, topk, rp, tw, ids, pl.bm, sorted, eids, npost,
                                 pl.cap, st);

@@ -1,0 +1,469 @@
+// The layer for one token (M = 1) with uint4 experts in two launches.
+//
+// The same operation as the grouped GEMMs of the layer ("[Kernel] add triton fused moe kernel for
+// gptq/awq", PR description: one launch over all experts; uint4 g128 with integer zero points):
+//   up:   inter[j, n] = SiLU(W13[e_j, n, :] . x) * (W13[e_j, I + n, :] . x)      n < I
+//   down: out[n]      = sum_j w_j * (W2[e_j, n, :] . inter[j, :])               n < H
+// with (e_j, w_j) the token's top-k experts and routing weights.  With one token a block of the
+// grouped GEMM holds one listed row of sixteen, and the layer's time goes to start-up and to the
+// passes between its launches (routing, align, the split first GEMM's SiLU pass, the combine);
+// here each weight row is one dot product, the first launch routes the token itself and the
+// second adds the top-k products.
+//
+// Arithmetic.  Each lane takes whole 128-k quantisation groups of a row.  The 8 nibbles of a
+// weight dword become four pairs of the activation dtype, (k0,k4) (k1,k5) (k2,k6) (k3,k7), each
+// nibble shifted into the top four mantissa bits of a number with unit last place (fp16 1024,
+// bf16 128): the pair value is magic + c q with c = 64 (fp16) or 8 (bf16), one shift and one
+// and-or per pair.  v_dot2_f32_{f16,bf16} multiplies the pairs with the matching activation
+// pairs (5-bit by 11- or 8-bit significands: exact in float32) into a float32 sum.  Per group,
+//   sum_k (q_k - z) a_k = (sum_k (magic + c q_k) a_k - (magic + c z) sum_k a_k) / c,
+// times the group scale, with sum_k a_k of every group formed once per workgroup; magic is at
+// most twice c times the largest q - z, so the subtraction cancels at most about one bit.  The
+// activations sit in LDS permuted per 8-k chunk to (a0,a4,a1,a5,a2,a6,a3,a7), and the 16 chunks
+// of a group rotated by the group index, so the lanes of a wavefront, which read the same chunk of
+// consecutive groups, hit different banks.
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+#include "route_body.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSWaves = 8;
+constexpr int kSThreads = kSWaves * kWave;
+constexpr int kRsrcS = 0x00020000;  // gfx9-family buffer descriptor: 32-bit data format
+
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float c) {
+  if constexpr (DT == 0)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w), __builtin_bit_cast(half2_t, a), c,
+                                  false);
+  else {
+    typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, w),
+                                           __builtin_bit_cast(bf162_t, a), c, false);
+  }
+}
+
+__device__ __forceinline__ uint32_t and_or_s(uint32_t a, uint32_t m, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);  // (a & m) | c
+}
+
+// LDS dword offset of 8-k chunk c of a staged vector: chunk r of group g sits at slot (r + g) % 16
+__device__ __forceinline__ int chunk_pos(int g, int r) { return 4 * (g * 16 + ((r + g) & 15)); }
+
+// Stage nvec activation vectors of length K (dtype, src + v * K) into LDS: sx + v * K / 2 dwords in
+// the permuted, rotated chunk layout, and ssum[v * G + g] = sum of group g of vector v (float32,
+// the 8 values of a chunk in order, then the 16 chunks of a group by a butterfly).
+template <int DT>
+__device__ void stage_vectors(const uint16_t* __restrict__ src, int nvec, int K,
+                              uint32_t* __restrict__ sx, float* __restrict__ ssum) {
+  const int nch = K / 8;
+  const int G = K / 128;
+  const int total = nvec * nch;  // a multiple of 16: whole groups exit the loop together
+  for (int t = threadIdx.x; t < total; t += kSThreads) {
+    const int v = t / nch;
+    const int c = t - v * nch;
+    const u32x4_t raw = *(const u32x4_t*)(src + (size_t)v * K + (size_t)c * 8);
+    const uint32_t r0 = raw[0], r1 = raw[1], r2 = raw[2], r3 = raw[3];
+    const u32x4_t pv = {__builtin_amdgcn_perm(r2, r0, 0x05040100u),
+                        __builtin_amdgcn_perm(r2, r0, 0x07060302u),
+                        __builtin_amdgcn_perm(r3, r1, 0x05040100u),
+                        __builtin_amdgcn_perm(r3, r1, 0x07060302u)};
+    *(u32x4_t*)(sx + (size_t)v * (K / 2) + chunk_pos(c >> 4, c & 15)) = pv;
+    float s = 0.f;
+    const uint32_t rr[4] = {r0, r1, r2, r3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += bits_to_float<DT>((uint16_t)(rr[i] & 0xFFFFu));
+      s += bits_to_float<DT>((uint16_t)(rr[i] >> 16));
+    }
+    s += __shfl_xor(s, 1, 16);
+    s += __shfl_xor(s, 2, 16);
+    s += __shfl_xor(s, 4, 16);
+    s += __shfl_xor(s, 8, 16);
+    if ((c & 15) == 0) ssum[v * G + (c >> 4)] = s;
+  }
+}
+
+// Nibble pair d of a weight dword (k offsets d and d + 4) moved into the mask bits of its
+// 16-bit halves: bits 6-9 (fp16) or 3-6 (bf16), the top four mantissa bits of the magic number.
+template <int DT, int D>
+__device__ __forceinline__ uint32_t pair_bits(uint32_t w) {
+  constexpr int sh = DT == 0 ? 6 - 4 * D : 3 - 4 * D;
+  if constexpr (sh >= 0) return w << sh;
+  else return w >> (-sh);
+}
+
+// sum_k (magic + c q_k) a_k over the 128 k of group g: w = the group's 64 bytes (4 x 16), sv = the
+// staged vector; four partial sums added in a fixed order
+template <int DT>
+__device__ __forceinline__ float group_dot(const u32x4_t (&w)[4], const uint32_t* sv, int g,
+                                           uint32_t mask, uint32_t magic) {
+  float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const u32x4_t a = *(const u32x4_t*)(sv + chunk_pos(g, 4 * q + d));
+      const uint32_t a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+      const uint32_t wd = w[q][d];
+      p0 = dot2<DT>(and_or_s(pair_bits<DT, 0>(wd), mask, magic), a0, p0);
+      p1 = dot2<DT>(and_or_s(pair_bits<DT, 1>(wd), mask, magic), a1, p1);
+      p2 = dot2<DT>(and_or_s(pair_bits<DT, 2>(wd), mask, magic), a2, p2);
+      p3 = dot2<DT>(and_or_s(pair_bits<DT, 3>(wd), mask, magic), a3, p3);
+    }
+  }
+  return (p0 + p1) + (p2 + p3);
+}
+
+// group scale / c and magic + c z of the group's zero point (see the file comment)
+template <int DT>
+__device__ __forceinline__ void group_terms(uint32_t sbits, uint32_t zbyte, int g, float& sc,
+                                            float& off) {
+  constexpr float c = DT == 0 ? 64.0f : 8.0f;
+  constexpr float magicv = DT == 0 ? 1024.0f : 128.0f;
+  sc = bits_to_float<DT>((uint16_t)(sbits & 0xFFFFu)) * (1.0f / c);
+  off = magicv + c * (float)((zbyte >> ((g & 1) * 4)) & 0xFu);
+}
+
+// ------------------------------------------------------------------------------------------------
+// up: wavefront 0 routes the token while the others start staging x; then one unit = (slot j,
+// output column n) per step group: lanes 0-31 the gate row n, lanes 32-63 the up row I + n, lane
+// l % 32 the groups l % 32 + 32 i, i < GPL.  A wavefront runs upw consecutive units in steps of at
+// most two groups per lane (P steps per unit), the weights of the next step in flight while it
+// computes one; the first step is issued before the activations are staged.
+// ------------------------------------------------------------------------------------------------
+template <int DT, int GPL>
+__global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
+  extern __shared__ uint32_t s_dyn[];
+  __shared__ float s_route[4 * kWave];
+  __shared__ float s_w_sink[kWave];
+  __shared__ int32_t s_id_sink[kWave];
+  __shared__ int32_t s_ids[kWave];
+  const int K = p.H, I = p.I;
+  const int G = K / 128;
+  uint32_t* sx = s_dyn;
+  float* ssum = (float*)(s_dyn + K / 2);
+
+  constexpr int CH = GPL < 2 ? GPL : 2;   // groups per lane and step
+  constexpr int P = GPL / CH;             // steps per unit
+  constexpr int QN = P == 1 ? 2 : P;      // steps per loop iteration (two slots alternate)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int U = p.topk * I;
+  const int N = 2 * I;
+  const uint32_t row_bytes = (uint32_t)K / 2;
+  const uint32_t srow = (uint32_t)G * 2;
+  const uint32_t zrow = (uint32_t)(K / 256);
+  constexpr uint32_t mask = DT == 0 ? 0x03C003C0u : 0x00780078u;
+  constexpr uint32_t magic = DT == 0 ? 0x64006400u : 0x43004300u;
+  const int u0 = (blockIdx.x * kSWaves + wave) * p.upw;
+
+  if (wave == 0) {
+    // every workgroup routes the token (a few hundred logits); the first one publishes the result
+    const bool pub = blockIdx.x == 0;
+    route_token<4>(p.logits, p.E, p.topk, p.rp, s_route, pub ? p.topk_w : s_w_sink,
+                   pub ? p.topk_ids : s_id_sink, s_ids);
+  }
+  __syncthreads();
+
+  u32x4_t wq[2][CH][4];
+  uint32_t sq[2][CH], zq[2][CH];
+  auto load_step = [&](int slot, int k, int part) {
+    const int u = min(u0 + k, U - 1);  // units past the end reload the last one (not stored)
+    const int j = u / I;
+    const int n = u - j * I;
+    int e = s_ids[j];
+    e = (unsigned)e < (unsigned)p.E ? e : 0;  // no id (NaN logits): rows of expert 0, unused
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w13 + (size_t)e * N * row_bytes), (short)0, (int)(N * row_bytes), kRsrcS);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint8_t*)p.s13 + (size_t)e * N * srow), (short)0, (int)(N * srow), kRsrcS);
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.z13 + (size_t)e * N * zrow), (short)0, (int)(N * zrow), kRsrcS);
+    const uint32_t row = (uint32_t)(h ? I + n : n);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int g = min(l32 + 32 * (part * CH + i), G - 1);  // past the row's groups: its last one
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        wq[slot][i][q] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, row * row_bytes + g * 64 + q * 16, 0, 0));
+      sq[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
+      zq[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
+    }
+  };
+  float acc = 0.f;
+  auto compute_step = [&](int slot, int k, int part) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int g = l32 + 32 * (part * CH + i);
+      if (g < G) {
+        float sc, off;
+        group_terms<DT>(sq[slot][i], zq[slot][i], g, sc, off);
+        const float d = group_dot<DT>(wq[slot][i], sx, g, mask, magic);
+        acc += sc * (d - off * ssum[g]);
+      }
+    }
+    if (part != P - 1) return;
+    // sum over the 32 lanes of each half (fixed order), then gate (lane 0) and up (lane 32)
+    acc += __shfl_xor(acc, 1, 32);
+    acc += __shfl_xor(acc, 2, 32);
+    acc += __shfl_xor(acc, 4, 32);
+    acc += __shfl_xor(acc, 8, 32);
+    acc += __shfl_xor(acc, 16, 32);
+    const float gate = __shfl(acc, 0, kWave);
+    const float up = __shfl(acc, 32, kWave);
+    const int u = u0 + k;
+    if (lane == 0 && u < U) {
+      const float v = gate / (1.0f + __expf(-gate)) * up;
+      ((uint16_t*)p.inter)[u] = float_to_bits<DT>(v);  // u = j * I + n
+    }
+    acc = 0.f;
+  };
+
+  load_step(0, 0, 0);  // in flight while x is staged
+  stage_vectors<DT>((const uint16_t*)p.x, 1, K, sx, ssum);
+  __syncthreads();
+
+  // step t = k * P + part uses slot t % 2
+  for (int k = 0; k < p.upw; k += QN / P) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int kn = k + (q + 1) / P;
+      if (kn < p.upw) load_step((q + 1) & 1, kn, (q + 1) % P);
+      if (k + q / P < p.upw) compute_step(q & 1, k + q / P, q % P);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// down: a workgroup covers RW consecutive output rows; wavefront w takes slot j = w % topk and the
+// rows of part w / topk (nrp = 8 / topk parts, RPW rows each; topk > 8: slots w, w + 8, ...).  A
+// row's G groups spread over L lanes (the smallest power of two >= G, at most 64; TPL groups per
+// lane, taken two per step), 64 / L rows per pass.  Each wavefront leaves w_j * (row . inter[j])
+// per row in LDS; the workgroup then adds the slots in ascending j and writes the rows.  The first
+// step's weights are requested before the intermediate rows are staged.
+// ------------------------------------------------------------------------------------------------
+template <int DT, int TPL>
+__global__ void __launch_bounds__(kSThreads) single_down_kernel(SingleParams p) {
+  extern __shared__ uint32_t s_dyn[];
+  const int K = p.I, H = p.H, topk = p.topk;
+  const int G = K / 128;
+  uint32_t* sx = s_dyn;                                   // topk vectors of K
+  float* ssum = (float*)(s_dyn + (size_t)topk * K / 2);  // topk x G
+  float* spart = ssum + topk * G;                         // topk x RW row results
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int L = p.lanes_per_row;       // power of two, >= G / TPL
+  const int RPP = kWave / L;           // rows per pass
+  const int sub = lane & (L - 1);
+  const int rsub = lane / L;
+  const int RW = p.rows_per_wg;
+  const int n0 = blockIdx.x * RW;
+  const uint32_t row_bytes = (uint32_t)K / 2;
+  const uint32_t srow = (uint32_t)G * 2;
+  const uint32_t zrow = (uint32_t)(K / 256);
+  constexpr uint32_t mask = DT == 0 ? 0x03C003C0u : 0x00780078u;
+  constexpr uint32_t magic = DT == 0 ? 0x64006400u : 0x43004300u;
+  const int nrp = topk >= kSWaves ? 1 : kSWaves / topk;
+  const int RPW = RW / nrp;            // rows of one wavefront's part (a multiple of RPP)
+  const int passes = RPW / RPP;
+  constexpr int CH = TPL < 2 ? TPL : 2;  // groups per lane and step
+  constexpr int P = TPL / CH;            // steps per pass of rows
+  constexpr int QN = P == 1 ? 2 : P;     // steps per loop iteration (two slots alternate)
+
+  // the (slot, part) a wavefront works on, set by select()
+  int j = 0, part = 0;
+  bool valid = false;
+  float wj = 0.f;
+  __amdgpu_buffer_rsrc_t rw, rs, rz;
+  auto select = [&](int jw) {
+    j = jw % topk;
+    part = jw / topk;
+    int e = p.topk_ids[j];
+    valid = (unsigned)e < (unsigned)p.E;  // routing gives [0, E); anything else adds nothing
+    wj = valid ? p.topk_w[j] : 0.0f;
+    e = valid ? e : 0;
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w2 + (size_t)e * H * row_bytes), (short)0,
+                                           (int)(H * row_bytes), kRsrcS);
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)p.s2 + (size_t)e * H * srow),
+                                           (short)0, (int)(H * srow), kRsrcS);
+    rz = __builtin_amdgcn_make_buffer_rsrc((void*)(p.z2 + (size_t)e * H * zrow), (short)0,
+                                           (int)(H * zrow), kRsrcS);
+  };
+
+  u32x4_t wq[2][CH][4];
+  uint32_t sq[2][CH], zq[2][CH];
+  auto load_step = [&](int slot, int ps, int gp) {
+    const uint32_t row = (uint32_t)min(n0 + part * RPW + ps * RPP + rsub, H - 1);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int g = min(sub + L * (gp * CH + i), G - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        wq[slot][i][q] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, row * row_bytes + g * 64 + q * 16, 0, 0));
+      sq[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
+      zq[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
+    }
+  };
+  float acc = 0.f;
+  auto compute_step = [&](int slot, int ps, int gp) {
+    const uint32_t* sv = sx + (size_t)j * K / 2;
+    const float* sj = ssum + j * G;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int g = sub + L * (gp * CH + i);
+      if (g < G) {
+        float sc, off;
+        group_terms<DT>(sq[slot][i], zq[slot][i], g, sc, off);
+        const float d = group_dot<DT>(wq[slot][i], sv, g, mask, magic);
+        acc += sc * (d - off * sj[g]);
+      }
+    }
+    if (gp != P - 1) return;
+    for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m, L);
+    const int r = part * RPW + ps * RPP + rsub;  // row within the workgroup
+    if (sub == 0) spart[j * RW + r] = valid ? wj * acc : 0.0f;
+    acc = 0.f;
+  };
+
+  const int njw = topk * nrp;
+  if (wave < njw) {  // in flight while the intermediate rows are staged
+    select(wave);
+    load_step(0, 0, 0);
+  }
+  stage_vectors<DT>((const uint16_t*)p.inter, topk, K, sx, ssum);
+  __syncthreads();
+
+  for (int jw = wave; jw < njw; jw += kSWaves) {
+    if (jw != wave) {
+      select(jw);
+      load_step(0, 0, 0);
+    }
+    // step t = ps * P + gp uses slot t % 2
+    for (int ps = 0; ps < passes; ps += QN / P) {
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        const int pn = ps + (q + 1) / P;
+        if (pn < passes) load_step((q + 1) & 1, pn, (q + 1) % P);
+        if (ps + q / P < passes) compute_step(q & 1, ps + q / P, q % P);
+      }
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < RW; r += kSThreads) {
+    const int n = n0 + r;
+    if (n >= H) continue;
+    float v = 0.f;
+    for (int jj = 0; jj < topk; ++jj) v += spart[jj * RW + r];
+    ((uint16_t*)p.out)[n] = float_to_bits<DT>(v);
+  }
+}
+
+constexpr int kCUs = 256;              // MI355X compute units
+constexpr size_t kLdsPerCU = 160 * 1024;
+
+// Workgroups of a kernel that one compute unit holds at once by its registers.
+template <typename F>
+int occupancy_of(F kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kSThreads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+// ... and by its LDS as well (`lds` dynamic bytes plus at most 2 KiB of static arrays)
+int resident_per_cu(int by_regs, size_t lds) {
+  return std::max(1, std::min(by_regs, (int)(kLdsPerCU / (lds + 2048))));
+}
+
+// Launch shape of the down kernel: L lanes per row (a power of two covering the row's groups in at
+// most 4 per lane), rows per workgroup a multiple of nrp * (64 / L).
+struct DownPlan {
+  int lanes, tpl, unit;
+  size_t lds_fixed;  // staged rows and group sums (the row results add topk * 4 bytes per row)
+};
+
+DownPlan down_plan(int H, int I, int topk) {
+  DownPlan d{};
+  const int G = I / 128;
+  d.lanes = 1;
+  while (d.lanes < G && d.lanes < kWave) d.lanes <<= 1;
+  d.tpl = (G + d.lanes - 1) / d.lanes;
+  const int nrp = topk >= kSWaves ? 1 : kSWaves / topk;
+  d.unit = nrp * (kWave / d.lanes);
+  d.lds_fixed = (size_t)topk * I * 2 + (size_t)topk * G * 4;
+  return d;
+}
+
+size_t up_lds(int H) { return (size_t)H * 2 + (size_t)(H / 128) * 4; }
+
+template <int DT, int GPL>
+hipError_t launch_up(SingleParams& p, hipStream_t stream) {
+  static const int occ = occupancy_of(single_up_kernel<DT, GPL>);
+  const size_t lds = up_lds(p.H);
+  const int U = p.topk * p.I;
+  // one round of resident workgroups, each wavefront a run of consecutive units
+  const int slots = kCUs * resident_per_cu(occ, lds);
+  int grid = std::min((U + kSWaves - 1) / kSWaves, slots);
+  p.upw = (U + grid * kSWaves - 1) / (grid * kSWaves);
+  grid = (U + kSWaves * p.upw - 1) / (kSWaves * p.upw);
+  hipLaunchKernelGGL((single_up_kernel<DT, GPL>), dim3(grid), dim3(kSThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT, int TPL>
+hipError_t launch_down(SingleParams& p, const DownPlan& d, hipStream_t stream) {
+  static const int occ = occupancy_of(single_down_kernel<DT, TPL>);
+  // one round of resident workgroups (rows per workgroup a multiple of the plan's unit)
+  const int units = (p.H + d.unit - 1) / d.unit;
+  size_t lds = d.lds_fixed + (size_t)p.topk * d.unit * 4;
+  const int slots = kCUs * resident_per_cu(occ, lds);
+  p.rows_per_wg = d.unit * ((units + slots - 1) / slots);
+  p.lanes_per_row = d.lanes;
+  const int grid = (p.H + p.rows_per_wg - 1) / p.rows_per_wg;
+  lds = d.lds_fixed + (size_t)p.topk * p.rows_per_wg * 4;
+  hipLaunchKernelGGL((single_down_kernel<DT, TPL>), dim3(grid), dim3(kSThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_single_dt(const SingleParams& p_in, hipStream_t stream) {
+  SingleParams p = p_in;
+  const int Gu = p.H / 128;
+  hipError_t e = Gu <= 32   ? launch_up<DT, 1>(p, stream)
+                 : Gu <= 64  ? launch_up<DT, 2>(p, stream)
+                 : Gu <= 128 ? launch_up<DT, 4>(p, stream)
+                             : launch_up<DT, 8>(p, stream);
+  if (e != hipSuccess) return e;
+  const DownPlan d = down_plan(p.H, p.I, p.topk);
+  return d.tpl <= 1   ? launch_down<DT, 1>(p, d, stream)
+         : d.tpl <= 2 ? launch_down<DT, 2>(p, d, stream)
+                      : launch_down<DT, 4>(p, d, stream);  // I <= 32768: at most 4 per lane
+}
+
+}  // namespace
+
+bool single_fits(int H, int I, int E, int topk) {
+  if (H % 256 || I % 256 || E < 1 || E > 256 || topk < 1 || topk > E || topk > kWave) return false;
+  if (H > 32768 || I > 32768) return false;  // at most 8 (up) and 4 (down) groups per lane
+  const DownPlan d = down_plan(H, I, topk);
+  // the most rows a down workgroup takes: one round over at least kCUs workgroups
+  const size_t units = (size_t)((H + d.unit - 1) / d.unit);
+  const size_t rows = (size_t)d.unit * ((units + kCUs - 1) / kCUs);
+  return up_lds(H) + 2048 <= kLdsPerCU && d.lds_fixed + (size_t)topk * rows * 4 + 2048 <= kLdsPerCU;
+}
+
+hipError_t launch_single(const SingleParams& p, int dtype, hipStream_t stream) {
+  if (!single_fits(p.H, p.I, p.E, p.topk)) return hipErrorInvalidValue;
+  return dtype == 0 ? launch_single_dt<0>(p, stream) : launch_single_dt<1>(p, stream);
+}
+
+}  // namespace moe

@@ -145,4 +145,31 @@ hipError_t launch_combine_rows(const void* y, int M, int topk, int H, int dtype,
 hipError_t launch_act_combine(const float* partial, int split, int slots, int I, int dtype,
                               void* inter, hipStream_t stream);
 
+// The layer for one token with uint4 g128 experts (gemv.hip), two launches.  up routes the token
+// (every workgroup for itself, the first one writing topk_w and topk_ids) and writes
+// inter[j, n] = SiLU(gate) * up for the topk slots; down writes out[n] = sum_j topk_w[j] *
+// (W2 row n of expert topk_ids[j] . inter[j]) in the activation dtype.
+struct SingleParams {
+  const void* x;              // dtype [H]
+  const float* logits;        // [E]
+  RoutingParams rp;
+  float* topk_w;              // [topk], written by up
+  int32_t* topk_ids;          // [topk], written by up
+  const uint8_t* w13;         // [E, 2I, H/2]
+  const void* s13;            // dtype [E, 2I, H/128]
+  const uint8_t* z13;         // [E, 2I, H/256]
+  const uint8_t* w2;          // [E, H, I/2]
+  const void* s2;             // dtype [E, H, I/128]
+  const uint8_t* z2;          // [E, H, I/256]
+  int E, H, I, topk;
+  void* inter;                // dtype [topk, I]
+  void* out;                  // dtype [H]
+  int upw;                    // set by launch_single
+  int lanes_per_row;          // set by launch_single
+  int rows_per_wg;            // set by launch_single
+};
+// E <= 256, topk <= E, H and I multiples of 256 up to 32768, the staged vectors within LDS
+bool single_fits(int H, int I, int E, int topk);
+hipError_t launch_single(const SingleParams& p, int dtype, hipStream_t stream);
+
 }  // namespace moe
