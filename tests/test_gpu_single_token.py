@@ -10,8 +10,8 @@ import torch
 import oracle as O
 import synth
 import weight_only_int4_topk_amd as B
-from tests.helpers import (assert_layer_close, cuda_layer, fused_vs_oracle, oracle_route,
-                           routing_of, run_fused)
+from tests.helpers import (assert_layer_close, assert_weights_close, cuda_layer, fused_vs_oracle,
+                           oracle_route, routing_of, run_fused)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,35 @@ def test_single_token_vs_oracle(name, seed):
 def test_single_token_grouped_gemm_path(name):
     """An explicit block_m keeps one token on the grouped GEMMs: both paths against the oracle."""
     fused_vs_oracle(CASES[name], 1, seed=3, block_m=16)
+
+
+ROUTINGS = [("softmax", 64, 6, 1, 1), ("softmax", 60, 4, 1, 1), ("softmax", 8, 2, 1, 1),
+            ("sigmoid", 96, 5, 6, 3), ("sigmoid", 256, 8, 8, 4), ("sigmoid", 8, 8, 1, 1),
+            ("sigmoid", 64, 32, 64, 40), ("sigmoid", 20, 3, 1, 1)]
+
+
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("score,E,k,ng,tg", ROUTINGS)
+@pytest.mark.parametrize("logits", ["normal", "ties", "neg_inf"])
+def test_single_token_routing(score, E, k, ng, tg, renorm, logits):
+    """The first launch routes the token itself: ids bit for bit and weights as the oracle's, for
+    each rule, with ties (logits on a grid of 0.5, equal values go to the lower id) and with -inf
+    logits (a quarter of the experts), and the layer output with them."""
+    wl = synth.Workload("r1", E=E, H=256, I=256, topk=k, Ms=(1,), score=score,
+                        renormalize=bool(renorm), num_groups=ng, topk_groups=tg, scale=1.5)
+    layer = synth.make_layer(wl, seed=5)
+    x = synth.make_x(wl, 1, seed=5)
+    lg = synth.make_logits(wl, 1, seed=5)
+    if logits == "ties":
+        lg = torch.round(lg * 2) / 2
+    elif logits == "neg_inf":
+        lg[0, 1::4] = -float("inf")
+    out, tw, ti = run_fused(wl, x.cuda(), lg.cuda(), cuda_layer(layer))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    assert_weights_close(tw, w_ref)
+    ref = O.moe_layer(x, ids_ref, w_ref, O.ExpertSource(layer, 4))
+    assert_layer_close(out, ref, f"one token, {score} E={E} topk={k}")
 
 
 def test_single_token_zero_activations_give_zero():

@@ -56,35 +56,47 @@ __device__ __forceinline__ int chunk_pos(int g, int r) { return 4 * (g * 16 + ((
 
 // Stage nvec activation vectors of length K (dtype, src + v * K) into LDS: sx + v * K / 2 dwords in
 // the permuted, rotated chunk layout, and ssum[v * G + g] = sum of group g of vector v (float32,
-// the 8 values of a chunk in order, then the 16 chunks of a group by a butterfly).
+// the 8 values of a chunk in order, then the 16 chunks of a group by a butterfly).  Each thread
+// issues the loads of four chunks before it stores any.
 template <int DT>
 __device__ void stage_vectors(const uint16_t* __restrict__ src, int nvec, int K,
                               uint32_t* __restrict__ sx, float* __restrict__ ssum) {
+  constexpr int kB = 4;
   const int nch = K / 8;
   const int G = K / 128;
-  const int total = nvec * nch;  // a multiple of 16: whole groups exit the loop together
-  for (int t = threadIdx.x; t < total; t += kSThreads) {
-    const int v = t / nch;
-    const int c = t - v * nch;
-    const u32x4_t raw = *(const u32x4_t*)(src + (size_t)v * K + (size_t)c * 8);
-    const uint32_t r0 = raw[0], r1 = raw[1], r2 = raw[2], r3 = raw[3];
-    const u32x4_t pv = {__builtin_amdgcn_perm(r2, r0, 0x05040100u),
-                        __builtin_amdgcn_perm(r2, r0, 0x07060302u),
-                        __builtin_amdgcn_perm(r3, r1, 0x05040100u),
-                        __builtin_amdgcn_perm(r3, r1, 0x07060302u)};
-    *(u32x4_t*)(sx + (size_t)v * (K / 2) + chunk_pos(c >> 4, c & 15)) = pv;
-    float s = 0.f;
-    const uint32_t rr[4] = {r0, r1, r2, r3};
+  const int total = nvec * nch;  // a multiple of 16: whole 16-lane groups are in or out together
+  for (int t0 = threadIdx.x; t0 < total; t0 += kB * kSThreads) {
+    u32x4_t raw[kB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s += bits_to_float<DT>((uint16_t)(rr[i] & 0xFFFFu));
-      s += bits_to_float<DT>((uint16_t)(rr[i] >> 16));
+    for (int b = 0; b < kB; ++b) {
+      const int t = t0 + b * kSThreads;
+      if (t < total) raw[b] = *(const u32x4_t*)(src + (size_t)t * 8);  // vector t / nch, chunk t % nch
     }
-    s += __shfl_xor(s, 1, 16);
-    s += __shfl_xor(s, 2, 16);
-    s += __shfl_xor(s, 4, 16);
-    s += __shfl_xor(s, 8, 16);
-    if ((c & 15) == 0) ssum[v * G + (c >> 4)] = s;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int t = t0 + b * kSThreads;
+      if (t >= total) continue;
+      const int v = t / nch;
+      const int c = t - v * nch;
+      const uint32_t r0 = raw[b][0], r1 = raw[b][1], r2 = raw[b][2], r3 = raw[b][3];
+      const u32x4_t pv = {__builtin_amdgcn_perm(r2, r0, 0x05040100u),
+                          __builtin_amdgcn_perm(r2, r0, 0x07060302u),
+                          __builtin_amdgcn_perm(r3, r1, 0x05040100u),
+                          __builtin_amdgcn_perm(r3, r1, 0x07060302u)};
+      *(u32x4_t*)(sx + (size_t)v * (K / 2) + chunk_pos(c >> 4, c & 15)) = pv;
+      float s = 0.f;
+      const uint32_t rr[4] = {r0, r1, r2, r3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s += bits_to_float<DT>((uint16_t)(rr[i] & 0xFFFFu));
+        s += bits_to_float<DT>((uint16_t)(rr[i] >> 16));
+      }
+      s += __shfl_xor(s, 1, 16);
+      s += __shfl_xor(s, 2, 16);
+      s += __shfl_xor(s, 4, 16);
+      s += __shfl_xor(s, 8, 16);
+      if ((c & 15) == 0) ssum[v * G + (c >> 4)] = s;
+    }
   }
 }
 
@@ -129,20 +141,179 @@ __device__ __forceinline__ void group_terms(uint32_t sbits, uint32_t zbyte, int 
   off = magicv + c * (float)((zbyte >> ((g & 1) * 4)) & 0xFu);
 }
 
+// The token's routing by the whole workgroup (E <= 256, topk <= 32): the same selection and
+// weights as route_token, without its topk rounds of a wave-wide arg-best.  Every candidate gets
+// a 64-bit key, its score mapped to an unsigned integer of the same order above its complemented
+// id, so that key order is route_token's order (larger score first, equal scores to the lower
+// id) and all keys differ; ineligible candidates (experts of dropped groups, NaN scores) get key
+// 0, below every other.  A candidate's place is the number of larger keys: first within its
+// wavefront's 64 candidates, then, for the topk best of each wavefront (which hold every
+// candidate of the overall top-k), among those.  `v` is the thread's logit (threads t < E).
+// Leaves the ids in wid[0, topk) (0x7fffffff where fewer candidates are eligible) and returns
+// the weight of place t to the threads t < topk.  Ends with a barrier.
+struct __attribute__((aligned(16))) RouteLds {
+  uint64_t key[256];
+  uint64_t surv[4 * 32];  // the topk best keys of each wavefront (0: none)
+  float gsc[64];
+  float val[256];
+  int wid[32];
+  float wval[32];
+};
+
+__device__ __forceinline__ uint64_t route_key(float v, int t) {
+  const uint32_t b = __float_as_uint(v + 0.0f);  // -0 -> +0: equal scores stay equal
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)t);
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ float route_single(float v, int E, int topk, const RoutingParams& rp, RouteLds& r) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const float kNone = -__builtin_inff();
+  if (rp.score == 1 && t < E) v = sigmoid_spec(v);
+  if (t < 256) r.val[t] = t < E ? v : 0.0f;  // the scores (softmax without renormalisation)
+  if (t < 4 * 32) r.surv[t] = 0;
+  if (t < topk) {
+    r.wid[t] = 0x7fffffff;
+    r.wval[t] = kNone;
+  }
+  bool elig = t < E && v == v;
+  const int ng = rp.num_groups;
+  if (rp.score == 1 && rp.topk_groups < ng) {
+    // group score: sum of the two largest scores of the group's contiguous experts
+    const int gs = E / ng;
+    if ((gs & (gs - 1)) == 0 && gs <= kWave) {
+      // groups of a power of two lanes: top-2 merges across the group's lanes (DPP within rows of
+      // 16, then row and half swaps), every lane of the group ends with the pair
+      float t1 = t < E ? v : kNone, t2 = kNone;
+      if (gs >= 2) top2_step<kDppXor1>(t1, t2);
+      if (gs >= 4) top2_step<kDppXor2>(t1, t2);
+      if (gs >= 8) top2_step<kDppHalfMirror>(t1, t2);
+      if (gs >= 16) top2_step<kDppMirror>(t1, t2);
+      if (gs >= 32) {
+        uint32_t a1, b1, a2, b2;
+        swap_pair<false>(__float_as_uint(t1), a1, b1);
+        swap_pair<false>(__float_as_uint(t2), a2, b2);
+        t1 = __uint_as_float(a1);
+        t2 = __uint_as_float(a2);
+        top2_merge(t1, t2, __uint_as_float(b1), __uint_as_float(b2));
+      }
+      if (gs >= 64) {
+        uint32_t a1, b1, a2, b2;
+        swap_pair<true>(__float_as_uint(t1), a1, b1);
+        swap_pair<true>(__float_as_uint(t2), a2, b2);
+        t1 = __uint_as_float(a1);
+        t2 = __uint_as_float(a2);
+        top2_merge(t1, t2, __uint_as_float(b1), __uint_as_float(b2));
+      }
+      if (t < E && t % gs == 0) r.gsc[t / gs] = gs >= 2 ? t1 + t2 : t1;
+      __syncthreads();
+    } else {
+      __syncthreads();  // the scores in val
+      if (t < ng) {
+        float b1 = kNone, b2 = kNone;
+        for (int i = 0; i < gs; ++i) {
+          const float x = r.val[t * gs + i];
+          if (x > b1) {
+            b2 = b1;
+            b1 = x;
+          } else if (x > b2) {
+            b2 = x;
+          }
+        }
+        r.gsc[t] = gs >= 2 ? b1 + b2 : b1;
+      }
+      __syncthreads();
+    }
+    // keep the topk_groups best groups (ties -> lower group id); each thread ranks its own group
+    if (t < E) {
+      const int g = t / gs;
+      const float mine = r.gsc[g];
+      int rank = 0;
+#pragma unroll 8
+      for (int o = 0; o < ng; ++o) rank += (o != g && better(r.gsc[o], o, mine, g)) ? 1 : 0;
+      if (rank >= rp.topk_groups) elig = false;
+    }
+  }
+  const uint64_t key = elig ? route_key(v, t) : 0ull;
+  if (t < 256) r.key[t] = key;
+  __syncthreads();
+  // place within the wavefront's 64 candidates (waves past E hold key 0 only)
+  if (elig) {
+    const uint64_t* kw = r.key + wave * kWave;
+    int c0 = 0, c1 = 0;
+#pragma unroll 8
+    for (int u = 0; u < kWave; u += 2) {
+      c0 += kw[u] > key ? 1 : 0;
+      c1 += kw[u + 1] > key ? 1 : 0;
+    }
+    const int lr = c0 + c1;
+    if (lr < topk) r.surv[wave * topk + lr] = key;
+  }
+  __syncthreads();
+  // place among the survivors
+  const int ns = ((E + kWave - 1) / kWave) * topk;
+  if (t < ns) {
+    const uint64_t k = r.surv[t];
+    if (k != 0) {
+      int c0 = 0, c1 = 0;
+      int u = 0;
+      for (; u + 1 < ns; u += 2) {
+        c0 += r.surv[u] > k ? 1 : 0;
+        c1 += r.surv[u + 1] > k ? 1 : 0;
+      }
+      if (u < ns) c0 += r.surv[u] > k ? 1 : 0;
+      const int rank = c0 + c1;
+      if (rank < topk) {
+        r.wid[rank] = (int)(0xFFFFFFFFu - (uint32_t)k);
+        r.wval[rank] = key_value(k);
+      }
+    }
+  }
+  __syncthreads();
+  if (t >= kWave) return 0.0f;
+  // weights, in route_token's order of operations
+  float denom = 0.0f, my = 0.0f;
+  if (rp.score == 0) {
+    const float mx = r.wval[0];
+    for (int j = 0; j < topk; ++j) {
+      const float ej = expf(r.wval[j] - mx);
+      denom += ej;
+      if (j == lane) my = ej;
+    }
+    if (!rp.renormalize) {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + kWave * i < E) part += expf(r.val[lane + kWave * i] - mx);
+      denom = wave_sum(part);
+    }
+  } else {
+    for (int j = 0; j < topk; ++j) {
+      denom += r.wval[j];
+      if (j == lane) my = r.wval[j];
+    }
+    if (!rp.renormalize) denom = 1.0f;
+  }
+  return my / denom * rp.scale;
+}
+
 // ------------------------------------------------------------------------------------------------
-// up: wavefront 0 routes the token while the others start staging x; then one unit = (slot j,
-// output column n) per step group: lanes 0-31 the gate row n, lanes 32-63 the up row I + n, lane
-// l % 32 the groups l % 32 + 32 i, i < GPL.  A wavefront runs upw consecutive units in steps of at
-// most two groups per lane (P steps per unit), the weights of the next step in flight while it
-// computes one; the first step is issued before the activations are staged.
+// up: the workgroup routes the token and stages x; then one unit = (slot j, output column n):
+// lanes 0-31 the gate row n, lanes 32-63 the up row I + n, lane l % 32 the groups l % 32 + 32 i,
+// i < GPL.  A wavefront runs upw consecutive units in steps of at most two groups per lane (P steps
+// per unit), the weights of the next step in flight while it computes one.
 // ------------------------------------------------------------------------------------------------
 template <int DT, int GPL>
 __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
   extern __shared__ uint32_t s_dyn[];
-  __shared__ float s_route[4 * kWave];
-  __shared__ float s_w_sink[kWave];
-  __shared__ int32_t s_id_sink[kWave];
-  __shared__ int32_t s_ids[kWave];
+  __shared__ RouteLds s_route;
   const int K = p.H, I = p.I;
   const int G = K / 128;
   uint32_t* sx = s_dyn;
@@ -164,13 +335,14 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
   constexpr uint32_t magic = DT == 0 ? 0x64006400u : 0x43004300u;
   const int u0 = (blockIdx.x * kSWaves + wave) * p.upw;
 
-  if (wave == 0) {
-    // every workgroup routes the token (a few hundred logits); the first one publishes the result
-    const bool pub = blockIdx.x == 0;
-    route_token<4>(p.logits, p.E, p.topk, p.rp, s_route, pub ? p.topk_w : s_w_sink,
-                   pub ? p.topk_ids : s_id_sink, s_ids);
+  // every workgroup routes the token; the first one publishes the result
+  const float logit = (int)threadIdx.x < p.E ? p.logits[threadIdx.x] : 0.0f;
+  const float wgt = route_single(logit, p.E, p.topk, p.rp, s_route);
+  const int* s_ids = s_route.wid;
+  if (blockIdx.x == 0 && (int)threadIdx.x < p.topk) {
+    p.topk_ids[threadIdx.x] = s_ids[threadIdx.x];
+    p.topk_w[threadIdx.x] = wgt;
   }
-  __syncthreads();
 
   u32x4_t wq[2][CH][4];
   uint32_t sq[2][CH], zq[2][CH];
@@ -379,9 +551,10 @@ int occupancy_of(F kernel) {
     n = 1;
   return n;
 }
-// ... and by its LDS as well (`lds` dynamic bytes plus at most 2 KiB of static arrays)
+// ... and by its LDS as well (`lds` dynamic bytes plus the static arrays)
+constexpr size_t kStaticLds = sizeof(RouteLds);
 int resident_per_cu(int by_regs, size_t lds) {
-  return std::max(1, std::min(by_regs, (int)(kLdsPerCU / (lds + 2048))));
+  return std::max(1, std::min(by_regs, (int)(kLdsPerCU / (lds + kStaticLds))));
 }
 
 // Launch shape of the down kernel: L lanes per row (a power of two covering the row's groups in at
@@ -458,7 +631,7 @@ bool single_fits(int H, int I, int E, int topk) {
   // the most rows a down workgroup takes: one round over at least kCUs workgroups
   const size_t units = (size_t)((H + d.unit - 1) / d.unit);
   const size_t rows = (size_t)d.unit * ((units + kCUs - 1) / kCUs);
-  return up_lds(H) + 2048 <= kLdsPerCU && d.lds_fixed + (size_t)topk * rows * 4 + 2048 <= kLdsPerCU;
+  return up_lds(H) + kStaticLds <= kLdsPerCU && d.lds_fixed + (size_t)topk * rows * 4 <= kLdsPerCU;
 }
 
 hipError_t launch_single(const SingleParams& p, int dtype, hipStream_t stream) {
