@@ -51,6 +51,26 @@ __device__ __forceinline__ uint32_t and_or_s(uint32_t a, uint32_t m, uint32_t c)
   return __builtin_amdgcn_bitop3_b32(a, m, c, 0xEA);  // (a & m) | c
 }
 
+// Sum over aligned groups of L lanes (L a power of two <= 64) in a fixed order, in registers: DPP
+// inside rows of 16, then row and half swaps; every lane of a group returns the group's sum.
+__device__ __forceinline__ float lane_group_sum(float v, int L) {
+  if (L >= 2) v += dpp_f<kDppXor1>(v);
+  if (L >= 4) v += dpp_f<kDppXor2>(v);
+  if (L >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (L >= 16) v += dpp_f<kDppMirror>(v);
+  if (L >= 32) {
+    uint32_t a, b;
+    swap_pair<false>(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+  }
+  if (L >= 64) {
+    uint32_t a, b;
+    swap_pair<true>(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+  }
+  return v;
+}
+
 // LDS dword offset of 8-k chunk c of a staged vector: chunk r of group g sits at slot (r + g) % 16
 __device__ __forceinline__ int chunk_pos(int g, int r) { return 4 * (g * 16 + ((r + g) & 15)); }
 
@@ -91,10 +111,7 @@ __device__ void stage_vectors(const uint16_t* __restrict__ src, int nvec, int K,
         s += bits_to_float<DT>((uint16_t)(rr[i] & 0xFFFFu));
         s += bits_to_float<DT>((uint16_t)(rr[i] >> 16));
       }
-      s += __shfl_xor(s, 1, 16);
-      s += __shfl_xor(s, 2, 16);
-      s += __shfl_xor(s, 4, 16);
-      s += __shfl_xor(s, 8, 16);
+      s = lane_group_sum(s, 16);  // the 16 chunks of a group sit in one row of 16 lanes
       if ((c & 15) == 0) ssum[v * G + (c >> 4)] = s;
     }
   }
@@ -352,20 +369,20 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
     const int n = u - j * I;
     int e = s_ids[j];
     e = (unsigned)e < (unsigned)p.E ? e : 0;  // no id (NaN logits): rows of expert 0, unused
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.w13 + (size_t)e * N * row_bytes), (short)0, (int)(N * row_bytes), kRsrcS);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const uint8_t*)p.s13 + (size_t)e * N * srow), (short)0, (int)(N * srow), kRsrcS);
     const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.z13 + (size_t)e * N * zrow), (short)0, (int)(N * zrow), kRsrcS);
     const uint32_t row = (uint32_t)(h ? I + n : n);
+    // the weights through plain global loads: for this pattern (32 lanes x 64 bytes per row, two
+    // rows per instruction) they stream faster than buffer loads (Mixtral shape 32.2 -> 29.4 us);
+    // every address is inside expert e's rows
+    const uint8_t* wrow = p.w13 + (size_t)e * N * row_bytes + (size_t)row * row_bytes;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int g = min(l32 + 32 * (part * CH + i), G - 1);  // past the row's groups: its last one
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        wq[slot][i][q] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, row * row_bytes + g * 64 + q * 16, 0, 0));
+      for (int q = 0; q < 4; ++q) wq[slot][i][q] = *(const u32x4_t*)(wrow + g * 64 + q * 16);
       sq[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
       zq[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
     }
@@ -383,14 +400,10 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
       }
     }
     if (part != P - 1) return;
-    // sum over the 32 lanes of each half (fixed order), then gate (lane 0) and up (lane 32)
-    acc += __shfl_xor(acc, 1, 32);
-    acc += __shfl_xor(acc, 2, 32);
-    acc += __shfl_xor(acc, 4, 32);
-    acc += __shfl_xor(acc, 8, 32);
-    acc += __shfl_xor(acc, 16, 32);
-    const float gate = __shfl(acc, 0, kWave);
-    const float up = __shfl(acc, 32, kWave);
+    // sum over the 32 lanes of each half, then gate (lane 0) and up (lane 32)
+    acc = lane_group_sum(acc, 32);
+    const float gate = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0));
+    const float up = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32));
     const int u = u0 + k;
     if (lane == 0 && u < U) {
       const float v = gate / (1.0f + __expf(-gate)) * up;
@@ -501,7 +514,7 @@ __global__ void __launch_bounds__(kSThreads) single_down_kernel(SingleParams p) 
       }
     }
     if (gp != P - 1) return;
-    for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m, L);
+    acc = lane_group_sum(acc, L);
     const int r = part * RPW + ps * RPP + rsub;  // row within the workgroup
     if (sub == 0) spart[j * RW + r] = valid ? wj * acc : 0.0f;
     acc = 0.f;
