@@ -197,7 +197,8 @@ SMALL = {
     "all_experts": synth.Workload("ae", E=4, H=256, I=256, topk=4, Ms=(21,)),
     # few workgroups: the first GEMM is split over K (14 k-blocks into 2 x 7, the second split
     # starting on an odd k-block) and SiLU(gate) * up runs after the float32 partials are summed
-    "split_odd_start": synth.Workload("so", E=8, H=1792, I=768, topk=2, Ms=(3,)),
+    # (BLOCK_M 16 given: with the library's choice three tokens take the few-token path)
+    "split_odd_start": synth.Workload("so", E=8, H=1792, I=768, topk=2, Ms=(3,), block_m=16),
     # BLOCK_M 64 (scales and zero points through the two-slot ring): zero-point rows of an odd
     # number of bytes (K / 256 = 7 and 5, so rows start on odd bytes and the 2-byte words the
     # kernel reads straddle rows), and the second GEMM split over K into 2 x 5 k-blocks, the second
@@ -307,22 +308,24 @@ def test_fused_empty_batch():
 # ------------------------------------------------------------------------------------------------
 # full-size layers (drawn on the GPU), sampled tokens against the oracle
 # ------------------------------------------------------------------------------------------------
-# Every M of the Mixtral-, Qwen2- and DeepSeek-V3 TP-share workloads, so each tile plan the library
-# picks at full size runs once: BLOCK_M 16/32/64, the first GEMM unsplit, split to ~512 workgroups
-# (DeepSeek-V3 TP share at M=1) and split towards one round (TP share at M=16 and 64, Qwen2 shape
-# at M=1), 8-wavefront workgroups.  Every token against the oracle; align of the full routing
-# result at the BLOCK_M the layer ran.
-FULL = [("mixtral", 64), ("mixtral", 16), ("mixtral", 4), ("mixtral", 1), ("qwen2", 512),
-        ("qwen2", 128), ("qwen2", 16), ("qwen2", 1), ("dsv3_tp8", 256), ("dsv3_tp8", 64),
-        ("dsv3_tp8", 16), ("dsv3_tp8", 1)]
+# Every M of the Mixtral-, Qwen2- and DeepSeek-V3 TP-share workloads, so each plan the library
+# picks at full size runs once: one token on the dot-product path, a few tokens of the TP share on
+# the grouped dot-product path, and the grouped GEMMs with BLOCK_M 16/32/64, the first GEMM
+# unsplit, split to ~512 workgroups and split towards one round, 8-wavefront workgroups; the
+# grouped GEMMs also at the sizes the dot-product paths take (BLOCK_M 16 given).  Every token
+# against the oracle; align of the full routing result at the BLOCK_M the grouped GEMMs ran.
+FULL = [("mixtral", 64, 0), ("mixtral", 16, 0), ("mixtral", 4, 0), ("mixtral", 1, 0),
+        ("mixtral", 1, 16), ("qwen2", 512, 0), ("qwen2", 128, 0), ("qwen2", 16, 0), ("qwen2", 1, 0),
+        ("qwen2", 1, 16), ("dsv3_tp8", 256, 0), ("dsv3_tp8", 64, 0), ("dsv3_tp8", 16, 0),
+        ("dsv3_tp8", 16, 16), ("dsv3_tp8", 4, 0), ("dsv3_tp8", 1, 0), ("dsv3_tp8", 1, 16)]
 
 
-@pytest.mark.parametrize("name,M", FULL)
-def test_fused_full_size_all_tokens(name, M):
+@pytest.mark.parametrize("name,M,bm", FULL)
+def test_fused_full_size_all_tokens(name, M, bm):
     wl = W[name]
-    print(f"full size {name} M={M}", flush=True)
-    out, ids, rel = fused_vs_oracle(wl, M, seed=0, device="cuda")
-    assert_align_exact(ids, wl.E, B.moe_pick_block_m(M, wl.E, wl.topk, wl.bits, wl.torch_dtype))
+    print(f"full size {name} M={M} block_m={bm}", flush=True)
+    out, ids, rel = fused_vs_oracle(wl, M, seed=0, device="cuda", block_m=bm)
+    assert_align_exact(ids, wl.E, bm or B.moe_pick_block_m(M, wl.E, wl.topk, wl.bits, wl.torch_dtype))
 
 
 @pytest.mark.parametrize("name", ["dsv3_prefill_int4", "dsv3_prefill_int8"])

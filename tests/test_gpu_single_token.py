@@ -1,8 +1,10 @@
-"""The layer for one token (M = 1, uint4, block_m left to the library): routing, then one dot
-product per weight row in two launches (SiLU(gate) * up; the second product with the top-k
-combine).  Against the oracle, every element, with the tolerance of the other layer tests; the
-shapes cover each groups-per-lane variant of both launches, quantisation groups that do not fill a
-wavefront, and the fallback to the grouped GEMMs where the staged activations exceed LDS."""
+"""The dot-product paths of the layer (uint4, block_m left to the library).  One token: one dot
+product per weight row in two launches (routing inside the first, SiLU(gate) * up; the second
+product with the top-k combine).  A few tokens (2 to 4, I <= 512): routing, then the same two
+launches with the slots grouped by expert in every workgroup.  Against the oracle, every element, with the tolerance of the
+other layer tests; the shapes cover each groups-per-lane variant of the launches, quantisation
+groups that do not fill a wavefront, one expert taking every token, and the fallback to the grouped
+GEMMs where the staged activations exceed LDS."""
 import numpy as np
 import pytest
 import torch
@@ -119,6 +121,81 @@ def test_single_token_deterministic_and_graph_replay():
     out2, _, _ = run_fused(wl, x, lg, layer)
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     ws = torch.empty((B.fused_moe_wna16_workspace_size(1, wl.H, wl.I, wl.E, wl.topk, B.QUANT_INT4,
+                                                       wl.torch_dtype, 0),), dtype=torch.uint8,
+                     device="cuda")
+    gout = torch.empty_like(out1)
+    run = lambda: B.fused_moe_wna16(x, lg, wl.topk, routing_of(wl), layer["w13"],
+                                    layer["w13_scales"], layer["w13_zeros"], layer["w2"],
+                                    layer["w2_scales"], layer["w2_zeros"], block_m=0,
+                                    workspace=ws, out=gout)
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        gout.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gout.view(torch.int16), out1.view(torch.int16)), f"replay {i}"
+        run_fused(wl, x, lg, layer)  # eager work between replays
+
+
+# ------------------------------------------------------------------------------------------------
+# a few tokens
+# ------------------------------------------------------------------------------------------------
+FEW = {
+    # many experts, narrow I (a tensor-parallel share): 32 slots over 64 experts
+    "tp_like_fp16": synth.Workload("f1", E=64, H=1024, I=256, topk=8, Ms=(4,), score="sigmoid",
+                                   num_groups=8, topk_groups=4, scale=2.5),
+    "tp_like_bf16": synth.Workload("f2", E=64, H=1024, I=256, topk=8, Ms=(3,), dtype="bf16",
+                                   score="sigmoid", num_groups=8, topk_groups=4, scale=2.5),
+    # 14 groups per first-launch row (half the lanes of each half-wavefront idle), two slots each
+    "softmax_top2": synth.Workload("f3", E=8, H=1792, I=512, topk=2, Ms=(2,)),
+    # 48 groups per first-launch row: the whole wavefront on one row at a time
+    "wide_h_bf16": synth.Workload("f4", E=16, H=6144, I=512, topk=4, Ms=(4,), dtype="bf16"),
+    # 64 groups per first-launch row, two second-launch groups per row
+    "widest_h": synth.Workload("f5", E=16, H=8192, I=256, topk=4, Ms=(3,)),
+    # 128 slots: top-32 of 64 experts for 4 tokens
+    "many_slots": synth.Workload("f7", E=64, H=512, I=256, topk=32, Ms=(4,), dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FEW))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_few_tokens_vs_oracle(name, seed):
+    wl = FEW[name]
+    print(f"few tokens {name} M={wl.Ms[0]} seed={seed}", flush=True)
+    fused_vs_oracle(wl, wl.Ms[0], seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_few_tokens_hot_expert(dtype):
+    """Every token's first choice is expert 3: one expert's rows meet all four tokens' rows (the
+    most a workgroup stages) in both launches."""
+    wl = synth.Workload("fh", E=32, H=1024, I=512, topk=2, Ms=(4,), dtype=dtype)
+    layer = synth.make_layer(wl, seed=8)
+    x = synth.make_x(wl, 4, seed=8)
+    lg = synth.make_logits(wl, 4, seed=8)
+    lg[:, 3] += 50.0
+    out, tw, ti = run_fused(wl, x.cuda(), lg.cuda(), cuda_layer(layer))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert (ids_ref[:, 0] == 3).all()
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    ref = O.moe_layer(x, ids_ref, w_ref, O.ExpertSource(layer, 4))
+    assert_layer_close(out, ref, f"few tokens, hot expert, {dtype}")
+
+
+def test_few_tokens_deterministic_and_graph_replay():
+    wl = FEW["tp_like_fp16"]
+    M = 4
+    layer = cuda_layer(synth.make_layer(wl, seed=1))
+    x = synth.make_x(wl, M, seed=1).cuda()
+    lg = synth.make_logits(wl, M, seed=1).cuda()
+    out1, _, _ = run_fused(wl, x, lg, layer)
+    out2, _, _ = run_fused(wl, x, lg, layer)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    ws = torch.empty((B.fused_moe_wna16_workspace_size(M, wl.H, wl.I, wl.E, wl.topk, B.QUANT_INT4,
                                                        wl.torch_dtype, 0),), dtype=torch.uint8,
                      device="cuda")
     gout = torch.empty_like(out1)

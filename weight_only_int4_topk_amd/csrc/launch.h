@@ -164,12 +164,18 @@ struct SingleParams {
   int E, H, I, topk;
   void* inter;                // dtype [topk, I]
   void* out;                  // dtype [H]
-  int upw;                    // set by launch_single
-  int lanes_per_row;          // set by launch_single
-  int rows_per_wg;            // set by launch_single
+  int upw;                    // set by launch_single / launch_few
+  int lanes_per_row;          // set by launch_single / launch_few
+  int rows_per_wg;            // set by launch_single / launch_few
+  int M;                      // launch_few: tokens (x is [M, H], out [M, H], inter [M * topk, I])
 };
 // E <= 256, topk <= E, H and I multiples of 256 up to 32768, the staged vectors within LDS
 bool single_fits(int H, int I, int E, int topk);
 hipError_t launch_single(const SingleParams& p, int dtype, hipStream_t stream);
+// The layer for a few tokens (2 <= M <= 8, M * topk <= 256, H and I <= 8192) after routing
+// (topk_w / topk_ids [M, topk] given): up and down as above, each workgroup grouping the slots by
+// expert so that every distinct expert's rows are read once for all its slots.
+bool few_fits(int M, int H, int I, int E, int topk);
+hipError_t launch_few(const SingleParams& p, int dtype, hipStream_t stream);
 
 }  // namespace moe
