@@ -2,7 +2,9 @@
 """Throughput of the fused MoE layer with uint4/int8 experts on one MI355X; prints one JSON line.
 
 A step is one call of the whole layer (routing, align, w13 grouped GEMM + SiLU*up, w2 grouped GEMM,
-weighted combine) on one batch of M tokens whose inputs are already in HBM.  `value` is tokens/s
+weighted combine) on one batch of M tokens whose inputs are already in HBM.  (One token, and two to
+four tokens of the DeepSeek-V3 TP share, take the layer's dot-product paths instead: `layer_path`
+in each workload row; their `w13_*` fields still time the grouped w13 GEMM alone.)  `value` is tokens/s
 over exactly --steps steps of the Mixtral-shaped layer at M = 64, replayed as one HIP graph that
 holds exactly --steps layer calls (after one graph of --warmup calls).  The layer exists in L device
 copies that the calls cycle through, as a model's layer stack would, so that the experts a call
@@ -218,7 +220,7 @@ class Bench:
         return finish if defer else finish()
 
     def _result(self, M, bm, active, L, G, t_layer, t_g1, steps, act_bytes, w13_bytes):
-        wl = self.wl
+        wl, B = self.wl, self.B
         us_layer = t_layer / steps * 1e6
         us_g1 = t_g1 / steps * 1e6
         flops_layer = 6.0 * wl.H * wl.I * M * wl.topk
@@ -227,8 +229,12 @@ class Bench:
         # 8 TB/s) and its MFMA floor (6 H I M k flops at 2.5 PFLOP/s)
         t_hbm = act_bytes / (HBM_PEAK_GBPS * 1e9)
         t_mfma = flops_layer / (MFMA_PEAK_TFLOPS * 1e12)
+        path = {B.PATH_GROUPED: "grouped GEMMs", B.PATH_ONE_TOKEN: "one-token dot products",
+                B.PATH_FEW_TOKENS: "few-token dot products"}[
+            B.fused_moe_wna16_path(M, wl.H, wl.I, wl.E, wl.topk, wl.bits)]
         res = dict(
-            M=M, block_m=bm, active_experts=active, layer_copies=L, graph_calls=G,
+            M=M, layer_path=path, block_m=bm, active_experts=active, layer_copies=L,
+            graph_calls=G,
             us_per_layer=round(us_layer, 2), tokens_per_s=round(M / (us_layer * 1e-6), 1),
             layer_GBps=round(act_bytes / (us_layer * 1e-6) / 1e9, 1),
             layer_hbm_frac=round(t_hbm / (us_layer * 1e-6), 4),

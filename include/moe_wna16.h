@@ -312,10 +312,16 @@ size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, cons
  *   out           device dtype [M, H]
  *   topk_weights_out / topk_ids_out: optional device [M, topk] copies of the routing result
  *   block_m       0 = library's choice, else one of {16, 32, 64, 128, 256}
- * Launches: routing and align (one launch for M <= 4), GEMM1 (+SiLU*up; split over K into float32
- * partials and a SiLU*up pass when its workgroups would not fill the chip), GEMM2 (split over K into
- * float32 partials at small M; unsplit with block_m 64, it writes dtype rows times the routing
- * weight), combine (float32 sums in a fixed order).  Deterministic: identical inputs give bitwise identical outputs.
+ * Launches, by the path fused_moe_wna16_path names:
+ *   MOE_PATH_GROUPED: routing and align (one launch for M <= 4), GEMM1 (+SiLU*up; split over K
+ *     into float32 partials and a SiLU*up pass when its workgroups would not fill the chip), GEMM2
+ *     (split over K into float32 partials at small M; unsplit with block_m 64, it writes dtype rows
+ *     times the routing weight), combine (float32 sums in a fixed order);
+ *   MOE_PATH_ONE_TOKEN: two launches of one dot product per weight row (the routing inside the
+ *     first, SiLU*up; the top-k combine inside the second);
+ *   MOE_PATH_FEW_TOKENS: routing, then the same two launches, each workgroup grouping the slots by
+ *     expert so that each distinct expert's rows are read once for all its slots.
+ * Deterministic: identical inputs give bitwise identical outputs.
  * Limits: those of the calls above with N = 2I and N = H; H % 256 == 0, I % 256 == 0,
  * M * topk <= 2^24, and below 2^31 bytes (32-bit offsets): x (M * H * 2), the intermediate rows
  * (M * topk * I * 2) and one expert's w13. */
@@ -325,6 +331,21 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
                     const void* w2_zeros, const moe_quant_t* quant, int dtype, int block_m,
                     void* workspace, size_t workspace_bytes, void* out, float* topk_weights_out,
                     int32_t* topk_ids_out, void* stream);
+
+/* The launch sequence fused_moe_wna16 takes for these sizes (act_order: the act-order entry point),
+ * decided from the sizes alone:
+ *   MOE_PATH_ONE_TOKEN  M = 1, uint4, block_m 0, E <= 256, the staged vectors within LDS
+ *                       (topk * I up to about 60 K columns);
+ *   MOE_PATH_FEW_TOKENS 2 <= M <= 4, uint4, block_m 0, I <= 512, H <= 8192, M * topk <= 256 (on the
+ *                       DeepSeek-V3 tensor-parallel share it measured 12 to 25 % faster than the
+ *                       grouped GEMMs; slower with wider I or more tokens);
+ *   MOE_PATH_GROUPED    otherwise.
+ * Returns -1 for sizes fused_moe_wna16 rejects. */
+#define MOE_PATH_GROUPED 0
+#define MOE_PATH_ONE_TOKEN 1
+#define MOE_PATH_FEW_TOKENS 2
+int fused_moe_wna16_path(int M, int H, int I, int E, int topk, const moe_quant_t* quant,
+                         int block_m, int act_order);
 
 /* Bytes of the static device scratch that fused_moe_wna16_noalloc uses as its workspace. */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

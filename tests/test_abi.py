@@ -88,6 +88,33 @@ def test_pick_block_m(lib):
     assert lib.moe_pick_block_m(16, 8, 2, 4, 2) == -1
 
 
+def test_layer_path():
+    """The launch sequence of the fused layer, decided from the sizes alone."""
+    path = B.fused_moe_wna16_path
+    one, few, grouped = B.PATH_ONE_TOKEN, B.PATH_FEW_TOKENS, B.PATH_GROUPED
+    assert path(1, 4096, 14336, 8, 2) == one              # Mixtral shape
+    assert path(1, 3584, 2560, 64, 8) == one              # Qwen2 shape
+    assert path(1, 7168, 256, 256, 8) == one              # DeepSeek-V3 TP share
+    assert path(1, 7168, 2048, 256, 8) == one             # DeepSeek-V3 all experts
+    assert path(2, 7168, 256, 256, 8) == few
+    assert path(4, 7168, 256, 256, 8) == few
+    assert path(5, 7168, 256, 256, 8) == grouped          # more tokens
+    assert path(16, 7168, 256, 256, 8) == grouped
+    assert path(2, 4096, 14336, 8, 2) == grouped          # wider I
+    assert path(2, 3584, 2560, 64, 8) == grouped
+    assert path(4, 16384, 256, 64, 8) == grouped          # H past 8192
+    assert path(1, 4096, 14336, 8, 2, block_m=16) == grouped
+    assert path(1, 4096, 14336, 8, 2, bits=8) == grouped
+    assert path(1, 4096, 14336, 8, 2, act_order=True) == grouped
+    assert path(1, 4096, 1024, 512, 8) == grouped         # E past 256
+    assert path(1, 256, 32768, 4, 4) == grouped           # staged rows past LDS
+    assert path(1, 256, 32768, 2, 2) == one
+    assert path(0, 4096, 14336, 8, 2) == -1
+    assert path(1, 100, 14336, 8, 2) == -1
+    assert path(1, 4096, 14336, 8, 9) == -1               # topk > E
+    assert path(1, 4096, 14336, 8, 2, block_m=48) == -1
+
+
 def test_align_capacity_formula(lib):
     assert lib.moe_align_capacity(8, 4, 4) == 20      # hand-worked fixture
     assert lib.moe_align_capacity(8, 5, 2) == 13

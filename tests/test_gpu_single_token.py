@@ -47,8 +47,11 @@ CASES = {
 @pytest.mark.parametrize("name", sorted(CASES))
 @pytest.mark.parametrize("seed", [0, 1])
 def test_single_token_vs_oracle(name, seed):
+    wl = CASES[name]
+    want = B.PATH_GROUPED if name == "widest_i_fallback" else B.PATH_ONE_TOKEN
+    assert B.fused_moe_wna16_path(1, wl.H, wl.I, wl.E, wl.topk) == want
     print(f"single token {name} seed={seed}", flush=True)
-    fused_vs_oracle(CASES[name], 1, seed=seed)
+    fused_vs_oracle(wl, 1, seed=seed)
 
 
 @pytest.mark.parametrize("name", ["tiny_fp16", "sigmoid_groups_bf16", "odd_groups_fp16"])
@@ -165,6 +168,7 @@ FEW = {
 @pytest.mark.parametrize("seed", [0, 1])
 def test_few_tokens_vs_oracle(name, seed):
     wl = FEW[name]
+    assert B.fused_moe_wna16_path(wl.Ms[0], wl.H, wl.I, wl.E, wl.topk) == B.PATH_FEW_TOKENS
     print(f"few tokens {name} M={wl.Ms[0]} seed={seed}", flush=True)
     fused_vs_oracle(wl, wl.Ms[0], seed=seed)
 
@@ -174,6 +178,7 @@ def test_few_tokens_hot_expert(dtype):
     """Every token's first choice is expert 3: one expert's rows meet all four tokens' rows (the
     most a workgroup stages) in both launches."""
     wl = synth.Workload("fh", E=32, H=1024, I=512, topk=2, Ms=(4,), dtype=dtype)
+    assert B.fused_moe_wna16_path(4, wl.H, wl.I, wl.E, wl.topk) == B.PATH_FEW_TOKENS
     layer = synth.make_layer(wl, seed=8)
     x = synth.make_x(wl, 4, seed=8)
     lg = synth.make_logits(wl, 4, seed=8)

@@ -19,7 +19,7 @@ __all__ = [
     "moe_wna16_batched_gemm", "moe_quant_int8_rows", "moe_w8a8_gemm", "fused_moe_w8a8",
     "fused_moe_wna16_act_order", "fused_moe_wna16_workspace_size", "fused_moe_wna16",
     "fused_moe_wna16_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_repack_uint4", "FORMAT_GPTQ",
-    "FORMAT_AWQ",
+    "FORMAT_AWQ", "fused_moe_wna16_path", "PATH_GROUPED", "PATH_ONE_TOKEN", "PATH_FEW_TOKENS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_wna16.so")
@@ -53,6 +53,7 @@ _SIGS = {
     "moe_topk_softmax": ([_P, _I, _I, _I, ctypes.POINTER(MoeRouting), _P, _P, _P], _I),
     "moe_align_capacity": ([_I, _I, _I], _I64),
     "moe_pick_block_m": ([_I, _I, _I, _I, _I], _I),
+    "fused_moe_wna16_path": ([_I, _I, _I, _I, _I, ctypes.POINTER(MoeQuant), _I, _I], _I),
     "moe_align_block_size": ([_P, _I, _I, _I, _P, _P, _P, _I64, _P], _I),
     "moe_wna16_gemm": ([_P, _I, _I, _P, _P, _P, ctypes.POINTER(MoeQuant), _I, _I, _I, _I,
                         _P, _P, _P, _I64, _I, _I, _P, _I, _P, _P], _I),
@@ -195,6 +196,16 @@ def moe_topk_softmax(logits, topk, rt: MoeRouting, topk_weights=None, topk_ids=N
     _check(lib().moe_topk_softmax(_ptr(logits), M, E, topk, ctypes.byref(rt), _ptr(topk_weights),
                                   _ptr(topk_ids), _stream(stream)))
     return topk_weights, topk_ids
+
+
+PATH_GROUPED, PATH_ONE_TOKEN, PATH_FEW_TOKENS = 0, 1, 2
+
+
+def fused_moe_wna16_path(M, H, I, E, topk, bits=4, block_m=0, act_order=False) -> int:
+    """The launch sequence fused_moe_wna16 takes for these sizes (PATH_*; -1: sizes it rejects)."""
+    q = QUANT_INT4 if bits == 4 else QUANT_INT8
+    return int(lib().fused_moe_wna16_path(M, H, I, E, topk, ctypes.byref(q), block_m,
+                                          1 if act_order else 0))
 
 
 def moe_pick_block_m(M, E, topk, bits=4, dtype=torch.float16) -> int:

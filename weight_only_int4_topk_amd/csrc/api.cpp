@@ -144,6 +144,15 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 constexpr int kFewMaxTokens = 4;
 constexpr int kFewMaxI = 512;
 
+// The launch sequence of the fused uint4/int8 layer (valid sizes assumed).
+int layer_path(int M, int H, int I, int E, int topk, int bits, int block_m, bool act_order) {
+  if (bits != 4 || act_order || block_m != 0) return MOE_PATH_GROUPED;
+  if (M == 1 && moe::single_fits(H, I, E, topk)) return MOE_PATH_ONE_TOKEN;
+  if (M >= 2 && M <= kFewMaxTokens && I <= kFewMaxI && moe::few_fits(M, H, I, E, topk))
+    return MOE_PATH_FEW_TOKENS;
+  return MOE_PATH_GROUPED;
+}
+
 // Column tiles of 16 per wavefront for a grouped GEMM with N weight rows.  Four tiles halve the
 // activation traffic per weight byte; they need block_m 16 (at 32 the 4-tile kernel takes 211
 // registers, two wavefronts per SIMD, against 128 and four with 2 tiles, and more wavefronts stream
@@ -862,10 +871,10 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
                               routing->topk_groups, routing->scale};
   hipError_t e;
 
-  // one token, uint4, tile size left to the library: one dot product per weight row in two
-  // launches (gemv.hip), the routing inside the first, the top-k combine inside the second
-  if (M == 1 && quant->bits == 4 && !act_order && block_m == 0 &&
-      moe::single_fits(H, I, E, topk)) {
+  const int path = layer_path(M, H, I, E, topk, quant->bits, block_m, act_order);
+  // one token: one dot product per weight row in two launches (gemv.hip), the routing inside the
+  // first, the top-k combine inside the second
+  if (path == MOE_PATH_ONE_TOKEN) {
     moe::SingleParams sp{};
     sp.x = x;
     sp.logits = router_logits;
@@ -889,10 +898,8 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
     return MOE_OK;
   }
 
-  // a few tokens, uint4, tile size left to the library: routing, then the two dot-product
-  // launches, each grouping the slots by expert
-  if (M >= 2 && M <= kFewMaxTokens && I <= kFewMaxI && quant->bits == 4 && !act_order &&
-      block_m == 0 && moe::few_fits(M, H, I, E, topk)) {
+  // a few tokens: routing, then the two dot-product launches, each grouping the slots by expert
+  if (path == MOE_PATH_FEW_TOKENS) {
     e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
     if (e != hipSuccess) return hip_fail(e, "routing launch");
     moe::SingleParams sp{};
@@ -1045,6 +1052,15 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
   return fused_impl(x, router_logits, M, H, I, E, topk, routing, w13, w13_scales, w13_zeros, w2,
                     w2_scales, w2_zeros, quant, dtype, block_m, workspace, workspace_bytes, out,
                     topk_weights_out, topk_ids_out, nullptr, nullptr, stream);
+}
+
+int fused_moe_wna16_path(int M, int H, int I, int E, int topk, const moe_quant_t* quant,
+                         int block_m, int act_order) {
+  if (M <= 0 || H <= 0 || I <= 0 || H % 256 || I % 256 || !quant) return -1;
+  if (E <= 0 || E > 1024 || topk <= 0 || topk > E || topk > 32) return -1;
+  if (quant->bits != 4 && quant->bits != 8) return -1;
+  if (block_m != 0 && !valid_block_m_wna16(block_m)) return -1;
+  return layer_path(M, H, I, E, topk, quant->bits, block_m, act_order != 0);
 }
 
 size_t fused_moe_wna16_act_order_workspace_size(int M, int H, int I, int E, int topk,
