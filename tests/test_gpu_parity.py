@@ -96,6 +96,45 @@ def test_align_skewed_and_foreign_ids():
     assert np.array_equal(O.to_numpy(ex), r_ex)
 
 
+@pytest.mark.parametrize("E,k,M,bm,hot", [(64, 8, 1024, 16, False), (256, 8, 4096, 64, False),
+                                         (256, 8, 4096, 256, True), (32, 2, 8192, 32, True)])
+def test_fused_layer_align_many_slots_exact(E, k, M, bm, hot):
+    """From 8192 slots on, the fused layer aligns with two launches over many workgroups (its
+    counts in the layer's workspace).  Its sorted ids, block expert ids and padded total, read back
+    from the workspace (laid out as routing weights, ids, sorted ids, block expert ids, total, each
+    at a 256-byte boundary), equal the oracle's bit for bit; with a hot expert (every token's first
+    choice) one expert's slots span many workgroups' chunks."""
+    wl = synth.Workload("am", E=E, H=256, I=256, topk=k, Ms=(M,))
+    layer = cuda_layer(synth.make_layer(wl, seed=11))
+    x = synth.make_x(wl, M, seed=11).cuda()
+    lg = synth.make_logits(wl, M, seed=11)
+    if hot:
+        lg[:, 1] += 50.0
+    lg = lg.cuda()
+    S = M * k
+    up = lambda v: (v + 255) // 256 * 256
+    cap = B.moe_align_capacity(S, E, bm)
+    need = B.fused_moe_wna16_workspace_size(M, wl.H, wl.I, E, k, B.QUANT_INT4, wl.torch_dtype, bm)
+    ws = torch.zeros((need,), dtype=torch.uint8, device="cuda")
+    B.fused_moe_wna16(x, lg, k, routing_of(wl), layer["w13"], layer["w13_scales"],
+                      layer["w13_zeros"], layer["w2"], layer["w2_scales"], layer["w2_zeros"],
+                      block_m=bm, workspace=ws)
+    torch.cuda.synchronize()
+    o_ids = up(S * 4)
+    o_sorted = o_ids + up(S * 4)
+    o_eids = o_sorted + up(cap * 4)
+    nblk = (cap + bm - 1) // bm
+    o_T = o_eids + up(nblk * 4)
+    words = lambda o, n: ws[o:o + 4 * n].view(torch.int32).cpu().numpy()
+    ids = words(o_ids, S).reshape(M, k)
+    ids_ref, _ = oracle_route(wl, lg)
+    assert np.array_equal(ids, ids_ref)
+    r_st, r_ex, r_T = O.align_block_size(ids_ref, E, bm, capacity=cap)
+    assert int(words(o_T, 1)[0]) == r_T
+    assert np.array_equal(words(o_sorted, cap), r_st)
+    assert np.array_equal(words(o_eids, nblk), r_ex)
+
+
 def test_align_golden(golden):
     g = golden("align_example.txt")
     ids = np.array([int(v) for v in g["topk_ids"][0].split()], np.int32)

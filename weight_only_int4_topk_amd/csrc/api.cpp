@@ -737,7 +737,13 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
   } else {
     e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
     if (e != hipSuccess) return hip_fail(e, "routing launch");
-    e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
+    // many slots: the many-workgroup align, its counts in the float32 row buffer (not yet in use)
+    if (moe::align_multi_pays(slots) &&
+        moe::align_multi_scratch_bytes(slots, E) <= pl.total - pl.off_y)
+      e = moe::launch_align_multi(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap,
+                                  (int32_t*)(ws + pl.off_y), st);
+    else
+      e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
     if (e != hipSuccess) return hip_fail(e, "align launch");
   }
   e = moe::launch_quant_rows(x, M, H, dtype, xq, xs, st);
@@ -953,7 +959,14 @@ int fused_impl(const void* x, const float* router_logits, int M, int H, int I, i
   } else {
     e = moe::launch_routing(router_logits, M, E, topk, rp, tw, ids, st);
     if (e != hipSuccess) return hip_fail(e, "routing launch");
-    e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
+    // many slots: the many-workgroup align, its counts in the float32 partial buffer (not yet in
+    // use)
+    if (moe::align_multi_pays(slots) &&
+        moe::align_multi_scratch_bytes(slots, E) <= pl.total - pl.off_part)
+      e = moe::launch_align_multi(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap,
+                                  (int32_t*)part, st);
+    else
+      e = moe::launch_align(ids, slots, E, pl.bm, sorted, eids, npost, pl.cap, st);
     if (e != hipSuccess) return hip_fail(e, "align launch");
   }
 

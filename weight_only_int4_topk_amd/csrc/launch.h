@@ -27,6 +27,13 @@ hipError_t launch_route_align(const float* logits, int M, int E, int topk, const
 hipError_t launch_align(const int32_t* topk_ids, int numel, int E, int block_m,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post,
                         int64_t capacity, hipStream_t stream);
+// The same output by two launches over many workgroups (for many slots: align_multi_pays);
+// scratch: device int32 of align_multi_scratch_bytes(numel, E) bytes.
+bool align_multi_pays(int numel);
+size_t align_multi_scratch_bytes(int numel, int E);
+hipError_t launch_align_multi(const int32_t* topk_ids, int numel, int E, int block_m,
+                              int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_post,
+                              int64_t capacity, int32_t* scratch, hipStream_t stream);
 
 struct GemmParams {
   const void* A;              // dtype [num_a_rows, K]
