@@ -313,7 +313,8 @@ size_t fused_moe_wna16_workspace_size(int M, int H, int I, int E, int topk, cons
  *   topk_weights_out / topk_ids_out: optional device [M, topk] copies of the routing result
  *   block_m       0 = library's choice, else one of {16, 32, 64, 128, 256}
  * Launches, by the path fused_moe_wna16_path names:
- *   MOE_PATH_GROUPED: routing and align (one launch for M <= 4), GEMM1 (+SiLU*up; split over K
+ *   MOE_PATH_GROUPED: routing and align (one launch for M <= 4; align over many workgroups in two
+ *     launches from 8192 slots, its counts in the workspace), GEMM1 (+SiLU*up; split over K
  *     into float32 partials and a SiLU*up pass when its workgroups would not fill the chip), GEMM2
  *     (split over K into float32 partials at small M; unsplit with block_m 64, it writes dtype rows
  *     times the routing weight), combine (float32 sums in a fixed order);
