@@ -366,9 +366,9 @@ def w8a8_sweep(steps, warmup, Ms=(1024, 4096), seed=0):
         x = synth.make_x(wl, M, seed=seed, device="cuda")
         lg = synth.make_logits(wl, M, seed=seed, device="cuda")
         tw, ti = B.moe_topk_softmax(lg, wl.topk, rt)
-        # the layers' choices: the w8a16 layer's block size, at most 128 rows for w8a8
+        # the layers' choices (the same block size for both at this shape)
         bm16 = B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype)
-        bm8 = min(128, bm16)
+        bm8 = bm16
         st, ex, npost = B.moe_align_block_size(ti, wl.E, bm8)
         st16, ex16, np16 = B.moe_align_block_size(ti, wl.E, bm16)
         q, sa = B.moe_quant_int8_rows(x)

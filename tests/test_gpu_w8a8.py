@@ -33,7 +33,7 @@ def test_quant_int8_rows_exact(dt, rows, K):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-@pytest.mark.parametrize("bm", [16, 64, 128])
+@pytest.mark.parametrize("bm", [16, 64, 128, 256])
 def test_w8a8_layout_probe_bit_exact(dt, bm):
     """Activation codes one-hot at column k with scale 1, routed to one expert: row k of the output
     is column k of that expert's int8 weights times their channel scales, which must equal the
@@ -87,6 +87,42 @@ def test_w8a8_gemm_vs_oracle(dt, bm, act, weighted):
                               *O.align_block_size(ids, wl.E, bm), bm, ns,
                               topk_weights=w if weighted else None, act=act)
     assert_layer_close(C, np.stack([ref[s] for s in range(ns)]), f"w8a8 act={act} bm={bm}")
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("act,weighted", [(1, False), (0, True)])
+def test_w8a8_gemm_256_rows_hot_experts(dt, act, weighted):
+    """256-row blocks with every count of filled 32-row tiles: expert 0 takes 300 slots (a full
+    block and a block of 44 rows), expert 1 takes 170 (six tiles, the last partial), expert 2 takes
+    the remaining 230 (eight tiles, the last partial); with the SiLU epilogue each wavefront's column
+    tile mixes 16 gate and the 16 matching up rows."""
+    wl = synth.Workload("h8", E=3, H=512, I=256, topk=1, Ms=(700,), dtype=dt, bits=8)
+    layer = synth.make_layer(wl, seed=11)
+    lay = cuda_layer(layer)
+    M = 700
+    ids = np.concatenate([np.zeros(300), np.ones(170), np.full(230, 2)]).astype(np.int32)
+    ids = ids[np.random.default_rng(3).permutation(M)].reshape(M, 1)
+    w = np.random.default_rng(4).uniform(0.1, 1.0, size=(M, 1)).astype(np.float32)
+    bm = 256
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), wl.E, bm)
+    tw = torch.from_numpy(w).cuda() if weighted else None
+    if act:
+        x = synth.make_x(wl, M, seed=12)
+        Aq, sa = O.quant_int8_rows(x)
+        name = "w13"
+    else:
+        h = (torch.randn(M, wl.I, generator=torch.Generator().manual_seed(13)) * 0.3)
+        Aq, sa = O.quant_int8_rows(h)
+        name = "w2"
+    C = B.moe_w8a8_gemm(torch.from_numpy(Aq).cuda(), torch.from_numpy(sa).cuda(), 1, lay[name],
+                        lay[name + "_scales"], st, ex, npost, bm, M, wl.torch_dtype,
+                        topk_weights=tw, act=act)
+    torch.cuda.synchronize()
+    ref = O.w8a8_grouped_gemm(Aq, sa, 1,
+                              lambda e: (O.to_numpy(layer[name][e]), O.to_numpy(layer[name + "_scales"][e])),
+                              *O.align_block_size(ids, wl.E, bm), bm, M,
+                              topk_weights=w if weighted else None, act=act)
+    assert_layer_close(C, np.stack([ref[s] for s in range(M)]), f"w8a8 256 rows act={act}")
 
 
 def test_w8a8_mixtral_shape_sampled():

@@ -48,7 +48,7 @@ def test_fused_w8a8_vs_oracle(name):
     assert_layer_close(out, ref, f"w8a8 {name}")
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 def test_fused_w8a8_block_sizes_deterministic(bm):
     wl = SMALL["softmax_fp16"]
     out1, x, ids, w, lay = _run(wl, 33, seed=6, block_m=bm)
@@ -85,7 +85,7 @@ def test_fused_w8a8_mixtral_shape_all_tokens():
 
 def test_fused_w8a8_dsv3_full_size_spaced_tokens():
     """DeepSeek-V3-shaped int8 experts (256 x H 7168 x I 2048, bf16, grouped sigmoid top-8) at the
-    batch sizes the bench times, M = 4096 and 1024, with the library's block size (128 rows at 4096
+    batch sizes the bench times, M = 4096 and 1024, with the library's block size (256 rows at 4096
     tokens, 64 at 1024): every token's routing exact, align exact at that block size, and 256 evenly
     spaced tokens of each batch (first and last included) against the oracle.  The smaller batch is
     the leading rows of the larger one, so the experts are copied and decoded once."""
@@ -96,8 +96,8 @@ def test_fused_w8a8_dsv3_full_size_spaced_tokens():
     ids, w = oracle_route(wl, lg)
     outs, rows = {}, {}
     for M in (4096, 1024):
-        bm = min(128, B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype))
-        assert bm == (64 if M == 1024 else 128)
+        bm = B.moe_pick_block_m(M, wl.E, wl.topk, 8, wl.torch_dtype)
+        assert bm == (64 if M == 1024 else 256)
         print(f"fused w8a8 dsv3 full size M={M} block_m={bm}", flush=True)
         ti = torch.empty((M, wl.topk), dtype=torch.int32, device="cuda")
         tw = torch.empty((M, wl.topk), dtype=torch.float32, device="cuda")

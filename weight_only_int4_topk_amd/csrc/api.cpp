@@ -597,8 +597,10 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
                 num_a_rows, a_row_div, num_slots);
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL)
     return fail(MOE_ERR_INVALID_ARG, "act = %d", act);
-  if (!valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 16, 32, 64, 128)", block_m);
+  if (!valid_block_m(block_m) && !(block_m == 256 && moe::w8a8_mma32_fits(256, act, N)))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "block_m = %d (supported: 16, 32, 64, 128; 256 where N / 2 (act) or N is a "
+                "multiple of 128 or 256)", block_m);
   if (K % 256) return fail(MOE_ERR_UNSUPPORTED, "K = %d must be a multiple of 256", K);
   if (N % 128) return fail(MOE_ERR_UNSUPPORTED, "N = %d must be a multiple of 128", N);
   if ((int64_t)num_a_rows * K >= ((int64_t)1 << 31) || (int64_t)N * K >= ((int64_t)1 << 31))
@@ -649,11 +651,18 @@ struct PlanW8 {
   size_t off_w, off_ids, off_sorted, off_eids, off_npost, off_xq, off_xs, off_inter, off_iq, off_is,
       off_y, total;
 };
+// 256-row blocks for both w8a8 GEMMs: the 32x32 integer kernel with one column tile per wavefront
+bool w8a8_fits_256(int H, int I) {
+  return moe::w8a8_mma32_fits(256, 1, 2 * I) && moe::w8a8_mma32_fits(256, 0, H);
+}
+
 PlanW8 make_plan_w8(int M, int H, int I, int E, int topk, int dtype, int block_m) {
   PlanW8 p{};
   const int64_t slots = (int64_t)M * topk;
-  // the int8-activation GEMM takes at most 128-row blocks
-  p.bm = block_m > 0 ? block_m : std::min(128, pick_block_m(M, topk, E, 8, dtype));
+  // the int8 block-size rule; 256 rows (a whole expert's slots: each weight read once, where 128
+  // rows read about half the experts' weights twice) where both GEMMs take them, else 128
+  p.bm = block_m > 0 ? block_m : pick_block_m(M, topk, E, 8, dtype);
+  if (block_m == 0 && p.bm == 256 && !w8a8_fits_256(H, I)) p.bm = 128;
   p.cap = align_capacity(slots, E, p.bm);
   const int64_t nblk = (p.cap + p.bm - 1) / p.bm;
   size_t off = 0;
@@ -675,7 +684,7 @@ PlanW8 make_plan_w8(int M, int H, int I, int E, int topk, int dtype, int block_m
 
 size_t fused_moe_w8a8_workspace_size(int M, int H, int I, int E, int topk, int dtype, int block_m) {
   if (M < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;
-  if (block_m != 0 && !valid_block_m(block_m)) return 0;
+  if (block_m != 0 && !valid_block_m(block_m) && !(block_m == 256 && w8a8_fits_256(H, I))) return 0;
   return make_plan_w8(M, H, I, E, topk, dtype, block_m).total;
 }
 
@@ -687,10 +696,10 @@ int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int 
   if (int rc = check_dtype(dtype)) return rc;
   if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "M=%d H=%d I=%d", M, H, I);
   if (int rc = check_routing(routing, E, topk)) return rc;
-  if (block_m != 0 && !valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128)", block_m);
   if (H % 256 || I % 256)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d and I = %d must be multiples of 256", H, I);
+  if (block_m != 0 && !valid_block_m(block_m) && !(block_m == 256 && w8a8_fits_256(H, I)))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d (supported: 0, 16, 32, 64, 128, 256)", block_m);
   if (H > kW8A8MaxK || I > kW8A8MaxK)
     return fail(MOE_ERR_UNSUPPORTED, "H = %d or I = %d > %d (int32 sums)", H, I, kW8A8MaxK);
   if ((int64_t)M * topk > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "M * topk > 2^24");

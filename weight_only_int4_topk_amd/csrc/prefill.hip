@@ -486,8 +486,11 @@ constexpr int kPrefillBufs = 2;
 typedef int32_t i32x16_t __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4v_t __attribute__((ext_vector_type(4)));
 
+// block_m 256 (MT = 8): one column tile per wavefront (eight 32-row accumulator tiles take the
+// registers, two wavefronts per SIMD), with the SiLU epilogue a mixed tile of 16 gate rows and the
+// 16 matching up rows, as in the 256-row prefill GEMM
 template <int DT, int MT, int NT, int WAVES, int ACT, int OUTF32>
-__global__ void __launch_bounds__(WAVES * 64, 2) w8a8_mma32_kernel(W8A8Params p) {
+__global__ void __launch_bounds__(WAVES * 64, MT == 8 ? 1 : 2) w8a8_mma32_kernel(W8A8Params p) {
   constexpr int THREADS = WAVES * kWave;
   constexpr int BM = 32 * MT;
   constexpr int KB = 64;                          // k (bytes) per k-block
@@ -497,9 +500,11 @@ __global__ void __launch_bounds__(WAVES * 64, 2) w8a8_mma32_kernel(W8A8Params p)
   constexpr int AV = (NCH + THREADS - 1) / THREADS;
   static_assert(NCH % kWave == 0 && (NCH >= THREADS ? NCH % THREADS == 0 : true),
                 "whole wavefronts of activation chunks");
-  static_assert(!ACT || NT % 2 == 0, "SiLU epilogue: gate and up tiles in pairs");
-  constexpr int NOUT = ACT ? NT / 2 : NT;
-  constexpr int WG_COLS = WAVES * NOUT * 32;
+  static_assert(!ACT || NT % 2 == 0 || NT == 1, "SiLU epilogue: paired or mixed tiles");
+  static_assert(MT != 8 || NT == 1, "256-row blocks: one column tile per wavefront");
+  constexpr bool MIXED = ACT && NT == 1;
+  constexpr int NOUT = ACT ? (MIXED ? 1 : NT / 2) : NT;
+  constexpr int WG_COLS = WAVES * NOUT * (MIXED ? 16 : 32);
   constexpr int LPK = 2 * NT;                     // weight loads per lane and k-block
 
   __shared__ __attribute__((aligned(16))) uint8_t s_a0[BM * KB];
@@ -530,14 +535,21 @@ __global__ void __launch_bounds__(WAVES * 64, 2) w8a8_mma32_kernel(W8A8Params p)
   const int kb_total = K / KB;
   const int c32 = lane & 31;
   const int h = lane >> 5;
-  int col[NT];
+  // col[t]: first output column of tile t (of the gate half with the SiLU epilogue); wrow[t]: the
+  // weight row lane l streams for tile t (mixed tile: gate rows in lanes c32 < 16, up rows above)
+  int col[NT], wrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if constexpr (ACT) {
+    if constexpr (MIXED) {
+      col[t] = nc * WG_COLS + wave * 16;
+      wrow[t] = c32 < 16 ? col[t] + c32 : N / 2 + col[t] + (c32 - 16);
+    } else if constexpr (ACT) {
       const int g0 = nc * WG_COLS + wave * NOUT * 32;
       col[t] = t < NOUT ? g0 + t * 32 : N / 2 + g0 + (t - NOUT) * 32;
+      wrow[t] = col[t] + c32;
     } else {
       col[t] = nc * WG_COLS + (wave * NT + t) * 32;
+      wrow[t] = col[t] + c32;
     }
   }
   const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
@@ -546,7 +558,7 @@ __global__ void __launch_bounds__(WAVES * 64, 2) w8a8_mma32_kernel(W8A8Params p)
       (void*)p.A, (short)0, (int)((size_t)p.num_a_rows * K), kRsrc3);
   uint32_t vw[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) vw[t] = (uint32_t)(col[t] + c32) * (uint32_t)K + h * 32;
+  for (int t = 0; t < NT; ++t) vw[t] = (uint32_t)wrow[t] * (uint32_t)K + h * 32;
 
   // activation chunks: slot idx = tid + i * THREADS of the unpadded tile (row idx / VPR, physical
   // chunk idx % VPR holding logical chunk (idx % VPR) ^ swz(row)); a wavefront past the tile's
@@ -640,20 +652,53 @@ __global__ void __launch_bounds__(WAVES * 64, 2) w8a8_mma32_kernel(W8A8Params p)
       }
     }
   };
-  static_assert(MT == 2 || MT == 4, "block_m 64 or 128");
+  static_assert(MT == 2 || MT == 4 || MT == 8, "block_m 64, 128 or 256");
   if constexpr (MT == 2) {
     if (mt_valid >= 2) kloop(std::integral_constant<int, 2>{});
     else kloop(std::integral_constant<int, 1>{});
-  } else {
+  } else if constexpr (MT == 4) {
     if (mt_valid >= 4) kloop(std::integral_constant<int, 4>{});
     else if (mt_valid == 3) kloop(std::integral_constant<int, 3>{});
     else if (mt_valid == 2) kloop(std::integral_constant<int, 2>{});
     else kloop(std::integral_constant<int, 1>{});
+  } else {
+    switch (mt_valid) {
+      case 8: kloop(std::integral_constant<int, 8>{}); break;
+      case 7: kloop(std::integral_constant<int, 7>{}); break;
+      case 6: kloop(std::integral_constant<int, 6>{}); break;
+      case 5: kloop(std::integral_constant<int, 5>{}); break;
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      default: kloop(std::integral_constant<int, 1>{}); break;
+    }
   }
   wait_vmcnt_p<0>();
 
   // epilogue: register i of lane l holds row 8 (i / 4) + 4 h + i % 4 of each 32-row tile
   const uint16_t* wsc = (const uint16_t*)p.w_scales + (size_t)e * N;
+  if constexpr (MIXED) {
+    // each lane scales its own row's sums (its weight row's scale), then lane c (c < 16) of each
+    // 32-lane half takes the up value of lane c + 16 and writes SiLU(gate) * up
+    const float ws = bits_to_float<DT>(wsc[wrow[0]]);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= mt_valid) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m * 32 + 8 * (i / 4) + 4 * h + (i % 4);
+        const float v = (float)acc[m][0][i] * s_as[r] * ws;
+        const float u = __shfl_xor(v, 16, kWave);
+        const int slot = s_slot[r];
+        if (c32 < 16 && slot >= 0) {
+          const float wscale = p.topk_w ? p.topk_w[slot] : 1.0f;
+          ((uint16_t*)p.C)[(size_t)slot * (N / 2) + col[0] + c32] =
+              float_to_bits<DT>(v / (1.0f + __expf(-v)) * u * wscale);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m >= mt_valid) continue;
@@ -688,13 +733,13 @@ template <int DT, int MT, int NT>
 hipError_t launch_w8a8_32(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
   constexpr int WV = kPrefillWaves;
   const int n_out = act ? p.N / 2 : p.N;
-  const int wg_cols = WV * (act ? NT / 2 : NT) * 32;
+  const int wg_cols = act ? (NT == 1 ? WV * 16 : WV * (NT / 2) * 32) : WV * NT * 32;
   const long long grid = (long long)(n_out / wg_cols) * p.num_blocks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 block(WV * kWave);
   if (act) {
-    if constexpr (NT % 2 == 0)
+    if constexpr (NT % 2 == 0 || MT == 8)
       hipLaunchKernelGGL((w8a8_mma32_kernel<DT, MT, NT, WV, 1, 0>), dim3((unsigned)grid), block, 0,
                          stream, p);
     else
@@ -711,8 +756,12 @@ hipError_t launch_w8a8_32(const W8A8Params& p, int act, int out_f32, hipStream_t
 
 template <int DT, int MT>
 hipError_t launch_w8a8_32_nt(const W8A8Params& p, int act, int out_f32, hipStream_t stream) {
-  if (act || p.N % (kPrefillWaves * 64) == 0) return launch_w8a8_32<DT, MT, 2>(p, act, out_f32, stream);
-  return launch_w8a8_32<DT, MT, 1>(p, act, out_f32, stream);
+  if constexpr (MT == 8) {
+    return launch_w8a8_32<DT, MT, 1>(p, act, out_f32, stream);
+  } else {
+    if (act || p.N % (kPrefillWaves * 64) == 0) return launch_w8a8_32<DT, MT, 2>(p, act, out_f32, stream);
+    return launch_w8a8_32<DT, MT, 1>(p, act, out_f32, stream);
+  }
 }
 
 
@@ -786,8 +835,8 @@ size_t prefill_lds_bytes(const GemmConfig& c) {
 }
 
 bool w8a8_mma32_fits(int block_m, int act, int N) {
-  if (block_m != 64 && block_m != 128) return false;
-  if (act) return (N / 2) % (kPrefillWaves * 32) == 0;
+  if (block_m != 64 && block_m != 128 && block_m != 256) return false;
+  if (act) return (N / 2) % (kPrefillWaves * (block_m == 256 ? 16 : 32)) == 0;
   return N % (kPrefillWaves * 32) == 0;
 }
 
@@ -795,10 +844,12 @@ hipError_t launch_w8a8_mma32(const W8A8Params& p, int block_m, int act, int dtyp
                              hipStream_t stream) {
   if (!w8a8_mma32_fits(block_m, act, p.N)) return hipErrorInvalidValue;
   if (dtype == 0)
-    return block_m == 64 ? launch_w8a8_32_nt<0, 2>(p, act, out_f32, stream)
-                         : launch_w8a8_32_nt<0, 4>(p, act, out_f32, stream);
-  return block_m == 64 ? launch_w8a8_32_nt<1, 2>(p, act, out_f32, stream)
-                       : launch_w8a8_32_nt<1, 4>(p, act, out_f32, stream);
+    return block_m == 64    ? launch_w8a8_32_nt<0, 2>(p, act, out_f32, stream)
+           : block_m == 128 ? launch_w8a8_32_nt<0, 4>(p, act, out_f32, stream)
+                            : launch_w8a8_32_nt<0, 8>(p, act, out_f32, stream);
+  return block_m == 64    ? launch_w8a8_32_nt<1, 2>(p, act, out_f32, stream)
+         : block_m == 128 ? launch_w8a8_32_nt<1, 4>(p, act, out_f32, stream)
+                          : launch_w8a8_32_nt<1, 8>(p, act, out_f32, stream);
 }
 
 hipError_t launch_prefill(const GemmParams& p_in, const GemmConfig& c, hipStream_t stream) {
