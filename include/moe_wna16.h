@@ -209,8 +209,9 @@ int moe_quant_int8_rows(const void* x, int rows, int K, int dtype, int8_t* q, fl
  *   B        device int8 [E, N, K], w_scales device dtype [E, N] (the int8 weight storage above)
  *   sorted_token_ids / expert_ids / num_tokens_post_padded: moe_align_block_size with block_m
  * Rows of C whose slot is not listed are not written.  num_slots = 0 returns MOE_OK at once.
- * Limits: block_m in {16, 32, 64, 128}, K % 256 == 0, N % 128 == 0, K <= 131072 (the int32 sums
- * of code products stay below 2^31). */
+ * Limits: block_m in {16, 32, 64, 128}, or 256 where N / 2 (act 1) is a multiple of 128 or N
+ * (act 0) a multiple of 256 (the 32x32 integer kernel, one column tile per wavefront), K % 256 == 0,
+ * N % 128 == 0, K <= 131072 (the int32 sums of code products stay below 2^31). */
 int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_row_div,
                   const int8_t* B, const void* w_scales, int E, int N, int K, int dtype,
                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
@@ -222,10 +223,11 @@ int moe_w8a8_gemm(const int8_t* A, const float* a_scales, int num_a_rows, int a_
  * quantised per slot, w8a8 GEMM2 into float32 rows, top-k weighted combine in float32 (fixed order).
  *   w13 device int8 [E, 2I, H], w13_scales device dtype [E, 2I]; w2 int8 [E, H, I], w2_scales [E, H]
  *   workspace: at least fused_moe_w8a8_workspace_size(...) bytes, 256-byte aligned
- *   block_m 0 = the library's choice (as moe_pick_block_m for int8 weights)
+ *   block_m 0 = the library's choice (moe_pick_block_m for int8 weights; 128 where it picks 256 and
+ *   256 is not available)
  * Deterministic.  Limits: H % 256 == 0, I % 256 == 0, H and I <= 131072 (int32 sums), block_m
- * in {0, 16, 32, 64, 128}, M * topk <= 2^24, and below 2^31 (32-bit offsets): M * H,
- * M * topk * I and 2I * H. */
+ * in {0, 16, 32, 64, 128}, or 256 where I % 128 == 0 (always, given I % 256 == 0), M * topk <=
+ * 2^24, and below 2^31 (32-bit offsets): M * H, M * topk * I and 2I * H. */
 int fused_moe_w8a8(const void* x, const float* router_logits, int M, int H, int I, int E, int topk,
                    const moe_routing_t* routing, const int8_t* w13, const void* w13_scales,
                    const int8_t* w2, const void* w2_scales, int dtype, int block_m,
@@ -294,8 +296,8 @@ int moe_repack_uint4(int format, const int32_t* qweight, const int32_t* qzeros, 
  * share one block and its weights are streamed and decoded once; bf16 uint4 keeps 64 up to 128
  * needed rows; fp16 uint4 stops at 64, and takes 32 where up to 128 rows would be needed (its
  * 64-row kernel stages activations through registers, which measured slower than two 32-row
- * blocks).  128- and 256-row blocks run on the 32x32 matrix cores.  fused_moe_w8a8 caps the choice
- * at 128.  Returns -1 for non-positive sizes, other bit widths or other dtypes. */
+ * blocks).  128- and 256-row blocks run on the 32x32 matrix cores (for fused_moe_w8a8 too).
+ * Returns -1 for non-positive sizes, other bit widths or other dtypes. */
 int moe_pick_block_m(int M, int E, int topk, int bits, int dtype);
 
 /* Workspace bytes fused_moe_wna16 needs for these sizes (block_m 0 = library's choice). */
