@@ -301,7 +301,11 @@ def test_w8a8_validation(lib):
                                  a["bm"], a["slots"], a["tw"], a["act"], a["C"], NULL)
 
     assert w8(bm=24) == UNSUPPORTED
-    assert w8(bm=256) == UNSUPPORTED                            # int8 activations: up to 128 rows
+    # 256-row blocks only on the 32x32 integer kernel: N / 2 (act 1) a multiple of 128, N (act 0)
+    # a multiple of 256
+    assert w8(bm=256, N=1152) == UNSUPPORTED
+    assert w8(bm=256, N=1152, act=0) == UNSUPPORTED
+    assert w8(bm=512) == UNSUPPORTED
     assert w8(slots=0, rows=0, A=NULL, sa=NULL, C=NULL, st=NULL, ex=NULL, npost=NULL) == OK
     assert w8(K=320) == UNSUPPORTED
     assert w8(N=1000) == UNSUPPORTED
