@@ -47,6 +47,30 @@ def test_routing_variants(score, E, k, ng, tg, renorm):
     assert_weights_close(tw, w_ref)
 
 
+@pytest.mark.parametrize("renorm", [0, 1])
+@pytest.mark.parametrize("score,E,k,ng,tg", [("softmax", 64, 6, 1, 1), ("softmax", 200, 8, 1, 1),
+                                              ("sigmoid", 96, 5, 6, 3), ("sigmoid", 256, 8, 8, 4),
+                                              ("sigmoid", 64, 32, 64, 40)])
+@pytest.mark.parametrize("logits", ["ties", "neg_inf"])
+@pytest.mark.parametrize("M", [33, 1024, 1025])
+def test_routing_ties_and_neg_inf(score, E, k, ng, tg, renorm, logits, M):
+    """64 to 256 experts up to 1024 tokens take the one-workgroup-per-token ranking launch, 1025
+    tokens the one-wavefront-per-token launch: the same ids bit for bit and the oracle's weights,
+    with ties (logits on a grid of 0.5: equal scores go to the lower id) and with -inf logits (a
+    quarter of the experts of every token)."""
+    wl = synth.Workload("rt", E=E, H=256, I=256, topk=k, Ms=(M,), score=score,
+                        renormalize=bool(renorm), num_groups=ng, topk_groups=tg, scale=1.5)
+    lg = synth.make_logits(wl, M, seed=7)
+    if logits == "ties":
+        lg = torch.round(lg * 2) / 2
+    else:
+        lg[:, 1::4] = -float("inf")
+    tw, ti = B.moe_topk_softmax(lg.cuda(), k, routing_of(wl))
+    ids_ref, w_ref = oracle_route(wl, lg)
+    assert np.array_equal(O.to_numpy(ti), ids_ref)
+    assert_weights_close(tw, w_ref)
+
+
 # ------------------------------------------------------------------------------------------------
 # align
 # ------------------------------------------------------------------------------------------------

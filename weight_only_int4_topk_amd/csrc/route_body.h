@@ -226,5 +226,169 @@ __device__ void route_token(const float* __restrict__ row, int E, int topk, cons
   }
 }
 
+
+// The token's routing by the whole workgroup (E <= 256, topk <= 32): the same selection and
+// weights as route_token, without its topk rounds of a wave-wide arg-best.  Every candidate gets
+// a 64-bit key, its score mapped to an unsigned integer of the same order above its complemented
+// id, so that key order is route_token's order (larger score first, equal scores to the lower
+// id) and all keys differ; ineligible candidates (experts of dropped groups, NaN scores) get key
+// 0, below every other.  A candidate's place is the number of larger keys: first within its
+// wavefront's 64 candidates, then, for the topk best of each wavefront (which hold every
+// candidate of the overall top-k), among those.  `v` is the thread's logit (threads t < E).
+// Leaves the ids in wid[0, topk) (0x7fffffff where fewer candidates are eligible) and returns
+// the weight of place t to the threads t < topk.  Ends with a barrier.
+struct __attribute__((aligned(16))) RouteLds {
+  uint64_t key[256];
+  uint64_t surv[4 * 32];  // the topk best keys of each wavefront (0: none)
+  float gsc[64];
+  float val[256];
+  int wid[32];
+  float wval[32];
+};
+
+__device__ __forceinline__ uint64_t route_key(float v, int t) {
+  const uint32_t b = __float_as_uint(v + 0.0f);  // -0 -> +0: equal scores stay equal
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)t);
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ float route_single(float v, int E, int topk, const RoutingParams& rp, RouteLds& r) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const float kNone = -__builtin_inff();
+  if (rp.score == 1 && t < E) v = sigmoid_spec(v);
+  if (t < 256) r.val[t] = t < E ? v : 0.0f;  // the scores (softmax without renormalisation)
+  if (t < 4 * 32) r.surv[t] = 0;
+  if (t < topk) {
+    r.wid[t] = 0x7fffffff;
+    r.wval[t] = kNone;
+  }
+  bool elig = t < E && v == v;
+  const int ng = rp.num_groups;
+  if (rp.score == 1 && rp.topk_groups < ng) {
+    // group score: sum of the two largest scores of the group's contiguous experts
+    const int gs = E / ng;
+    if ((gs & (gs - 1)) == 0 && gs <= kWave) {
+      // groups of a power of two lanes: top-2 merges across the group's lanes (DPP within rows of
+      // 16, then row and half swaps), every lane of the group ends with the pair
+      float t1 = t < E ? v : kNone, t2 = kNone;
+      if (gs >= 2) top2_step<kDppXor1>(t1, t2);
+      if (gs >= 4) top2_step<kDppXor2>(t1, t2);
+      if (gs >= 8) top2_step<kDppHalfMirror>(t1, t2);
+      if (gs >= 16) top2_step<kDppMirror>(t1, t2);
+      if (gs >= 32) {
+        uint32_t a1, b1, a2, b2;
+        swap_pair<false>(__float_as_uint(t1), a1, b1);
+        swap_pair<false>(__float_as_uint(t2), a2, b2);
+        t1 = __uint_as_float(a1);
+        t2 = __uint_as_float(a2);
+        top2_merge(t1, t2, __uint_as_float(b1), __uint_as_float(b2));
+      }
+      if (gs >= 64) {
+        uint32_t a1, b1, a2, b2;
+        swap_pair<true>(__float_as_uint(t1), a1, b1);
+        swap_pair<true>(__float_as_uint(t2), a2, b2);
+        t1 = __uint_as_float(a1);
+        t2 = __uint_as_float(a2);
+        top2_merge(t1, t2, __uint_as_float(b1), __uint_as_float(b2));
+      }
+      if (t < E && t % gs == 0) r.gsc[t / gs] = gs >= 2 ? t1 + t2 : t1;
+      __syncthreads();
+    } else {
+      __syncthreads();  // the scores in val
+      if (t < ng) {
+        float b1 = kNone, b2 = kNone;
+        for (int i = 0; i < gs; ++i) {
+          const float x = r.val[t * gs + i];
+          if (x > b1) {
+            b2 = b1;
+            b1 = x;
+          } else if (x > b2) {
+            b2 = x;
+          }
+        }
+        r.gsc[t] = gs >= 2 ? b1 + b2 : b1;
+      }
+      __syncthreads();
+    }
+    // keep the topk_groups best groups (ties -> lower group id); each thread ranks its own group
+    if (t < E) {
+      const int g = t / gs;
+      const float mine = r.gsc[g];
+      int rank = 0;
+#pragma unroll 8
+      for (int o = 0; o < ng; ++o) rank += (o != g && better(r.gsc[o], o, mine, g)) ? 1 : 0;
+      if (rank >= rp.topk_groups) elig = false;
+    }
+  }
+  const uint64_t key = elig ? route_key(v, t) : 0ull;
+  if (t < 256) r.key[t] = key;
+  __syncthreads();
+  // place within the wavefront's 64 candidates (waves past E hold key 0 only)
+  if (elig) {
+    const uint64_t* kw = r.key + wave * kWave;
+    int c0 = 0, c1 = 0;
+#pragma unroll 8
+    for (int u = 0; u < kWave; u += 2) {
+      c0 += kw[u] > key ? 1 : 0;
+      c1 += kw[u + 1] > key ? 1 : 0;
+    }
+    const int lr = c0 + c1;
+    if (lr < topk) r.surv[wave * topk + lr] = key;
+  }
+  __syncthreads();
+  // place among the survivors
+  const int ns = ((E + kWave - 1) / kWave) * topk;
+  if (t < ns) {
+    const uint64_t k = r.surv[t];
+    if (k != 0) {
+      int c0 = 0, c1 = 0;
+      int u = 0;
+      for (; u + 1 < ns; u += 2) {
+        c0 += r.surv[u] > k ? 1 : 0;
+        c1 += r.surv[u + 1] > k ? 1 : 0;
+      }
+      if (u < ns) c0 += r.surv[u] > k ? 1 : 0;
+      const int rank = c0 + c1;
+      if (rank < topk) {
+        r.wid[rank] = (int)(0xFFFFFFFFu - (uint32_t)k);
+        r.wval[rank] = key_value(k);
+      }
+    }
+  }
+  __syncthreads();
+  if (t >= kWave) return 0.0f;
+  // weights, in route_token's order of operations
+  float denom = 0.0f, my = 0.0f;
+  if (rp.score == 0) {
+    const float mx = r.wval[0];
+    for (int j = 0; j < topk; ++j) {
+      const float ej = expf(r.wval[j] - mx);
+      denom += ej;
+      if (j == lane) my = ej;
+    }
+    if (!rp.renormalize) {
+      float part = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + kWave * i < E) part += expf(r.val[lane + kWave * i] - mx);
+      denom = wave_sum(part);
+    }
+  } else {
+    for (int j = 0; j < topk; ++j) {
+      denom += r.wval[j];
+      if (j == lane) my = r.wval[j];
+    }
+    if (!rp.renormalize) denom = 1.0f;
+  }
+  return my / denom * rp.scale;
+}
+
 }  // namespace
 }  // namespace moe

@@ -1,5 +1,6 @@
-// Top-k routing on gfx950: one 64-lane wavefront per token, four tokens per workgroup (the
-// per-token rule is in route_body.h).
+// Top-k routing on gfx950: one 64-lane wavefront per token, four tokens per workgroup, or (64 to 256
+// experts, up to 1024 tokens) one workgroup per token ranking 64-bit order keys (the per-token
+// rules are in route_body.h).
 #include "align_body.h"
 #include "common.h"
 #include "launch.h"
@@ -23,6 +24,24 @@ __global__ void __launch_bounds__(256) routing_kernel(const float* __restrict__ 
   if (token >= M) return;
   route_token<EPL>(logits + (size_t)token * E, E, topk, p, s_score[wid],
                    out_w + (size_t)token * topk, out_ids + (size_t)token * topk, nullptr);
+}
+
+// One token per workgroup of 256 threads (E <= 256, topk <= 32, at most 64 groups): route_single's
+// ranking (each candidate's place from 64-bit order keys, within its wavefront and then among the
+// wavefronts' survivors) instead of topk rounds of a wavefront-wide arg-best; same ids and weights.
+__global__ void __launch_bounds__(256) routing_rank_kernel(const float* __restrict__ logits, int E,
+                                                           int topk, RoutingParams p,
+                                                           float* __restrict__ out_w,
+                                                           int32_t* __restrict__ out_ids) {
+  __shared__ RouteLds r;
+  const int m = blockIdx.x;
+  const int t = threadIdx.x;
+  const float v = t < E ? logits[(size_t)m * E + t] : 0.0f;
+  const float w = route_single(v, E, topk, p, r);
+  if (t < topk) {
+    out_ids[(size_t)m * topk + t] = r.wid[t];
+    out_w[(size_t)m * topk + t] = w;
+  }
 }
 
 // Small batches (M <= 4 tokens, E <= 256): routing and align in one workgroup of 16 wavefronts,
@@ -117,9 +136,22 @@ hipError_t launch_route_align(const float* logits, int M, int E, int topk, const
                       num_post, capacity, stream);
 }
 
+// The ranking launch where it measured faster (routing alone, graph replays): 256 experts top-8
+// grouped sigmoid 6.0 -> 4.0 us at M = 1, 6.4 -> 4.2 at 16, 6.9 -> 5.7 at 1024, but 11.2 -> 12.9
+// at 4096; 64 experts top-8 3.6 -> 2.7 at M = 1, 4.3 -> 3.4 at 1024, 6.1 -> 6.3 at 4096; 8 experts
+// top-2 slower at every M (1.9 -> 2.4 us at M = 1).
+bool routing_rank_pays(int M, int E, int topk, const RoutingParams& p) {
+  return E >= 64 && E <= 256 && topk <= 32 && p.num_groups <= 64 && M <= 1024;
+}
+
 hipError_t launch_routing(const float* logits, int M, int E, int topk, const RoutingParams& p,
                           float* topk_w, int32_t* topk_ids, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (routing_rank_pays(M, E, topk, p)) {
+    hipLaunchKernelGGL(routing_rank_kernel, dim3(M), dim3(256), 0, stream, logits, E, topk, p,
+                       topk_w, topk_ids);
+    return hipGetLastError();
+  }
   if (E <= 64) return launch_epl<1>(logits, M, E, topk, p, topk_w, topk_ids, stream);
   if (E <= 128) return launch_epl<2>(logits, M, E, topk, p, topk_w, topk_ids, stream);
   if (E <= 256) return launch_epl<4>(logits, M, E, topk, p, topk_w, topk_ids, stream);
