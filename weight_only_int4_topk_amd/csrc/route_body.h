@@ -1,5 +1,7 @@
-// Top-k routing of one token on one 64-lane wavefront (route_token), shared by the routing
-// launches and the single-token layer.
+// Top-k routing of one token, on one 64-lane wavefront (route_token: topk rounds of a wavefront-wide
+// arg-best) or on a workgroup of 256 threads (route_single: each candidate ranked by 64-bit order
+// keys), shared by the routing launches and the single-token layer; both give the same ids and
+// weights.
 //
 // Softmax rule: ids are the topk largest logits (ties to the lower expert id); ranking logits ranks
 // softmax probabilities without any rounding, so ids are exact.  Sigmoid rule (DeepSeek-V3 style):
