@@ -167,8 +167,10 @@ int pick_ntw(int act, int N, int bm, int64_t est_blocks) {
 // Wavefronts per workgroup.  8 share one activation tile, so each issues half the activation loads
 // per weight byte of a 4-wavefront workgroup:
 //   - the second GEMM at block_m 32 (2 column tiles) where N divides the wider workgroup (measured
-//     on the fused layer: Mixtral shape at M = 64 -2.2 %, Qwen2 shape at M = 128 -1.3 %; for the
-//     first GEMM it measured neutral to slower, and it keeps 4);
+//     on the fused layer: Mixtral shape at M = 64 -2.2 %, Qwen2 shape at M = 128 -1.3 %);
+//   - the first GEMM at block_m 32 for wide experts (I >= 8192: Mixtral shape at M = 64, three
+//     alternating runs each, 202-203 -> 196-199 us per layer); for narrower ones (Qwen2 shape, I =
+//     2560, M = 128: 237.6 -> 244.9 us) it keeps 4;
 //   - both GEMMs at block_m 64 and 128 when the activations go straight from memory into LDS
 //     (bf16 activations or int8 weights), where the activation loads are two to four times the
 //     weight loads (DeepSeek-V3-shaped prefill layers: -2 to -5 %); with fp16 uint4 weights, whose
@@ -179,7 +181,8 @@ int pick_waves(int act, int N, int bm, int ntw, int dtype, int bits) {
     if (dtype != 1 && bits != 8) return 4;
     return (act ? (N / 2) % 128 : N % 256) == 0 ? 8 : 4;
   }
-  if (act || bm != 32) return 4;
+  if (bm != 32) return 4;
+  if (act) return (N / 2 >= 8192 && (N / 2) % 128 == 0) ? 8 : 4;
   return N % 256 == 0 ? 8 : 4;
 }
 
