@@ -231,6 +231,29 @@ def test_grouped_gemm_vs_oracle(dt, bits, bm, act, weighted):
     assert_layer_close(C, refm, f"gemm act={act}")
 
 
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_grouped_gemm_silu_wide_experts(dt, weighted):
+    """block_m 32 with SiLU(gate) * up for wide experts (I = 8192): the first GEMM's eight-wavefront
+    workgroup (128 gate columns), every slot and column against the oracle."""
+    wl = synth.Workload("w", E=3, H=256, I=8192, topk=2, Ms=(40,), dtype=dt)
+    layer = synth.make_layer(wl, seed=12)
+    lay = cuda_layer(layer)
+    M, bm = 40, 32
+    x = synth.make_x(wl, M, seed=12)
+    lg = synth.make_logits(wl, M, seed=12)
+    ids, w = oracle_route(wl, lg)
+    ns = M * wl.topk
+    st, ex, npost = B.moe_align_block_size(torch.from_numpy(ids).cuda(), wl.E, bm)
+    tw = torch.from_numpy(w.astype(np.float32)).cuda() if weighted else None
+    C = B.moe_wna16_gemm(x.cuda(), wl.topk, lay["w13"], lay["w13_scales"], lay["w13_zeros"], st, ex,
+                         npost, bm, ns, topk_weights=tw, act=1)
+    ref = O.grouped_gemm(x, wl.topk, O.ExpertSource(layer, 4).w13, *O.align_block_size(ids, wl.E, bm),
+                         bm, ns, topk_weights=w if weighted else None, act=1)
+    torch.cuda.synchronize()
+    assert_layer_close(C, np.stack([ref[s] for s in range(ns)]), "gemm silu wide experts")
+
+
 # ------------------------------------------------------------------------------------------------
 # the fused layer
 # ------------------------------------------------------------------------------------------------
