@@ -339,8 +339,8 @@ int fused_moe_wna16(const void* x, const float* router_logits, int M, int H, int
  * decided from the sizes alone:
  *   MOE_PATH_ONE_TOKEN  M = 1, uint4, block_m 0, E <= 256, the staged vectors within LDS
  *                       (topk * I up to about 60 K columns);
- *   MOE_PATH_FEW_TOKENS 2 <= M <= 4, uint4, block_m 0, I <= 512, H <= 8192, M * topk <= 256 (on the
- *                       DeepSeek-V3 tensor-parallel share it measured 12 to 25 % faster than the
+ *   MOE_PATH_FEW_TOKENS 2 <= M <= 5, uint4, block_m 0, I <= 512, H <= 8192, M * topk <= 256 (on the
+ *                       DeepSeek-V3 tensor-parallel share it measured 7 to 25 % faster than the
  *                       grouped GEMMs; slower with wider I or more tokens);
  *   MOE_PATH_GROUPED    otherwise.
  * Returns -1 for sizes fused_moe_wna16 rejects. */

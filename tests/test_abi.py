@@ -98,7 +98,8 @@ def test_layer_path():
     assert path(1, 7168, 2048, 256, 8) == one             # DeepSeek-V3 all experts
     assert path(2, 7168, 256, 256, 8) == few
     assert path(4, 7168, 256, 256, 8) == few
-    assert path(5, 7168, 256, 256, 8) == grouped          # more tokens
+    assert path(5, 7168, 256, 256, 8) == few
+    assert path(6, 7168, 256, 256, 8) == grouped          # more tokens
     assert path(16, 7168, 256, 256, 8) == grouped
     assert path(2, 4096, 14336, 8, 2) == grouped          # wider I
     assert path(2, 3584, 2560, 64, 8) == grouped

@@ -161,6 +161,9 @@ FEW = {
     "widest_h": synth.Workload("f5", E=16, H=8192, I=256, topk=4, Ms=(3,)),
     # 128 slots: top-32 of 64 experts for 4 tokens
     "many_slots": synth.Workload("f7", E=64, H=512, I=256, topk=32, Ms=(4,), dtype="bf16"),
+    # the most tokens the path takes: 5 tokens, 40 slots over 64 experts
+    "tp_like_m5": synth.Workload("f8", E=64, H=1024, I=256, topk=8, Ms=(5,), score="sigmoid",
+                                 num_groups=8, topk_groups=4, scale=2.5),
 }
 
 
@@ -174,14 +177,15 @@ def test_few_tokens_vs_oracle(name, seed):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_few_tokens_hot_expert(dtype):
-    """Every token's first choice is expert 3: one expert's rows meet all four tokens' rows (the
-    most a workgroup stages) in both launches."""
-    wl = synth.Workload("fh", E=32, H=1024, I=512, topk=2, Ms=(4,), dtype=dtype)
-    assert B.fused_moe_wna16_path(4, wl.H, wl.I, wl.E, wl.topk) == B.PATH_FEW_TOKENS
+@pytest.mark.parametrize("M", [4, 5])
+def test_few_tokens_hot_expert(dtype, M):
+    """Every token's first choice is expert 3: one expert's rows meet every token's rows (five is
+    the most a workgroup stages) in both launches."""
+    wl = synth.Workload("fh", E=32, H=1024, I=512, topk=2, Ms=(M,), dtype=dtype)
+    assert B.fused_moe_wna16_path(M, wl.H, wl.I, wl.E, wl.topk) == B.PATH_FEW_TOKENS
     layer = synth.make_layer(wl, seed=8)
-    x = synth.make_x(wl, 4, seed=8)
-    lg = synth.make_logits(wl, 4, seed=8)
+    x = synth.make_x(wl, M, seed=8)
+    lg = synth.make_logits(wl, M, seed=8)
     lg[:, 3] += 50.0
     out, tw, ti = run_fused(wl, x.cuda(), lg.cuda(), cuda_layer(layer))
     ids_ref, w_ref = oracle_route(wl, lg)

@@ -136,12 +136,12 @@ int pick_block_m(int M, int topk, int E, int bits, int dtype) {
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// The few-token dot-product path: up to 4 tokens with I <= 512 (a tensor-parallel share of many
+// The few-token dot-product path: up to 5 tokens with I <= 512 (a tensor-parallel share of many
 // experts).  Measured against the grouped GEMMs on the DeepSeek-V3 TP share (graph replays, layer
-// us): M = 2 26.4 against 35.1, M = 3 35.0 / 40.0, M = 4 38.2 / 47.2, M = 5 47.9 / 51.4, M = 6
-// 62.8 / 55.9, M = 8 72.7 / 63.4; with I = 2560 (Qwen2 shape) M = 2 83 / 63 and M = 3 112 / 74,
-// so there it stays off.
-constexpr int kFewMaxTokens = 4;
+// us): M = 2 26.4 against 35.1, M = 3 35.0 / 40.0, M = 4 38.2 / 47.2; with both routing launches
+// ranking per workgroup, M = 5 45.8 / 49.3, M = 6 60.0 / 53.6, M = 7 67.3 / 54.7, M = 8 70.0 /
+// 61.0; with I = 2560 (Qwen2 shape) M = 2 83 / 63 and M = 3 112 / 74, so there it stays off.
+constexpr int kFewMaxTokens = 5;
 constexpr int kFewMaxI = 512;
 
 // The launch sequence of the fused uint4/int8 layer (valid sizes assumed).
