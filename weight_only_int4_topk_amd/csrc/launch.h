@@ -125,7 +125,7 @@ hipError_t launch_quant_rows(const void* x, int rows, int K, int dtype, int8_t* 
 // out_f32 (act 0 only): C is float [num_slots, N] (the fused layer's second GEMM, combined later)
 hipError_t launch_w8a8_gemm(const W8A8Params& p, int block_m, int act, int dtype,
                             hipStream_t stream, int out_f32 = 0);
-// The same GEMM on the 32x32x32 integer matrix cores (prefill.hip), block_m 64 and 128;
+// The same GEMM on the 32x32x32 integer matrix cores (prefill.hip), block_m 64, 128 and 256;
 // launch_w8a8_gemm takes it wherever w8a8_mma32_fits.
 bool w8a8_mma32_fits(int block_m, int act, int N);
 hipError_t launch_w8a8_mma32(const W8A8Params& p, int block_m, int act, int dtype, int out_f32,
