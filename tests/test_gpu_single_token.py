@@ -36,7 +36,11 @@ CASES = {
     "wide_h": synth.Workload("wh1", E=4, H=12288, I=512, topk=2, Ms=(1,), dtype="bf16"),
     # 256 groups per first-launch row: four steps
     "widest_h": synth.Workload("wh2", E=2, H=32768, I=256, topk=1, Ms=(1,)),
-    # 256 groups per second-launch row over 64 lanes: two steps of two groups per lane; with
+    # 66 and 112 groups per second-launch row over 64 lanes: two steps of one group per lane, the
+    # second step partly empty with 66
+    "two_steps_ragged_i": synth.Workload("ti1", E=8, H=512, I=8448, topk=2, Ms=(1,)),
+    "two_steps_i_bf16": synth.Workload("ti2", E=8, H=256, I=14336, topk=2, Ms=(1,), dtype="bf16"),
+    # 256 groups per second-launch row over 64 lanes: four steps of one group per lane; with
     # topk 2 the staged intermediate rows take 128 KiB of LDS
     "widest_i": synth.Workload("wi1", E=2, H=256, I=32768, topk=2, Ms=(1,), dtype="bf16"),
     # the same with topk 4 exceeds LDS: the grouped GEMMs run instead

@@ -195,8 +195,9 @@ __device__ __forceinline__ void group_terms(uint32_t sbits, uint32_t zbyte, int 
 // ------------------------------------------------------------------------------------------------
 // up: the workgroup routes the token and stages x; then one unit = (slot j, output column n):
 // lanes 0-31 the gate row n, lanes 32-63 the up row I + n, lane l % 32 the groups l % 32 + 32 i,
-// i < GPL.  A wavefront runs upw consecutive units in steps of at most two groups per lane (P steps
-// per unit), the weights of the next step in flight while it computes one.
+// i < GPL.  A wavefront runs upw consecutive units in steps of one group per lane (GPL steps per
+// unit, few registers per step so that more wavefronts are resident), the weights of the next step
+// in flight while it computes one.
 // ------------------------------------------------------------------------------------------------
 template <int DT, int GPL>
 __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
@@ -207,8 +208,7 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
   uint32_t* sx = s_dyn;
   float* ssum = (float*)(s_dyn + K / 2);
 
-  constexpr int CH = GPL < 2 ? GPL : 2;   // groups per lane and step
-  constexpr int P = GPL / CH;             // steps per unit
+  constexpr int P = GPL;                  // steps per unit (one group per lane and step)
   constexpr int QN = P == 1 ? 2 : P;      // steps per loop iteration (two slots alternate)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -232,8 +232,8 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
     p.topk_w[threadIdx.x] = wgt;
   }
 
-  u32x4_t wq[2][CH][4];
-  uint32_t sq[2][CH], zq[2][CH];
+  u32x4_t wq[2][4];
+  uint32_t sq[2], zq[2];
   auto load_step = [&](int slot, int k, int part) {
     const int u = min(u0 + k, U - 1);  // units past the end reload the last one (not stored)
     const int j = u / I;
@@ -249,26 +249,20 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
     // rows per instruction) they stream faster than buffer loads (Mixtral shape 32.2 -> 29.4 us);
     // every address is inside expert e's rows
     const uint8_t* wrow = p.w13 + (size_t)e * N * row_bytes + (size_t)row * row_bytes;
+    const int g = min(l32 + 32 * part, G - 1);  // past the row's groups: its last one
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int g = min(l32 + 32 * (part * CH + i), G - 1);  // past the row's groups: its last one
-#pragma unroll
-      for (int q = 0; q < 4; ++q) wq[slot][i][q] = *(const u32x4_t*)(wrow + g * 64 + q * 16);
-      sq[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
-      zq[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
-    }
+    for (int q = 0; q < 4; ++q) wq[slot][q] = *(const u32x4_t*)(wrow + g * 64 + q * 16);
+    sq[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
+    zq[slot] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
   };
   float acc = 0.f;
   auto compute_step = [&](int slot, int k, int part) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int g = l32 + 32 * (part * CH + i);
-      if (g < G) {
-        float sc, off;
-        group_terms<DT>(sq[slot][i], zq[slot][i], g, sc, off);
-        const float d = group_dot<DT>(wq[slot][i], sx, g, mask, magic);
-        acc += sc * (d - off * ssum[g]);
-      }
+    const int g = l32 + 32 * part;
+    if (g < G) {
+      float sc, off;
+      group_terms<DT>(sq[slot], zq[slot], g, sc, off);
+      const float d = group_dot<DT>(wq[slot], sx, g, mask, magic);
+      acc += sc * (d - off * ssum[g]);
     }
     if (part != P - 1) return;
     // sum over the 32 lanes of each half, then gate (lane 0) and up (lane 32)
@@ -302,7 +296,7 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
 // down: a workgroup covers RW consecutive output rows; wavefront w takes slot j = w % topk and the
 // rows of part w / topk (nrp = 8 / topk parts, RPW rows each; topk > 8: slots w, w + 8, ...).  A
 // row's G groups spread over L lanes (the smallest power of two >= G, at most 64; TPL groups per
-// lane, taken two per step), 64 / L rows per pass.  Each wavefront leaves w_j * (row . inter[j])
+// lane, one per step: fewer registers, so more wavefronts in flight), 64 / L rows per pass.  Each wavefront leaves w_j * (row . inter[j])
 // per row in LDS; the workgroup then adds the slots in ascending j and writes the rows.  The first
 // step's weights are requested before the intermediate rows are staged.
 // ------------------------------------------------------------------------------------------------
@@ -331,9 +325,8 @@ __global__ void __launch_bounds__(kSThreads) single_down_kernel(SingleParams p) 
   const int nrp = topk >= kSWaves ? 1 : kSWaves / topk;
   const int RPW = RW / nrp;            // rows of one wavefront's part (a multiple of RPP)
   const int passes = RPW / RPP;
-  constexpr int CH = TPL < 2 ? TPL : 2;  // groups per lane and step
-  constexpr int P = TPL / CH;            // steps per pass of rows
-  constexpr int QN = P == 1 ? 2 : P;     // steps per loop iteration (two slots alternate)
+  constexpr int P = TPL;               // steps per pass of rows (one group per lane and step)
+  constexpr int QN = P == 1 ? 2 : P;   // steps per loop iteration (two slots alternate)
 
   // the (slot, part) a wavefront works on, set by select()
   int j = 0, part = 0;
@@ -355,34 +348,28 @@ __global__ void __launch_bounds__(kSThreads) single_down_kernel(SingleParams p) 
                                            (int)(H * zrow), kRsrcS);
   };
 
-  u32x4_t wq[2][CH][4];
-  uint32_t sq[2][CH], zq[2][CH];
+  u32x4_t wq[2][4];
+  uint32_t sq[2], zq[2];
   auto load_step = [&](int slot, int ps, int gp) {
     const uint32_t row = (uint32_t)min(n0 + part * RPW + ps * RPP + rsub, H - 1);
+    const int g = min(sub + L * gp, G - 1);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int g = min(sub + L * (gp * CH + i), G - 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        wq[slot][i][q] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, row * row_bytes + g * 64 + q * 16, 0, 0));
-      sq[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
-      zq[slot][i] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
-    }
+    for (int q = 0; q < 4; ++q)
+      wq[slot][q] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, row * row_bytes + g * 64 + q * 16, 0, 0));
+    sq[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, row * srow + g * 2, 0, 0);
+    zq[slot] = __builtin_amdgcn_raw_buffer_load_b8(rz, row * zrow + (g >> 1), 0, 0);
   };
   float acc = 0.f;
   auto compute_step = [&](int slot, int ps, int gp) {
     const uint32_t* sv = sx + (size_t)j * K / 2;
     const float* sj = ssum + j * G;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int g = sub + L * (gp * CH + i);
-      if (g < G) {
-        float sc, off;
-        group_terms<DT>(sq[slot][i], zq[slot][i], g, sc, off);
-        const float d = group_dot<DT>(wq[slot][i], sv, g, mask, magic);
-        acc += sc * (d - off * sj[g]);
-      }
+    const int g = sub + L * gp;
+    if (g < G) {
+      float sc, off;
+      group_terms<DT>(sq[slot], zq[slot], g, sc, off);
+      const float d = group_dot<DT>(wq[slot], sv, g, mask, magic);
+      acc += sc * (d - off * sj[g]);
     }
     if (gp != P - 1) return;
     acc = lane_group_sum(acc, L);
