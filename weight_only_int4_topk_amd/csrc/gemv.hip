@@ -296,9 +296,10 @@ __global__ void __launch_bounds__(kSThreads) single_up_kernel(SingleParams p) {
 // down: a workgroup covers RW consecutive output rows; wavefront w takes slot j = w % topk and the
 // rows of part w / topk (nrp = 8 / topk parts, RPW rows each; topk > 8: slots w, w + 8, ...).  A
 // row's G groups spread over L lanes (the smallest power of two >= G, at most 64; TPL groups per
-// lane, one per step: fewer registers, so more wavefronts in flight), 64 / L rows per pass.  Each wavefront leaves w_j * (row . inter[j])
-// per row in LDS; the workgroup then adds the slots in ascending j and writes the rows.  The first
-// step's weights are requested before the intermediate rows are staged.
+// lane, one per step: fewer registers, so more wavefronts in flight), 64 / L rows per pass.  Each
+// wavefront leaves w_j * (row . inter[j]) per row in LDS; the workgroup then adds the slots in
+// ascending j and writes the rows.  The first step's weights are requested before the
+// intermediate rows are staged.
 // ------------------------------------------------------------------------------------------------
 template <int DT, int TPL>
 __global__ void __launch_bounds__(kSThreads) single_down_kernel(SingleParams p) {
