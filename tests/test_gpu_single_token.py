@@ -32,9 +32,9 @@ CASES = {
     # 14 and 10 groups per row: lanes without a group in both launches
     "odd_groups_fp16": synth.Workload("og1", E=16, H=1792, I=1280, topk=4, Ms=(1,)),
     "odd_groups_bf16": synth.Workload("og2", E=16, H=1792, I=1280, topk=4, Ms=(1,), dtype="bf16"),
-    # 96 groups per first-launch row: two steps of two groups per lane
+    # 96 groups per first-launch row over 32 lanes: four steps of one group per lane, the last empty
     "wide_h": synth.Workload("wh1", E=4, H=12288, I=512, topk=2, Ms=(1,), dtype="bf16"),
-    # 256 groups per first-launch row: four steps
+    # 256 groups per first-launch row over 32 lanes: eight steps
     "widest_h": synth.Workload("wh2", E=2, H=32768, I=256, topk=1, Ms=(1,)),
     # 66 and 112 groups per second-launch row over 64 lanes: two steps of one group per lane, the
     # second step partly empty with 66
@@ -119,8 +119,10 @@ def test_single_token_fp16_tiny_activations():
                        "tiny activations, one token")
 
 
-def test_single_token_deterministic_and_graph_replay():
-    wl = CASES["sigmoid_groups_bf16"]
+# one step per lane in both launches; two steps of the second launch; four of the first
+@pytest.mark.parametrize("name", ["sigmoid_groups_bf16", "two_steps_i_bf16", "wide_h"])
+def test_single_token_deterministic_and_graph_replay(name):
+    wl = CASES[name]
     layer = cuda_layer(synth.make_layer(wl, seed=1))
     x = synth.make_x(wl, 1, seed=1).cuda()
     lg = synth.make_logits(wl, 1, seed=1).cuda()
