@@ -47,6 +47,11 @@ SMALL = {
     "sigmoid_groups": synth.Workload("c", E=64, H=512, I=256, topk=8, Ms=(20,), score="sigmoid",
                                      num_groups=8, topk_groups=4, scale=2.5),
     "single_token": synth.Workload("d", E=8, H=1792, I=768, topk=2, Ms=(1,)),
+    # one token, more experts and slots, and a wider first-GEMM K
+    "single_token_sigmoid_bf16": synth.Workload("e", E=64, H=2048, I=512, topk=8, Ms=(1,),
+                                                dtype="bf16", score="sigmoid", num_groups=8,
+                                                topk_groups=4, scale=2.5),
+    "single_token_two_steps": synth.Workload("f", E=16, H=6144, I=768, topk=4, Ms=(1,)),
 }
 
 
@@ -92,6 +97,31 @@ def test_act_order_mixtral_shape_all_tokens():
     wl = synth.WORKLOADS["mixtral"]
     out, ref, rows = _run(wl, 16, seed=0, device="cuda")
     assert_layer_close(O.to_numpy(out)[rows], ref, "act-order mixtral")
+
+
+def test_act_order_mixtral_shape_one_token():
+    wl = synth.WORKLOADS["mixtral"]
+    out, ref, rows = _run(wl, 1, seed=0, device="cuda")
+    assert_layer_close(O.to_numpy(out)[rows], ref, "act-order mixtral, one token")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_act_order_one_token_matches_grouped_with_entries_out_of_range(dtype):
+    """Permutation entries outside [0, H) / [0, I) read as zero whatever the block size: the
+    library's choice (block_m 0) against 16-row blocks on the same inputs."""
+    wl = SMALL["single_token"].with_(dtype=dtype)
+    lay = synth.make_layer_act_order(wl, seed=5, device="cuda")
+    lay["w13_perm"][:, 5] = wl.H
+    lay["w13_perm"][1, 200] = -1
+    lay["w2_perm"][:, 7] = wl.I + 3
+    x = synth.make_x(wl, 1, seed=5, device="cuda")
+    lg = synth.make_logits(wl, 1, seed=5, device="cuda")
+    outs = [B.fused_moe_wna16_act_order(x, lg, wl.topk, routing_of(wl), lay["w13"],
+                                        lay["w13_scales"], lay["w13_zeros"], lay["w13_perm"],
+                                        lay["w2"], lay["w2_scales"], lay["w2_zeros"],
+                                        lay["w2_perm"], block_m=bm) for bm in (0, 16)]
+    torch.cuda.synchronize()
+    assert_layer_close(outs[0], O.to_numpy(outs[1]), f"act-order, two block sizes, {dtype}")
 
 
 def test_act_order_largest_batch_sampled():
